@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE-layer hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+route -> (dispatch FP8 fake-quant) -> permute -> grouped SwiGLU FFN (gate/up
+then down, BF16 MFMA) -> (shared expert) -> combine (+ combine-row FP8
+fake-quant).  Inputs and weights are resident in HBM before timing starts.
+
+Prints ONE JSON line: routed tokens/s for the layer, the roofline of the
+dominant kernel (timed with HIP events on the stream it runs on), per-stage
+times / achieved GB/s / MFMA utilisation, and the CPU oracle timed on a
+bounded sample on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense BF16 MFMA, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def algorithmic(cfg, counts: np.ndarray) -> dict:
+    """Bytes (and FLOPs) each stage must move (compute) at minimum: every
+    input read once, every output written once, padding rows and re-reads
+    not counted."""
+    T, H, E, K, I = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I
+    Tv = cfg.T_valid
+    N = int(counts.sum())
+    E_act = int((counts > 0).sum())
+    st = {}
+    st["route"] = dict(bytes=4 * T * E + 8 * T * K + (T if cfg.pad_rows else 0))
+    if cfg.dispatch_block:
+        st["dispatch_qdq"] = dict(bytes=4 * Tv * H)
+    st["permute"] = dict(bytes=8 * T * K + 2 * Tv * H + 2 * N * H + 4 * T * K + 8 * N + 8 * E)
+    st["ffn_gate_up"] = dict(bytes=2 * 2 * E_act * I * H + 2 * N * H + 2 * N * I,
+                             flops=4 * N * I * H)
+    st["ffn_down"] = dict(bytes=2 * E_act * I * H + 2 * N * I + 2 * N * H + 4 * N,
+                          flops=2 * N * I * H)
+    if cfg.shared_I:
+        Is = cfg.shared_I
+        st["shared_ffn"] = dict(bytes=6 * Is * H + 2 * T * H + 2 * T * H, flops=6 * T * Is * H)
+    st["combine"] = dict(bytes=2 * N * H + 4 * T * K + 2 * T * H + (2 * T * H if cfg.shared_I else 0))
+    return st
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(os.path.join(ROOT, "combine_top_route_moe_amd", "csrc"))):
+        with open(os.path.join(ROOT, "combine_top_route_moe_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
+    taken on the kernels as they are now (same source hash); else None."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, logits, hidden, row_valid, budget_s: float):
+    """Time the oracle layer (as it stands) on a bounded sample of tokens."""
+    import oracle
+    import workloads
+
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"]
+        if blas:
+            cores = min(cores, max(blas))
+    except Exception:
+        pass
+    # a contiguous prefix of the batch, sized so the run stays within budget:
+    # probe with a small sample, then scale
+    weights_cache = {}
+
+    def weights(e):
+        if e not in weights_cache:
+            weights_cache[e] = workloads.expert_weights(cfg, e)
+        return weights_cache[e]
+
+    shared = workloads.shared_weights(cfg)
+
+    def run(n):
+        rv = None if row_valid is None else row_valid[:n]
+        t0 = time.perf_counter()
+        oracle.moe_layer(logits[:n], hidden[:n], weights, cfg.K, rv,
+                         dispatch_block=cfg.dispatch_block or None, pad_pow2=cfg.pad_pow2,
+                         shared_weights=shared, combine_qdq=cfg.combine_qdq)
+        return time.perf_counter() - t0
+
+    n = min(cfg.T, 64)
+    for e in range(cfg.E):            # weight generation is not part of the timed oracle
+        weights(e)
+    dt = run(n)
+    while n < cfg.T and dt < budget_s / 4:
+        n = min(cfg.T, n * 4)
+        dt = run(n)
+    tv = n if row_valid is None else int(row_valid[:n].sum())
+    return {"value": tv / dt, "unit": "routed tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} of {cfg.T} tokens of the {cfg.name} batch "
+                      f"({tv} routed), whole layer, float64 numpy, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="balanced",
+                    help="tiny | balanced | skewed | deepseek | prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU expert-parallel exchange is not implemented", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    from combine_top_route_moe_amd import MoELayer, ops
+
+    cfg = workloads.CONFIGS[args.config]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if ops.moe_device_check(0) != 0:
+        raise SystemExit("device 0 is not a gfx950 GPU")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    logits_h = workloads.logits(cfg)
+    hidden_h = workloads.hidden(cfg)
+    valid_h = workloads.row_valid(cfg)
+    logits = torch.from_numpy(logits_h).to(dev)
+    hidden = bf16(hidden_h)
+    row_valid = None if valid_h is None else torch.from_numpy(valid_h).to(dev)
+
+    layer = MoELayer(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, dev, shared_I=cfg.shared_I,
+                     dispatch_block=cfg.dispatch_block, combine_qdq=cfg.combine_qdq,
+                     pad_pow2=cfg.pad_pow2)
+    w13 = torch.empty(cfg.E, 2 * cfg.I, cfg.H, dtype=torch.bfloat16, device=dev)
+    w2 = torch.empty(cfg.E, cfg.H, cfg.I, dtype=torch.bfloat16, device=dev)
+
+    def put(e, a, b):
+        w13[e].copy_(bf16(a))
+        w2[e].copy_(bf16(b))
+
+    workloads.for_each_expert(cfg, put)
+    sw = workloads.shared_weights(cfg)
+    layer.set_weights(w13, w2, *(bf16(x) for x in sw) if sw else (None, None))
+    if cfg.combine_qdq:
+        layer.calibrate_combine_scale(logits, hidden, row_valid)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        layer.forward(logits, hidden, row_valid)
+    torch.cuda.synchronize()
+    layer.dev_error.zero_()
+
+    # HIP events between stages, on the stream the kernels are launched on
+    stream = torch.cuda.current_stream()
+    marks = []
+
+    def mark(name):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(stream)
+        marks[-1].append((name, ev))
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        start = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        marks.append([("start", start)])
+        layer.forward(logits, hidden, row_valid, mark)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert layer.dev_error.item() == 0, "device error word set during the timed run"
+
+    stage_ms = {}
+    for step in marks:
+        for (_, a), (name, b) in zip(step[:-1], step[1:]):
+            stage_ms.setdefault(name, []).append(a.elapsed_time(b))
+    stage_ms = {k: float(np.mean(v)) for k, v in stage_ms.items()}
+
+    counts = layer.perm.counts.cpu().numpy()
+    alg = algorithmic(cfg, counts)
+    stages = {}
+    for name, ms in stage_ms.items():
+        a = alg.get(name, {})
+        d = {"ms": round(ms, 5)}
+        if "bytes" in a:
+            d["alg_bytes"] = a["bytes"]
+            d["GBps"] = round(a["bytes"] / (ms * 1e-3) / 1e9, 1)
+            d["hbm_frac"] = round(d["GBps"] / PEAK_HBM_GBPS, 4)
+        if "flops" in a:
+            d["TFLOPs"] = round(a["flops"] / (ms * 1e-3) / 1e12, 2)
+            d["mfma_util"] = round(d["TFLOPs"] / PEAK_BF16_TFLOPS, 4)
+        stages[name] = d
+
+    dom = max(stage_ms, key=stage_ms.get)
+    a = alg[dom]
+    intensity = a.get("flops", 0) / a["bytes"]
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    if intensity >= ridge:
+        roof = {"bound": "mfma", "achieved": stages[dom]["TFLOPs"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": stages[dom]["GBps"], "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = {"ffn_gate_up": "grouped_gemm_kernel<true>",
+                      "ffn_down": "grouped_gemm_kernel<false>"}.get(dom, dom)
+    roof["alg_bytes_per_launch"] = a["bytes"]
+    roof["traffic"] = committed_traffic(dom, cfg.name)
+
+    ms_step = elapsed / args.steps * 1e3
+    gemm_flops = alg["ffn_gate_up"]["flops"] + alg["ffn_down"]["flops"]
+    gemm_ms = stage_ms["ffn_gate_up"] + stage_ms["ffn_down"]
+    result = {
+        "metric": "routed tokens/sec per MoE layer; grouped-GEMM MFMA util; permute/combine GB/s",
+        "value": round(cfg.T_valid / (elapsed / args.steps), 1),
+        "unit": "routed tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) logits and hidden, N(0,0.02) weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "T_valid": cfg.T_valid, "H": cfg.H,
+                   "E": cfg.E, "K": cfg.K, "I": cfg.I, "shared_I": cfg.shared_I,
+                   "routed_rows": int(counts.sum()), "dispatch_fp8_block": cfg.dispatch_block,
+                   "combine_fp8": cfg.combine_qdq, "pad_pow2": cfg.pad_pow2,
+                   "parallelism": "single GPU (all experts local)"},
+        "grouped_gemm_mfma_util": round(gemm_flops / (gemm_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+        "permute_GBps": stages["permute"]["GBps"],
+        "combine_GBps": stages["combine"]["GBps"],
+        "stages": stages,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, logits_h, hidden_h, valid_h, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+// C ABI of the MoE hot path: host-side argument checks, size queries and
+// kernel launches.  Every check here looks at scalars and pointers only —
+// nothing reads device memory or synchronizes — so the calls stay
+// asynchronous and can be captured into a HIP graph.
+#include <string.h>
+
+#include "common.h"
+
+namespace moe {
+int launch_route(const float*, const uint8_t*, int, int, int, int, int32_t*, float*, hipStream_t);
+int launch_fake_quant(const uint16_t*, uint16_t*, int64_t, int, const int32_t*, int, const float*,
+                      float*, float*, hipStream_t);
+int launch_scale_from_amax(const float*, float*, hipStream_t);
+int launch_combine(const uint16_t*, int64_t, const int32_t*, const uint16_t*, int, int, int,
+                   const float*, uint16_t*, int32_t*, hipStream_t);
+size_t permute_workspace_bytes(int64_t, int);
+int launch_permute(const int32_t*, const float*, const uint16_t*, int, int, int, int, int, int,
+                   int64_t, int32_t*, int32_t*, uint16_t*, int32_t*, int32_t*, float*, void*,
+                   int32_t*, hipStream_t);
+size_t grouped_ffn_workspace_bytes(int64_t, int);
+int launch_grouped_ffn(const uint16_t*, const int32_t*, const int32_t*, int, int, int,
+                       const uint16_t*, const uint16_t*, const float*, uint16_t*, int64_t, int,
+                       void*, int32_t*, hipStream_t);
+
+__global__ void __launch_bounds__(256) copy_kernel(const uint4* __restrict__ src,
+                                                   uint4* __restrict__ dst, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    dst[i] = src[i];
+}
+}  // namespace moe
+
+using namespace moe;
+
+static inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size or bad flag)";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape (H and I must be multiples of 128; E, G <= 1024; K <= 32)";
+    case MOE_ERR_WORKSPACE: return "workspace smaller than the size query requires";
+    case MOE_ERR_HIP: return "HIP runtime error or kernel launch failure";
+    case MOE_ERR_DEVICE: return "the current device is not a gfx950 (MI355X-class) GPU";
+    default: return "unknown status";
+  }
+}
+
+int moe_device_check(int device) {
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return MOE_ERR_HIP;
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MOE_ERR_DEVICE;
+  return MOE_OK;
+}
+
+int moe_route(const float* logits, const uint8_t* row_valid, int T, int E, int K, int flags,
+              int32_t* topk_idx, float* topk_w, void* stream) {
+  if (T < 0 || E < 1 || K < 1 || K > E) return MOE_ERR_INVALID_ARG;
+  if (K > 32 || E > 1024) return MOE_ERR_UNSUPPORTED;
+  if (flags & ~MOE_ROUTE_RENORM) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  return launch_route(logits, row_valid, T, E, K, (flags & MOE_ROUTE_RENORM) ? 1 : 0, topk_idx,
+                      topk_w, as_stream(stream));
+}
+
+int64_t moe_permute_capacity(int T, int K, int num_local_experts, int flags) {
+  if (T < 0 || K < 1 || num_local_experts < 1) return 0;
+  const int64_t tk = (int64_t)T * K;
+  if (!(flags & MOE_PERMUTE_PAD_POW2)) return tk;
+  // sum_e next_pow2(c_e) <= sum_e (2 c_e - 1) over non-empty experts, and
+  // each non-empty expert pads by at most next_pow2(tk) - 1 rows
+  const int64_t bound = 2 * tk;
+  int64_t p = 1;
+  while (p < tk) p <<= 1;
+  const int64_t per_expert = (int64_t)num_local_experts * p;
+  return bound < per_expert ? bound : per_expert;
+}
+
+size_t moe_permute_workspace_bytes(int T, int K, int num_local_experts, int flags) {
+  (void)flags;
+  if (T < 0 || K < 1 || num_local_experts < 1) return 0;
+  return permute_workspace_bytes((int64_t)T * K, num_local_experts);
+}
+
+int moe_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t* hidden, int T, int K,
+                int H, int expert_begin, int num_local_experts, int flags, int64_t capacity,
+                int32_t* counts, int32_t* cu_seqlens, uint16_t* x_perm, int32_t* row_of,
+                int32_t* src_of, float* w_perm, void* workspace, size_t workspace_bytes,
+                int32_t* dev_error, void* stream) {
+  if (T < 0 || K < 1 || H < 1 || num_local_experts < 1 || capacity < 0 || expert_begin < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (flags & ~MOE_PERMUTE_PAD_POW2) return MOE_ERR_INVALID_ARG;
+  if (H % 128 || num_local_experts > 1024 || K > 64) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * K > 0x7fffffffLL || capacity > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  if (!counts || !cu_seqlens) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!topk_idx || !topk_w || !hidden || !row_of)) return MOE_ERR_INVALID_ARG;
+  if (capacity > 0 && (!x_perm || !src_of || !w_perm)) return MOE_ERR_INVALID_ARG;
+  if ((hidden && !aligned16(hidden)) || (x_perm && !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
+  const size_t need = permute_workspace_bytes((int64_t)T * K, num_local_experts);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+  return launch_permute(topk_idx, topk_w, hidden, T, K, H, expert_begin, num_local_experts,
+                        (flags & MOE_PERMUTE_PAD_POW2) ? 1 : 0, capacity, counts, cu_seqlens,
+                        x_perm, row_of, src_of, w_perm, workspace, dev_error, as_stream(stream));
+}
+
+size_t moe_grouped_ffn_workspace_bytes(int64_t capacity, int num_groups, int H, int I) {
+  (void)num_groups;
+  (void)H;
+  if (capacity < 0 || I < 1) return 0;
+  return grouped_ffn_workspace_bytes(capacity, I);
+}
+
+int moe_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32_t* counts,
+                    int num_groups, int H, int I, const uint16_t* w13, const uint16_t* w2,
+                    const float* row_scale, uint16_t* y, int64_t capacity, int stages,
+                    void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream) {
+  if (num_groups < 1 || H < 1 || I < 1 || capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (stages < 1 || stages > MOE_FFN_ALL) return MOE_ERR_INVALID_ARG;
+  if (H % 128 || I % 128 || num_groups > 1024) return MOE_ERR_UNSUPPORTED;
+  if (capacity > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  if (!cu_seqlens || !counts) return MOE_ERR_INVALID_ARG;
+  if ((stages & MOE_FFN_GATE_UP) && (!x || !w13)) return MOE_ERR_INVALID_ARG;
+  if ((stages & MOE_FFN_DOWN) && (!y || !w2)) return MOE_ERR_INVALID_ARG;
+  if ((x && !aligned16(x)) || (y && !aligned16(y)) || (w13 && !aligned16(w13)) ||
+      (w2 && !aligned16(w2)))
+    return MOE_ERR_INVALID_ARG;
+  const size_t need = grouped_ffn_workspace_bytes(capacity, I);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return MOE_ERR_WORKSPACE;
+  return launch_grouped_ffn(x, cu_seqlens, counts, num_groups, H, I, w13, w2, row_scale, y,
+                            capacity, stages, workspace, dev_error, as_stream(stream));
+}
+
+int moe_fake_quant_rows(const uint16_t* in, uint16_t* out, int64_t n_rows, int H,
+                        const int32_t* row_src, int mode, int block, const float* scale,
+                        float* block_scales, float* amax_out, void* stream) {
+  if (n_rows < 0 || H < 1) return MOE_ERR_INVALID_ARG;
+  if (mode != MOE_FQ_PER_TENSOR && mode != MOE_FQ_BLOCK) return MOE_ERR_INVALID_ARG;
+  if (H % 128) return MOE_ERR_UNSUPPORTED;
+  if (mode == MOE_FQ_BLOCK && block != 128) return MOE_ERR_UNSUPPORTED;
+  if (n_rows == 0) return MOE_OK;
+  if (!in || (!out && (mode == MOE_FQ_BLOCK || scale))) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(in) || (out && !aligned16(out))) return MOE_ERR_INVALID_ARG;
+  return launch_fake_quant(in, out, n_rows, H, row_src, mode, scale, block_scales, amax_out,
+                           as_stream(stream));
+}
+
+int moe_scale_from_amax(const float* amax, float* scale, void* stream) {
+  if (!amax || !scale) return MOE_ERR_INVALID_ARG;
+  return launch_scale_from_amax(amax, scale, as_stream(stream));
+}
+
+int moe_combine(const uint16_t* rows, int64_t num_rows, const int32_t* row_of,
+                const uint16_t* shared, int T, int K, int H, const float* row_qdq_scale,
+                uint16_t* out, int32_t* dev_error, void* stream) {
+  if (T < 0 || K < 1 || H < 1 || num_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (H % 128) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!row_of || !out || (num_rows > 0 && !rows)) return MOE_ERR_INVALID_ARG;
+  if ((rows && !aligned16(rows)) || !aligned16(out) || (shared && !aligned16(shared)))
+    return MOE_ERR_INVALID_ARG;
+  return launch_combine(rows, num_rows, row_of, shared, T, K, H, row_qdq_scale, out, dev_error,
+                        as_stream(stream));
+}
+
+int moe_copy_bytes(const void* src, void* dst, size_t bytes, void* stream) {
+  if (bytes % 16) return MOE_ERR_INVALID_ARG;
+  if (bytes == 0) return MOE_OK;
+  if (!src || !dst || !aligned16(src) || !aligned16(dst)) return MOE_ERR_INVALID_ARG;
+  const int64_t n = (int64_t)(bytes / 16);
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
+                     static_cast<const uint4*>(src), static_cast<uint4*>(dst), n);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // extern "C"

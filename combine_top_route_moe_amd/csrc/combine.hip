@@ -1,0 +1,80 @@
+// Ordered combine of the per-(token, slot) rows.
+//
+// Source: "Add MoE dispatch/combine fake quantization for vLLM's DeepGEMM
+// Mega-MoE", PR summary and "How it works": valid slots in ascending order,
+// FP32 starting from zero, one BF16 rounding, a fused shared expert's slot
+// last and unquantized.
+//
+// Each thread owns 8 consecutive channels of one token (a 16-byte vector):
+// it walks the token's K slots in order, gathers one vector per valid slot
+// (a contiguous 16-byte load from that slot's row) and adds it with plain
+// binary32 adds — the file is built with -ffp-contract=off and there is no
+// multiply to fuse with — so the order of the adds is exactly the page's.
+// Stores are coalesced 16-byte vectors of the output row.
+#include "common.h"
+
+namespace moe {
+
+template <bool QDQ>
+__global__ void __launch_bounds__(256) combine_kernel(
+    const uint16_t* __restrict__ rows, int64_t num_rows, const int32_t* __restrict__ row_of,
+    const uint16_t* __restrict__ shared, int T, int K, int H,
+    const float* __restrict__ qdq_scale, uint16_t* __restrict__ out,
+    int32_t* __restrict__ dev_error) {
+  const int vec_per_row = H / 8;
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= (int64_t)T * vec_per_row) return;
+  const int64_t t = v / vec_per_row;
+  const int c = (int)(v - t * vec_per_row);
+  const float s = QDQ ? *qdq_scale : 1.0f;
+
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+  const int32_t* ro = row_of + t * K;
+  for (int k = 0; k < K; ++k) {
+    const int32_t r = ro[k];
+    if (r < 0) continue;
+    if (r >= num_rows) {
+      raise_error(dev_error, MOE_DEVERR_ROW_RANGE);
+      continue;
+    }
+    uint4 raw = reinterpret_cast<const uint4*>(rows + (int64_t)r * H)[c];
+    float f[8];
+    unpack8(raw, f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float x = f[j];
+      if (QDQ) x = bf16_to_f32(qdq_e4m3(x, s));
+      acc[j] = acc[j] + x;
+    }
+  }
+  if (shared) {
+    uint4 raw = reinterpret_cast<const uint4*>(shared + t * H)[c];
+    float f[8];
+    unpack8(raw, f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = acc[j] + f[j];
+  }
+  uint32_t h[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) h[j] = f32_to_bf16(acc[j]);
+  reinterpret_cast<uint4*>(out + t * H)[c] = pack8(h);
+}
+
+int launch_combine(const uint16_t* rows, int64_t num_rows, const int32_t* row_of,
+                   const uint16_t* shared, int T, int K, int H, const float* qdq_scale,
+                   uint16_t* out, int32_t* dev_error, hipStream_t stream) {
+  const int64_t nvec = (int64_t)T * (H / 8);
+  if (nvec == 0) return MOE_OK;
+  dim3 block(256), grid((unsigned)((nvec + 255) / 256));
+  if (qdq_scale)
+    hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, stream, rows, num_rows, row_of,
+                       shared, T, K, H, qdq_scale, out, dev_error);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, stream, rows, num_rows, row_of,
+                       shared, T, K, H, qdq_scale, out, dev_error);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace moe

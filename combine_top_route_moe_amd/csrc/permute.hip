@@ -1,0 +1,215 @@
+// Permute of the routed (token, slot) rows into expert-contiguous segments.
+//
+// Source: "[Distributed][MoonEP] BF16 integration of MoonEP balanced EP
+// backend", "Purpose" (rows grouped per expert as [NvS, H] + cu_seqlens);
+// "[Bugfix][MoE] Size the permute scratch from its inputs", PR summary and
+// "Details" (int32 metadata over the expanded rows sized from the inputs,
+// power-of-two receive buckets, permuted rows in a caller buffer).
+//
+// Rows inside a segment are ordered by the flat slot index i = t*K + k, so
+// the result is unique and deterministic.  Three launches:
+//   1. chunk_rank: one wavefront per chunk of 1024 flat slots walks its
+//      chunk 64 slots at a time.  Lanes holding the same expert find each
+//      other with one ballot per bit of the expert id; a lane's rank is the
+//      number of same-expert lanes below it plus the running count of that
+//      expert in the chunk (kept in LDS).  Writes rank[i] and the chunk's
+//      per-expert totals.
+//   2. scan: one workgroup turns the chunk totals into per-expert counts,
+//      segment sizes (optionally next_pow2), cu_seqlens, and the absolute
+//      first row of every (chunk, expert) pair; it also marks pow2 padding
+//      rows (src_of = -1, w_perm = 0) and checks the capacity.
+//   3. scatter: one workgroup per token group computes row_of / src_of /
+//      w_perm for its slots and copies each token row once from HBM into
+//      its K destination rows with 16-byte vector loads and stores.
+#include "common.h"
+
+namespace moe {
+
+constexpr int kChunk = 1024;
+
+__global__ void __launch_bounds__(64) permute_chunk_rank_kernel(
+    const int32_t* __restrict__ topk_idx, int64_t TK, int expert_begin, int El, int nbits,
+    int32_t* __restrict__ table /* [nchunks][El] */, int32_t* __restrict__ rank /* [TK] */) {
+  __shared__ int32_t running[1024];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < El; e += kWave) running[e] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * kChunk;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int step = 0; step < kChunk / kWave; ++step) {
+    const int64_t i = base + step * kWave + lane;
+    int e = -1;
+    if (i < TK) {
+      int id = topk_idx[i];
+      int le = id - expert_begin;
+      if (id >= 0 && le >= 0 && le < El) e = le;
+    }
+    uint64_t peers = __ballot(e >= 0);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bb = __ballot(bit);
+      peers &= bit ? bb : ~bb;
+    }
+    const int below = __popcll(peers & lt_mask);
+    int before = 0;
+    if (e >= 0) before = running[e];
+    // all lanes have read running[] before any leader updates it (one wave,
+    // LDS operations retire in program order)
+    if (e >= 0 && below == 0) running[e] = before + __popcll(peers);
+    if (i < TK) rank[i] = e >= 0 ? before + below : -1;
+  }
+  __syncthreads();
+  int32_t* trow = table + (int64_t)blockIdx.x * El;
+  for (int e = lane; e < El; e += kWave) trow[e] = running[e];
+}
+
+__device__ __forceinline__ int next_pow2_dev(int n) {
+  if (n <= 1) return n;
+  return 1 << (32 - __clz(n - 1));
+}
+
+__global__ void __launch_bounds__(1024) permute_scan_kernel(
+    int32_t* __restrict__ table, int nchunks, int El, int pad_pow2, int64_t capacity,
+    int32_t* __restrict__ counts, int32_t* __restrict__ cu_seqlens, int32_t* __restrict__ src_of,
+    float* __restrict__ w_perm, int32_t* __restrict__ dev_error) {
+  __shared__ int32_t s_wave[16];
+  const int tid = threadIdx.x;
+  const int e = tid;
+  int total = 0;
+  if (e < El) {
+    for (int c = 0; c < nchunks; ++c) total += table[(int64_t)c * El + e];
+  }
+  const int size = (e < El) ? (pad_pow2 ? next_pow2_dev(total) : total) : 0;
+  // block-wide inclusive scan of size over 1024 threads
+  const int lane = tid & 63, wid = tid >> 6;
+  int x = size;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_wave[wid] = x;
+  __syncthreads();
+  if (wid == 0) {
+    int w = lane < 16 ? s_wave[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      int y = __shfl_up(w, off, kWave);
+      if (lane >= off) w += y;
+    }
+    if (lane < 16) s_wave[lane] = w;
+  }
+  __syncthreads();
+  const int incl = x + (wid > 0 ? s_wave[wid - 1] : 0);
+  const int start = incl - size;
+  if (e < El) {
+    counts[e] = total;
+    cu_seqlens[e] = start;
+    if (e == El - 1) {
+      cu_seqlens[El] = incl;
+      if ((int64_t)incl > capacity) raise_error(dev_error, MOE_DEVERR_CAPACITY);
+    }
+    int running = start;
+    for (int c = 0; c < nchunks; ++c) {
+      const int64_t k = (int64_t)c * El + e;
+      const int cnt = table[k];
+      table[k] = running;
+      running += cnt;
+    }
+    for (int r = start + total; r < start + size && (int64_t)r < capacity; ++r) {
+      src_of[r] = -1;
+      w_perm[r] = 0.0f;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) permute_scatter_kernel(
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
+    const uint16_t* __restrict__ hidden, int T, int K, int H, int expert_begin, int El,
+    int tok_per_block, int64_t capacity, const int32_t* __restrict__ table,
+    const int32_t* __restrict__ rank, uint16_t* __restrict__ x_perm, int32_t* __restrict__ row_of,
+    int32_t* __restrict__ src_of, float* __restrict__ w_perm, int32_t* __restrict__ dev_error) {
+  __shared__ int32_t dest[256];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * tok_per_block;
+  const int nslots = tok_per_block * K;
+  if (tid < nslots) {
+    const int t = t0 + tid / K;
+    int r = -1;
+    if (t < T) {
+      const int64_t i = (int64_t)t0 * K + tid;
+      const int rk = rank[i];
+      if (rk >= 0) {
+        const int e = topk_idx[i] - expert_begin;
+        const int64_t rr = (int64_t)table[(i / kChunk) * El + e] + rk;
+        if (rr < capacity) {
+          r = (int)rr;
+          src_of[r] = (int32_t)i;
+          w_perm[r] = topk_w[i];
+        } else {
+          raise_error(dev_error, MOE_DEVERR_CAPACITY);
+        }
+      }
+      row_of[i] = r;
+    }
+    dest[tid] = r;
+  }
+  __syncthreads();
+  const int nvec = H / 8;
+  const int total = tok_per_block * nvec;
+  for (int idx = tid; idx < total; idx += blockDim.x) {
+    const int tl = idx / nvec;
+    const int c = idx - tl * nvec;
+    const int t = t0 + tl;
+    if (t >= T) break;
+    bool any = false;
+    for (int k = 0; k < K; ++k) any |= dest[tl * K + k] >= 0;
+    if (!any) continue;
+    const uint4 val = reinterpret_cast<const uint4*>(hidden + (int64_t)t * H)[c];
+    for (int k = 0; k < K; ++k) {
+      const int r = dest[tl * K + k];
+      if (r >= 0) reinterpret_cast<uint4*>(x_perm + (int64_t)r * H)[c] = val;
+    }
+  }
+}
+
+size_t permute_workspace_bytes(int64_t TK, int El) {
+  const int64_t nchunks = (TK + kChunk - 1) / kChunk;
+  size_t table = (size_t)nchunks * El * sizeof(int32_t);
+  table = (table + 255) & ~(size_t)255;
+  size_t rank = (size_t)TK * sizeof(int32_t);
+  return table + ((rank + 255) & ~(size_t)255);
+}
+
+int launch_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t* hidden, int T,
+                   int K, int H, int expert_begin, int El, int pad_pow2, int64_t capacity,
+                   int32_t* counts, int32_t* cu_seqlens, uint16_t* x_perm, int32_t* row_of,
+                   int32_t* src_of, float* w_perm, void* workspace, int32_t* dev_error,
+                   hipStream_t stream) {
+  const int64_t TK = (int64_t)T * K;
+  const int nchunks = (int)((TK + kChunk - 1) / kChunk);
+  size_t table_bytes = ((size_t)nchunks * El * sizeof(int32_t) + 255) & ~(size_t)255;
+  int32_t* table = static_cast<int32_t*>(workspace);
+  int32_t* rank = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + table_bytes);
+  int nbits = 1;
+  while ((1 << nbits) < El) ++nbits;
+
+  if (nchunks > 0)
+    hipLaunchKernelGGL(permute_chunk_rank_kernel, dim3(nchunks), dim3(kWave), 0, stream, topk_idx,
+                       TK, expert_begin, El, nbits, table, rank);
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, stream, table, nchunks, El,
+                     pad_pow2, capacity, counts, cu_seqlens, src_of, w_perm, dev_error);
+  if (T > 0) {
+    const int nvec = H / 8;
+    int tpb = 256 / nvec;
+    if (tpb < 1) tpb = 1;
+    if (tpb * K > 256) tpb = 256 / K;
+    const int grid = (T + tpb - 1) / tpb;
+    hipLaunchKernelGGL(permute_scatter_kernel, dim3(grid), dim3(256), 0, stream, topk_idx, topk_w,
+                       hidden, T, K, H, expert_begin, El, tpb, capacity, table, rank, x_perm,
+                       row_of, src_of, w_perm, dev_error);
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace moe

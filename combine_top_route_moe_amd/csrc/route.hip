@@ -1,0 +1,127 @@
+// Top-k routing: one wavefront per token row.
+//
+// Each lane holds the logits of experts lane, lane+64, ... in registers; the
+// K winners are extracted one at a time by a wave-wide argmax with the
+// (larger value, then lower index) order, so slot 0 is the largest logit
+// and equal logits go to the lower expert index.  Selection compares the
+// float32 logits themselves; the weights are softmax terms over the chosen
+// slots (or over all experts) evaluated in double and stored as float.
+// Source: "[Kernel] DeepEP dispatch-combine kernel integration", review
+// threads (router ids and weights [T, K]); "Add MoE dispatch/combine fake
+// quantization for vLLM's DeepGEMM Mega-MoE", review thread on the buffer
+// check (padding slots carry -1).
+#include "common.h"
+
+namespace moe {
+
+// EPL: experts per lane (E <= 64 * EPL).
+template <int EPL>
+__global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ logits,
+                                                    const uint8_t* __restrict__ row_valid,
+                                                    int T, int E, int K, int renorm,
+                                                    int32_t* __restrict__ topk_idx,
+                                                    float* __restrict__ topk_w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  if (t >= T) return;
+  int32_t* out_idx = topk_idx + (int64_t)t * K;
+  float* out_w = topk_w + (int64_t)t * K;
+  if (row_valid && !row_valid[t]) {
+    for (int k = lane; k < K; k += kWave) {
+      out_idx[k] = -1;
+      out_w[k] = 0.0f;
+    }
+    return;
+  }
+
+  const float* row = logits + (int64_t)t * E;
+  float v[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    int e = lane + j * kWave;
+    v[j] = e < E ? row[e] : 0.0f;
+  }
+  uint32_t taken = 0;  // bit j: expert lane + 64 j already chosen (or absent)
+#pragma unroll
+  for (int j = 0; j < EPL; ++j)
+    if (lane + j * kWave >= E) taken |= 1u << j;
+
+  float sel_v = 0.0f;  // lane k keeps slot k's logit (k < 64)
+  int sel_e = -1;
+  float lmax = 0.0f;
+  for (int k = 0; k < K; ++k) {
+    // lane-local best among untaken: higher value, then lower index
+    bool has = false;
+    float bv = 0.0f;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      if (taken & (1u << j)) continue;
+      int e = lane + j * kWave;
+      if (!has || v[j] > bv || (v[j] == bv && e < be)) {
+        has = true;
+        bv = v[j];
+        be = e;
+      }
+    }
+    // wave argmax
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      float ov = __shfl_xor(bv, off, kWave);
+      int oe = __shfl_xor(be, off, kWave);
+      bool ohas = __shfl_xor((int)has, off, kWave) != 0;
+      if (ohas && (!has || ov > bv || (ov == bv && oe < be))) {
+        has = true;
+        bv = ov;
+        be = oe;
+      }
+    }
+    // every lane now holds the winner (bv, be)
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (k == 0) lmax = bv;
+    if (lane == k) {
+      sel_v = bv;
+      sel_e = be;
+    }
+  }
+
+  // weights: exp(l_k - l_max) / sum, in double
+  double num = 0.0;
+  if (lane < K) num = exp((double)sel_v - (double)lmax);
+  double den = 0.0;
+  if (renorm) {
+    den = num;
+  } else {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (lane + j * kWave < E) den += exp((double)v[j] - (double)lmax);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, kWave);
+  if (lane < K) {
+    out_idx[lane] = sel_e;
+    out_w[lane] = (float)(num / den);
+  }
+}
+
+int launch_route(const float* logits, const uint8_t* row_valid, int T, int E, int K, int renorm,
+                 int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+  const int waves = 4;
+  dim3 grid((T + waves - 1) / waves), block(waves * kWave);
+  int epl = (E + kWave - 1) / kWave;
+#define MOE_ROUTE_CASE(N)                                                                  \
+  if (epl <= N) {                                                                          \
+    hipLaunchKernelGGL(route_kernel<N>, grid, block, 0, stream, logits, row_valid, T, E, K, \
+                       renorm, topk_idx, topk_w);                                          \
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;                         \
+  }
+  MOE_ROUTE_CASE(1)
+  MOE_ROUTE_CASE(2)
+  MOE_ROUTE_CASE(4)
+  MOE_ROUTE_CASE(8)
+  MOE_ROUTE_CASE(16)
+#undef MOE_ROUTE_CASE
+  return MOE_ERR_UNSUPPORTED;
+}
+
+}  // namespace moe

@@ -1,0 +1,140 @@
+"""One MoE layer on one GPU: buffers owned once, the ABI calls in order.
+
+Order of the stages (titles of the pages they come from):
+  route           "[Kernel] DeepEP dispatch-combine kernel integration"
+  dispatch QDQ    "Add MoE dispatch/combine fake quantization for vLLM's
+                  DeepGEMM Mega-MoE", "How it works"
+  permute         "[Distributed][MoonEP] BF16 integration of MoonEP balanced
+                  EP backend", "Purpose"; "[Bugfix][MoE] Size the permute
+                  scratch from its inputs"
+  grouped FFN     MoonEP page, commit message adding the modular experts
+  shared expert   Mega-MoE page: a fused shared expert's slot, added last
+  combine (+QDQ)  Mega-MoE page, PR summary and "How it works"
+
+Every buffer is allocated once in the constructor (torch is the allocator);
+``forward`` only enqueues kernels on the current stream, never synchronizes
+and never allocates, so it can be timed back to back or captured in a graph.
+"""
+
+from __future__ import annotations
+
+from typing import Callable, Dict, Optional
+
+import torch
+
+from . import ops
+
+
+class MoELayer:
+    def __init__(self, T: int, H: int, E: int, K: int, I: int, device="cuda",
+                 shared_I: int = 0, dispatch_block: int = 0, combine_qdq: bool = False,
+                 pad_pow2: bool = False, renormalize: bool = True, expert_begin: int = 0,
+                 num_local_experts: Optional[int] = None):
+        self.T, self.H, self.E, self.K, self.I = T, H, E, K, I
+        self.shared_I = shared_I
+        self.dispatch_block = dispatch_block
+        self.combine_qdq = combine_qdq
+        self.pad_pow2 = pad_pow2
+        self.renormalize = renormalize
+        self.expert_begin = expert_begin
+        self.El = E if num_local_experts is None else num_local_experts
+        dev = torch.device(device)
+        self.device = dev
+        f32 = dict(dtype=torch.float32, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        bf = dict(dtype=torch.bfloat16, device=dev)
+
+        self.topk_idx = torch.empty(T, K, **i32)
+        self.topk_w = torch.empty(T, K, **f32)
+        self.hidden_q = torch.empty(T, H, **bf) if dispatch_block else None
+        self.capacity = ops.moe_permute_capacity(T, K, self.El, pad_pow2)
+        self.perm = ops.alloc_permuted(T, K, H, self.El, self.capacity, dev)
+        self.perm_ws = torch.empty(max(ops.moe_permute_workspace_bytes(T, K, self.El, pad_pow2), 1),
+                                   dtype=torch.uint8, device=dev)
+        self.ffn_ws = torch.empty(max(ops.moe_grouped_ffn_workspace_bytes(self.capacity, self.El, H, I), 1),
+                                  dtype=torch.uint8, device=dev)
+        self.y_perm = torch.empty(self.capacity, H, **bf)
+        self.out = torch.empty(T, H, **bf)
+        self.dev_error = torch.zeros(1, **i32)
+        self.combine_scale = torch.zeros(1, **f32) if combine_qdq else None
+        self.amax = torch.zeros(1, **f32)
+        if shared_I:
+            self.shared_out = torch.empty(T, H, **bf)
+            self.shared_cu = torch.tensor([0, T], **i32)
+            self.shared_counts = torch.tensor([T], **i32)
+            self.shared_ws = torch.empty(max(ops.moe_grouped_ffn_workspace_bytes(T, 1, H, shared_I), 1),
+                                         dtype=torch.uint8, device=dev)
+        else:
+            self.shared_out = None
+        self.w13 = self.w2 = self.shared_w13 = self.shared_w2 = None
+
+    # ------------------------------------------------------------------ weights
+    def set_weights(self, w13: torch.Tensor, w2: torch.Tensor,
+                    shared_w13: Optional[torch.Tensor] = None,
+                    shared_w2: Optional[torch.Tensor] = None) -> None:
+        """Device bf16 weights: w13 [E_l, 2I, H], w2 [E_l, H, I] (local experts)."""
+        self.w13, self.w2 = w13, w2
+        self.shared_w13, self.shared_w2 = shared_w13, shared_w2
+
+    # ------------------------------------------------------------------ stages
+    def forward(self, logits: torch.Tensor, hidden: torch.Tensor,
+                row_valid: Optional[torch.Tensor] = None,
+                mark: Optional[Callable[[str], None]] = None) -> torch.Tensor:
+        """Run the whole layer; ``mark(name)`` is called after each stage is
+        enqueued (the bench records events there)."""
+        m = mark or (lambda name: None)
+        ops.moe_route(logits, self.K, row_valid, self.renormalize, self.topk_idx, self.topk_w)
+        m("route")
+        x = hidden
+        if self.dispatch_block:
+            ops.moe_fake_quant_rows(hidden, self.hidden_q, None, ops.MOE_FQ_BLOCK,
+                                    self.dispatch_block)
+            x = self.hidden_q
+            m("dispatch_qdq")
+        p = self.perm
+        ops.moe_permute(self.topk_idx, self.topk_w, x, self.El, self.expert_begin, self.pad_pow2,
+                        self.capacity, p, self.perm_ws, self.dev_error)
+        m("permute")
+        ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, self.w13, self.w2, p.w_perm,
+                            self.y_perm, ops.MOE_FFN_GATE_UP, self.ffn_ws, self.dev_error)
+        m("ffn_gate_up")
+        ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, self.w13, self.w2, p.w_perm,
+                            self.y_perm, ops.MOE_FFN_DOWN, self.ffn_ws, self.dev_error)
+        m("ffn_down")
+        if self.shared_I:
+            ops.moe_grouped_ffn(hidden, self.shared_cu, self.shared_counts, self.shared_w13,
+                                self.shared_w2, None, self.shared_out, ops.MOE_FFN_ALL,
+                                self.shared_ws, self.dev_error)
+            m("shared_ffn")
+        ops.moe_combine(self.y_perm, p.row_of, self.T, self.K, self.shared_out,
+                        self.combine_scale if self.combine_qdq else None, self.out,
+                        self.dev_error)
+        m("combine")
+        return self.out
+
+    def calibrate_combine_scale(self, logits, hidden, row_valid=None) -> torch.Tensor:
+        """One-time max calibration of the constant combine-row scale: run the
+        layer without combine-row QDQ, take max|row| over the routed rows and
+        store amax/448 on the device."""
+        qdq = self.combine_qdq
+        self.combine_qdq = False
+        self.forward(logits, hidden, row_valid)
+        self.combine_qdq = qdq
+        self.amax.zero_()
+        ops.moe_fake_quant_rows(self.y_perm, None, self.perm.src_of, ops.MOE_FQ_PER_TENSOR,
+                                128, None, None, self.amax)
+        if self.combine_scale is None:
+            self.combine_scale = torch.zeros(1, dtype=torch.float32, device=self.device)
+        ops.moe_scale_from_amax(self.amax, self.combine_scale)
+        return self.combine_scale
+
+    def stage_outputs(self) -> Dict[str, torch.Tensor]:
+        p = self.perm
+        d = dict(topk_idx=self.topk_idx, topk_w=self.topk_w, counts=p.counts,
+                 cu_seqlens=p.cu_seqlens, x_perm=p.x_perm, row_of=p.row_of, src_of=p.src_of,
+                 w_perm=p.w_perm, y_perm=self.y_perm, out=self.out)
+        if self.hidden_q is not None:
+            d["hidden_q"] = self.hidden_q
+        if self.shared_out is not None:
+            d["shared"] = self.shared_out
+        return d

@@ -1,0 +1,202 @@
+"""Python binding of the C ABI: one function per entry point, same names.
+
+Argument marshalling only.  torch supplies device memory and the current
+stream; every step of the path runs in the HIP kernels of ``libmoe.so``.
+Outputs that the caller does not pass are allocated here with
+``torch.empty`` on the input's device.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from ._lib import load, check
+
+MOE_ROUTE_RENORM = 1
+MOE_PERMUTE_PAD_POW2 = 1
+MOE_FFN_GATE_UP, MOE_FFN_DOWN, MOE_FFN_ALL = 1, 2, 3
+MOE_FQ_PER_TENSOR, MOE_FQ_BLOCK = 0, 1
+MOE_DEVERR_ROW_RANGE, MOE_DEVERR_CAPACITY = 1, 2
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _want(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def moe_device_check(device: int = 0) -> int:
+    return load().moe_device_check(device)
+
+
+def moe_route(logits: torch.Tensor, k: int, row_valid: Optional[torch.Tensor] = None,
+              renormalize: bool = True, topk_idx=None, topk_w=None, stream=None):
+    _want(logits, torch.float32, "logits")
+    T, E = logits.shape
+    dev = logits.device
+    if row_valid is not None:
+        _want(row_valid, torch.uint8, "row_valid")
+    topk_idx = torch.empty(T, k, dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
+    topk_w = torch.empty(T, k, dtype=torch.float32, device=dev) if topk_w is None else topk_w
+    check("moe_route", load().moe_route(
+        _ptr(logits), _ptr(row_valid), T, E, k, MOE_ROUTE_RENORM if renormalize else 0,
+        _ptr(topk_idx), _ptr(topk_w), _stream(stream)))
+    return topk_idx, topk_w
+
+
+def moe_permute_capacity(T: int, K: int, num_local_experts: int, pad_pow2: bool = False) -> int:
+    return load().moe_permute_capacity(T, K, num_local_experts, MOE_PERMUTE_PAD_POW2 if pad_pow2 else 0)
+
+
+def moe_permute_workspace_bytes(T: int, K: int, num_local_experts: int, pad_pow2: bool = False) -> int:
+    return load().moe_permute_workspace_bytes(T, K, num_local_experts,
+                                              MOE_PERMUTE_PAD_POW2 if pad_pow2 else 0)
+
+
+@dataclass
+class Permuted:
+    counts: torch.Tensor
+    cu_seqlens: torch.Tensor
+    x_perm: torch.Tensor
+    row_of: torch.Tensor
+    src_of: torch.Tensor
+    w_perm: torch.Tensor
+
+
+def alloc_permuted(T: int, K: int, H: int, num_local_experts: int, capacity: int,
+                   device) -> Permuted:
+    i32 = dict(dtype=torch.int32, device=device)
+    return Permuted(
+        counts=torch.empty(num_local_experts, **i32),
+        cu_seqlens=torch.empty(num_local_experts + 1, **i32),
+        x_perm=torch.empty(capacity, H, dtype=torch.bfloat16, device=device),
+        row_of=torch.empty(T * K, **i32),
+        src_of=torch.empty(capacity, **i32),
+        w_perm=torch.empty(capacity, dtype=torch.float32, device=device),
+    )
+
+
+def moe_permute(topk_idx: torch.Tensor, topk_w: torch.Tensor, hidden: torch.Tensor,
+                num_local_experts: int, expert_begin: int = 0, pad_pow2: bool = False,
+                capacity: Optional[int] = None, out: Optional[Permuted] = None,
+                workspace: Optional[torch.Tensor] = None,
+                dev_error: Optional[torch.Tensor] = None, stream=None) -> Permuted:
+    _want(topk_idx, torch.int32, "topk_idx")
+    _want(topk_w, torch.float32, "topk_w")
+    _want(hidden, torch.bfloat16, "hidden")
+    T, K = topk_idx.shape
+    H = hidden.shape[1]
+    flags = MOE_PERMUTE_PAD_POW2 if pad_pow2 else 0
+    lib = load()
+    if capacity is None:
+        capacity = out.x_perm.shape[0] if out is not None else lib.moe_permute_capacity(
+            T, K, num_local_experts, flags)
+    if out is None:
+        out = alloc_permuted(T, K, H, num_local_experts, capacity, hidden.device)
+    ws_need = lib.moe_permute_workspace_bytes(T, K, num_local_experts, flags)
+    if workspace is None:
+        workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=hidden.device)
+    check("moe_permute", lib.moe_permute(
+        _ptr(topk_idx), _ptr(topk_w), _ptr(hidden), T, K, H, expert_begin, num_local_experts,
+        flags, capacity, _ptr(out.counts), _ptr(out.cu_seqlens), _ptr(out.x_perm),
+        _ptr(out.row_of), _ptr(out.src_of), _ptr(out.w_perm), _ptr(workspace),
+        workspace.numel(), _ptr(dev_error), _stream(stream)))
+    return out
+
+
+def moe_grouped_ffn_workspace_bytes(capacity: int, num_groups: int, H: int, I: int) -> int:
+    return load().moe_grouped_ffn_workspace_bytes(capacity, num_groups, H, I)
+
+
+def moe_grouped_ffn(x: torch.Tensor, cu_seqlens: torch.Tensor, counts: torch.Tensor,
+                    w13: torch.Tensor, w2: torch.Tensor, row_scale: Optional[torch.Tensor] = None,
+                    y: Optional[torch.Tensor] = None, stages: int = MOE_FFN_ALL,
+                    workspace: Optional[torch.Tensor] = None,
+                    dev_error: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    _want(x, torch.bfloat16, "x")
+    _want(w13, torch.bfloat16, "w13")
+    _want(w2, torch.bfloat16, "w2")
+    _want(cu_seqlens, torch.int32, "cu_seqlens")
+    _want(counts, torch.int32, "counts")
+    if row_scale is not None:
+        _want(row_scale, torch.float32, "row_scale")
+    capacity, H = x.shape
+    G, two_i, H2 = w13.shape
+    I = two_i // 2
+    if H2 != H or tuple(w2.shape) != (G, H, I):
+        raise ValueError("weight shapes do not match x")
+    if counts.numel() != G or cu_seqlens.numel() != G + 1:
+        raise ValueError("counts / cu_seqlens do not match the number of groups")
+    lib = load()
+    y = torch.empty(capacity, H, dtype=torch.bfloat16, device=x.device) if y is None else y
+    need = lib.moe_grouped_ffn_workspace_bytes(capacity, G, H, I)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    check("moe_grouped_ffn", lib.moe_grouped_ffn(
+        _ptr(x), _ptr(cu_seqlens), _ptr(counts), G, H, I, _ptr(w13), _ptr(w2), _ptr(row_scale),
+        _ptr(y), capacity, stages, _ptr(workspace), workspace.numel(), _ptr(dev_error),
+        _stream(stream)))
+    return y
+
+
+def moe_fake_quant_rows(inp: torch.Tensor, out: Optional[torch.Tensor] = None,
+                        row_src: Optional[torch.Tensor] = None, mode: int = MOE_FQ_BLOCK,
+                        block: int = 128, scale: Optional[torch.Tensor] = None,
+                        block_scales: Optional[torch.Tensor] = None,
+                        amax_out: Optional[torch.Tensor] = None, stream=None):
+    _want(inp, torch.bfloat16, "in")
+    n_rows, H = inp.shape
+    if out is None and (mode == MOE_FQ_BLOCK or scale is not None):
+        out = torch.empty_like(inp)
+    if row_src is not None:
+        _want(row_src, torch.int32, "row_src")
+    check("moe_fake_quant_rows", load().moe_fake_quant_rows(
+        _ptr(inp), _ptr(out), n_rows, H, _ptr(row_src), mode, block, _ptr(scale),
+        _ptr(block_scales), _ptr(amax_out), _stream(stream)))
+    return out
+
+
+def moe_scale_from_amax(amax: torch.Tensor, scale: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    _want(amax, torch.float32, "amax")
+    scale = torch.empty(1, dtype=torch.float32, device=amax.device) if scale is None else scale
+    check("moe_scale_from_amax", load().moe_scale_from_amax(_ptr(amax), _ptr(scale), _stream(stream)))
+    return scale
+
+
+def moe_combine(rows: torch.Tensor, row_of: torch.Tensor, T: int, K: int,
+                shared: Optional[torch.Tensor] = None, qdq_scale: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, dev_error: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    _want(rows, torch.bfloat16, "rows")
+    _want(row_of, torch.int32, "row_of")
+    num_rows, H = rows.shape
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=rows.device) if out is None else out
+    check("moe_combine", load().moe_combine(
+        _ptr(rows), num_rows, _ptr(row_of), _ptr(shared), T, K, H, _ptr(qdq_scale), _ptr(out),
+        _ptr(dev_error), _stream(stream)))
+    return out
+
+
+def moe_copy_bytes(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst smaller than src")
+    check("moe_copy_bytes", load().moe_copy_bytes(_ptr(src), _ptr(dst), n, _stream(stream)))

@@ -1,0 +1,229 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) MoE-layer hot path.
+ *
+ * The layer: route each token to its top-k experts, optionally fake-quantize
+ * the expert inputs to FP8, permute the routed (token, slot) rows into
+ * expert-contiguous segments, run every expert's SwiGLU FFN over its segment
+ * as a grouped GEMM, optionally fake-quantize the per-(token, slot) rows, and
+ * combine them in a fixed order.
+ *
+ * Conventions for every entry point
+ *   - Tensor arguments are DEVICE pointers to contiguous row-major arrays on
+ *     the current HIP device; bf16 tensors are passed as uint16_t bit
+ *     patterns.  bf16 rows must start on 16-byte boundaries (guaranteed when
+ *     the base pointer is 16-byte aligned and H is a multiple of 128).
+ *   - The caller owns every buffer.  No entry point allocates, frees or
+ *     synchronizes; each only enqueues kernels on `stream` (a hipStream_t;
+ *     NULL is the default stream), so every call can be captured into a
+ *     HIP graph.  Size queries tell the caller how much workspace to own.
+ *   - Argument errors that the host can see from scalars and pointers return
+ *     a negative status synchronously and enqueue nothing.
+ *   - Errors that depend on device data (an out-of-range row index, a
+ *     segment larger than the buffer) never trap: the offending element is
+ *     skipped and, when `dev_error` is non-NULL, the first such error's
+ *     MOE_DEVERR_* code is stored into *dev_error (only if it was 0).  The
+ *     caller zeroes *dev_error and reads it back whenever it chooses.
+ *   - Calls are stateless and re-entrant; two calls race only if they share
+ *     an output or workspace buffer on concurrent streams.
+ *
+ * Sources (titles of the pages the operations come from):
+ *   [P1] "Add MoE dispatch/combine fake quantization for vLLM's DeepGEMM
+ *        Mega-MoE" (NVIDIA Model-Optimizer pull request)
+ *   [P2] "[Kernel] DeepEP dispatch-combine kernel integration" (vLLM)
+ *   [P3] "[Distributed][MoonEP] BF16 integration of MoonEP balanced EP
+ *        backend" (vLLM)
+ *   [P4] "[Bugfix][MoE] Size the permute scratch from its inputs" (vLLM)
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes (return values) ------------------------------------- */
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null required pointer, negative size, K > E */
+  MOE_ERR_UNSUPPORTED = -2, /* shape outside what the kernels handle (e.g.
+                               H or I not a multiple of 128, E > 1024)     */
+  MOE_ERR_WORKSPACE = -3,   /* workspace smaller than the size query says */
+  MOE_ERR_HIP = -4,         /* a HIP runtime call or launch failed        */
+  MOE_ERR_DEVICE = -5       /* the current device is not a gfx950 GPU     */
+};
+
+/* ---- device error word codes (first error wins) ----------------------- */
+enum {
+  MOE_DEVERR_ROW_RANGE = 1, /* a row index points outside its buffer       */
+  MOE_DEVERR_CAPACITY = 2   /* the segments need more rows than `capacity` */
+};
+
+/* ---- flags -------------------------------------------------------------- */
+enum { MOE_ROUTE_RENORM = 1 };        /* moe_route: renormalise over top-k */
+enum { MOE_PERMUTE_PAD_POW2 = 1 };    /* moe_permute: pow2 segment buckets */
+enum { MOE_FFN_GATE_UP = 1,           /* moe_grouped_ffn stages            */
+       MOE_FFN_DOWN = 2,
+       MOE_FFN_ALL = 3 };
+enum { MOE_FQ_PER_TENSOR = 0,         /* moe_fake_quant_rows modes         */
+       MOE_FQ_BLOCK = 1 };
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* moe_status_string(int status);
+
+/* Check that `device` is a gfx950 GPU this library was built for.
+ * Returns MOE_OK, MOE_ERR_DEVICE (another architecture) or MOE_ERR_HIP.
+ * A host that cannot run the path fails here with a clear status rather
+ * than inside a kernel launch ([P3], review thread on the system-support
+ * probe run at backend selection). */
+int moe_device_check(int device);
+
+/* ---- route --------------------------------------------------------------
+ * Per token t with row_valid[t] != 0 (all tokens when row_valid is NULL):
+ * choose the K experts with the largest float32 logits — slot 0 the
+ * largest, ties to the lower expert index — and give them the weights
+ * exp(l_k - l_max) / sum_j exp(l_j - l_max), the sum running over the K
+ * chosen experts with MOE_ROUTE_RENORM, else over all E experts (computed
+ * in double, stored as float).  Padding tokens get topk_idx = -1 and
+ * topk_w = 0 in every slot ([P1] review thread on the buffer check:
+ * `valid = topk_idx >= 0`; [P2] review threads: router ids and weights
+ * are [T, K] per token; the workloads' softmax -> top-k -> renormalise).
+ *
+ *   logits    [T, E] float32        row_valid  [T] uint8 or NULL
+ *   topk_idx  [T, K] int32 (out)    topk_w     [T, K] float32 (out)
+ * Requires 1 <= K <= min(E, 32), E <= 1024.  T = 0 enqueues nothing.
+ * NaN logits are unsupported (their slot choice is unspecified). */
+int moe_route(const float* logits, const uint8_t* row_valid, int T, int E, int K,
+              int flags, int32_t* topk_idx, float* topk_w, void* stream);
+
+/* ---- permute ------------------------------------------------------------
+ * Group the routed (token, slot) pairs of the local experts
+ * [expert_begin, expert_begin + num_local_experts) into expert-contiguous
+ * segments ([P3] "Purpose": tokens arrive grouped per expert as [NvS, H]
+ * plus cu_seqlens; [P4] PR summary and "Details": index metadata over the
+ * expanded rows, sized from the inputs received, power-of-two receive
+ * buckets, the permuted hidden states in a caller buffer).
+ *
+ * Slot (t, k) with flat index i = t*K + k is routed to local expert
+ * e = topk_idx[i] - expert_begin when 0 <= e < num_local_experts; any other
+ * value (negative = padding, or another rank's expert) is not routed here.
+ *   counts[e]      number of rows routed to e
+ *   cu_seqlens[e]  first row of segment e; segment sizes are counts[e], or
+ *                  next_pow2(counts[e]) (0 stays 0) with MOE_PERMUTE_PAD_POW2;
+ *                  cu_seqlens[num_local_experts] = rows used
+ *   rows of a segment: its routed slots in ascending flat index i, then the
+ *                  pow2 padding rows
+ *   row_of[i]      permuted row of slot i, or -1 when not routed here
+ *   src_of[r]      flat slot index of row r, or -1 for a padding row
+ *   w_perm[r]      topk_w[src_of[r]], 0 for a padding row
+ *   x_perm[r, :]   hidden[src_of[r] / K, :]; padding rows are not written
+ *
+ *   topk_idx [T, K] int32   topk_w [T, K] float32   hidden [T, H] bf16
+ *   counts [E_l] int32, cu_seqlens [E_l + 1] int32, row_of [T*K] int32,
+ *   src_of [capacity] int32, w_perm [capacity] float32,
+ *   x_perm [capacity, H] bf16 — all outputs.
+ * `capacity` is the number of rows the caller allocated in x_perm, src_of
+ * and w_perm; moe_permute_capacity() is always enough.  If the segments
+ * need more rows, rows at or past `capacity` are not written and
+ * MOE_DEVERR_CAPACITY is raised.  `workspace` holds
+ * moe_permute_workspace_bytes() bytes of scratch (contents on entry are
+ * ignored).  Requires H % 128 == 0, 1 <= num_local_experts <= 1024. */
+int64_t moe_permute_capacity(int T, int K, int num_local_experts, int flags);
+size_t moe_permute_workspace_bytes(int T, int K, int num_local_experts, int flags);
+int moe_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t* hidden,
+                int T, int K, int H, int expert_begin, int num_local_experts, int flags,
+                int64_t capacity, int32_t* counts, int32_t* cu_seqlens, uint16_t* x_perm,
+                int32_t* row_of, int32_t* src_of, float* w_perm, void* workspace,
+                size_t workspace_bytes, int32_t* dev_error, void* stream);
+
+/* ---- grouped SwiGLU FFN -------------------------------------------------
+ * For every group g with n = counts[g] rows starting at row c = cu_seqlens[g]
+ * of x ([P3] commit message adding the modular experts: gate, up and down
+ * grouped matmuls over the cu_seqlens segments, route weights applied before
+ * the down projection, empty segments skipped; [P2] review thread on the
+ * DeepEP + DeepGEMM test: w1 holds 2n rows, gate and up):
+ *   h      = x[c:c+n] @ w13[g]^T            (float32 accumulate)  [n, 2I]
+ *   a      = bf16( silu(h[:, :I]) * h[:, I:] )                    [n, I]
+ *   y[c:c+n] = bf16( row_scale[c:c+n] * (a @ w2[g]^T) )           [n, H]
+ * row_scale NULL means 1.  Rows of a segment past counts[g] (pow2 padding)
+ * are neither read nor written.  The shared expert is the case
+ * num_groups = 1, counts = {T}, cu_seqlens = {0, T}, row_scale = NULL.
+ *
+ *   x [capacity, H] bf16;  w13 [G, 2I, H] bf16 (gate rows [0, I), up rows
+ *   [I, 2I)); w2 [G, H, I] bf16; row_scale [capacity] float32 or NULL;
+ *   y [capacity, H] bf16 (out); cu_seqlens [G + 1], counts [G] int32.
+ * `stages` selects MOE_FFN_GATE_UP (writes `a` into the workspace),
+ * MOE_FFN_DOWN (reads it) or MOE_FFN_ALL; a DOWN-only call must get the
+ * workspace a GATE_UP call with the same segments filled.  Segments that
+ * reach past `capacity` are skipped and raise MOE_DEVERR_ROW_RANGE.
+ * Requires H % 128 == 0, I % 128 == 0, 1 <= G <= 1024. */
+size_t moe_grouped_ffn_workspace_bytes(int64_t capacity, int num_groups, int H, int I);
+int moe_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32_t* counts,
+                    int num_groups, int H, int I, const uint16_t* w13, const uint16_t* w2,
+                    const float* row_scale, uint16_t* y, int64_t capacity, int stages,
+                    void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream);
+
+/* ---- FP8 fake-quant of bf16 rows ---------------------------------------
+ * QDQ to OCP E4M3FN and back ([P1] PR summary and "How it works": the
+ * dispatch quantizer fake-quantizes the experts' input tokens, the combine
+ * quantizer the router-weighted per-(token, slot) BF16 rows with a
+ * calibrated (max) or constant global scale; [P2] review thread on the
+ * low-latency dispatch: FP8 with block scales):
+ *   x' = bf16( fl32( e4m3( clamp(fl32(x / s), -448, 448) ) * s ) )
+ * with IEEE float32 division and multiplication, e4m3 and bf16 both
+ * round-to-nearest-even.
+ *   MOE_FQ_BLOCK:      s = fl32(amax / 448) per row and per `block`
+ *                      contiguous channels; an all-zero block gives +0;
+ *                      block_scales [n_rows, H/block] float32 (or NULL)
+ *                      receives s.  `scale` is ignored.
+ *   MOE_FQ_PER_TENSOR: s = *scale (a device scalar, s > 0).  With scale ==
+ *                      NULL nothing is written to `out` (calibration only).
+ * Rows with row_src != NULL and row_src[r] < 0 are skipped: copied from
+ * `in` unchanged when out != in, else untouched.  When amax_out != NULL,
+ * max |x| over the rows not skipped is max-accumulated into *amax_out
+ * (the caller sets it to 0 once; repeated calls give the running max, the
+ * calibrated amax of [P1] "Testing").  in == out (in place) is allowed.
+ * Requires H % block == 0 and block == 128 in block mode. */
+int moe_fake_quant_rows(const uint16_t* in, uint16_t* out, int64_t n_rows, int H,
+                        const int32_t* row_src, int mode, int block, const float* scale,
+                        float* block_scales, float* amax_out, void* stream);
+
+/* scale[0] = fl32(amax[0] / 448) (IEEE division) on the device: turns a
+ * calibrated amax into the constant per-tensor E4M3FN scale ([P1] "How it
+ * works": a calibrated (max) or constant global combine scale; the
+ * workloads' 1/448 * max|row|).  Both are device scalars. */
+int moe_scale_from_amax(const float* amax, float* scale, void* stream);
+
+/* ---- combine ------------------------------------------------------------
+ * out[t, :] = bf16( ((+0 + r_{t,k0}) + r_{t,k1}) + ... + shared[t, :] )
+ * over the valid slots k0 < k1 < ... of token t (row_of[t*K + k] >= 0),
+ * each r_{t,k} = rows[row_of[t*K + k], :], every add one IEEE float32
+ * add in exactly this order, then one round-to-nearest-even to bf16; the
+ * shared expert's row is added last and never quantized ([P1] PR summary
+ * and "How it works": ascending slot, FP32 from zero, one BF16 rounding,
+ * a fused shared expert's slot last and unquantized).
+ * row_qdq_scale != NULL fake-quantizes each routed row with that per-tensor
+ * device scalar before it is added (the same bits as moe_fake_quant_rows
+ * in MOE_FQ_PER_TENSOR mode followed by this call).
+ *   rows [num_rows, H] bf16; row_of [T*K] int32; shared [T, H] bf16 or
+ *   NULL; out [T, H] bf16 (out).  row_of entries >= num_rows are skipped
+ *   and raise MOE_DEVERR_ROW_RANGE.  A token with no valid slot and no
+ *   shared row gets +0.  Requires H % 128 == 0. */
+int moe_combine(const uint16_t* rows, int64_t num_rows, const int32_t* row_of,
+                const uint16_t* shared, int T, int K, int H, const float* row_qdq_scale,
+                uint16_t* out, int32_t* dev_error, void* stream);
+
+/* ---- streaming copy -----------------------------------------------------
+ * dst[0:bytes) = src[0:bytes) with 16-byte vector loads and stores: the
+ * plain copy kernel whose measured time and HBM byte counters calibrate the
+ * bandwidth and counter figures of the kernels above.  `bytes` must be a
+ * multiple of 16 and both pointers 16-byte aligned. */
+int moe_copy_bytes(const void* src, void* dst, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,338 @@
+"""Per-stage parity of the HIP kernels (through the C ABI) with the oracle.
+
+Bit-exact: top-k indices, permute counts / cu_seqlens / maps / rows, FP8
+fake-quant outputs and scales, combine outputs given identical rows.
+Router weights: rtol 1e-6.  Grouped FFN: Frobenius relative error <= 2e-2
+against the float64 oracle over the valid rows.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from combine_top_route_moe_amd import ops
+from oracle.numerics import bf16_bits_to_f32, f32_to_bf16_bits
+from tests.gpu_util import need_gpu, dev_bf16, host_bits, dev, host, rel_err, stacked_weights
+
+pytestmark = pytest.mark.gpu
+
+FFN_TOL = 2e-2
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def setup_module(module):
+    need_gpu()
+    assert ops.moe_device_check(0) == 0, "not a gfx950 device"
+
+
+# ---------------------------------------------------------------------- route
+
+def _route_case(logits, k, row_valid=None, renorm=True):
+    ref_idx, ref_w = oracle.route(logits, row_valid, k, renorm)
+    idx, w = ops.moe_route(dev(logits), k, None if row_valid is None else dev(row_valid), renorm)
+    np.testing.assert_array_equal(host(idx), ref_idx)
+    np.testing.assert_allclose(host(w), ref_w, rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("name", list(workloads.CONFIGS))
+def test_route_workloads(name):
+    cfg = workloads.CONFIGS[name]
+    _route_case(workloads.logits(cfg), cfg.K, workloads.row_valid(cfg))
+
+
+@pytest.mark.parametrize("T,E,K", [(1, 1, 1), (7, 3, 2), (33, 100, 5), (64, 1024, 32), (300, 256, 8), (5, 65, 32)])
+def test_route_shapes_and_ties(T, E, K):
+    rng = np.random.default_rng(T * 1000 + E + K)
+    logits = rng.integers(-3, 4, size=(T, E)).astype(np.float32)    # many ties
+    _route_case(logits, K)
+    logits2 = rng.standard_normal((T, E)).astype(np.float32)
+    _route_case(logits2, K, renorm=False)
+    valid = (rng.random(T) > 0.3).astype(np.uint8)
+    _route_case(logits2, K, valid)
+
+
+def test_route_rejects_bad_args():
+    x = torch.zeros(4, 8, device="cuda")
+    with pytest.raises(RuntimeError):
+        ops.moe_route(x, 9)
+
+
+# ----------------------------------------------------------------- fake quant
+
+def _all_finite_bf16_rows(H=128):
+    bits = np.arange(2 ** 16, dtype=np.uint32).astype(np.uint16)
+    f = bf16_bits_to_f32(bits)
+    bits = bits[np.isfinite(f)]
+    pad = (-len(bits)) % H
+    bits = np.concatenate([bits, np.zeros(pad, np.uint16)])
+    return bits.reshape(-1, H)
+
+
+def test_fake_quant_block_exhaustive():
+    rows = _all_finite_bf16_rows(128)
+    rng = np.random.default_rng(0)
+    rows = rows[rng.permutation(len(rows))]          # mix magnitudes across blocks
+    rows = np.concatenate([rows, rng.permutation(rows.reshape(-1)).reshape(rows.shape)])
+    rows = rows.reshape(-1, 512)                     # 4 blocks per row
+    ref, ref_s = oracle.fake_quant_block(rows, 128)
+    scales = torch.empty(rows.shape[0], 4, dtype=torch.float32, device="cuda")
+    out = ops.moe_fake_quant_rows(dev_bf16(rows), block_scales=scales)
+    np.testing.assert_array_equal(host_bits(out), ref)
+    np.testing.assert_array_equal(host(scales), ref_s)
+
+
+@pytest.mark.parametrize("s", [1.0, 2.0 ** -7, 0.0123, 3.7e-3, 1.0 / 448, 0.3, 1e-30, 7e20])
+def test_fake_quant_per_tensor_exhaustive(s):
+    rows = _all_finite_bf16_rows(128)
+    scale = torch.tensor([s], dtype=torch.float32, device="cuda")
+    out = ops.moe_fake_quant_rows(dev_bf16(rows), mode=ops.MOE_FQ_PER_TENSOR, scale=scale)
+    ref = oracle.fake_quant_per_tensor(rows, np.float32(s))
+    np.testing.assert_array_equal(host_bits(out), ref)
+
+
+def test_fake_quant_row_skip_inplace_and_amax():
+    rng = np.random.default_rng(1)
+    x = f32_to_bf16_bits((rng.standard_normal((37, 256)) * 5).astype(np.float32))
+    x[3, :128] = 0
+    src = np.where(rng.random(37) < 0.3, -1, np.arange(37)).astype(np.int32)
+    mask = src >= 0
+    # block mode, out of place, skipped rows copied
+    ref, ref_s = oracle.fake_quant_block(x, 128, row_mask=mask)
+    scales = torch.full((37, 2), 99.0, device="cuda")
+    amax = torch.zeros(1, device="cuda")
+    out = ops.moe_fake_quant_rows(dev_bf16(x), row_src=dev(src), block_scales=scales, amax_out=amax)
+    np.testing.assert_array_equal(host_bits(out), ref)
+    np.testing.assert_array_equal(host(scales), ref_s)
+    assert host(amax)[0] == oracle.calibrate_amax(x, mask)
+    # per-tensor in place: skipped rows untouched
+    s = np.float32(0.01)
+    xd = dev_bf16(x)
+    ops.moe_fake_quant_rows(xd, xd, dev(src), ops.MOE_FQ_PER_TENSOR, scale=torch.tensor([s], device="cuda"))
+    np.testing.assert_array_equal(host_bits(xd), oracle.fake_quant_per_tensor(x, s, row_mask=mask))
+    # calibration only, running max over two calls
+    amax.zero_()
+    ops.moe_fake_quant_rows(dev_bf16(x[:10]), None, None, ops.MOE_FQ_PER_TENSOR, amax_out=amax)
+    ops.moe_fake_quant_rows(dev_bf16(x[10:]), None, None, ops.MOE_FQ_PER_TENSOR, amax_out=amax)
+    assert host(amax)[0] == oracle.calibrate_amax(x)
+    sc = ops.moe_scale_from_amax(amax)
+    assert host(sc)[0] == np.float32(oracle.calibrate_amax(x) / np.float32(448))
+
+
+# -------------------------------------------------------------------- permute
+
+def _permute_case(idx, w, hid, El, begin=0, pow2=False, capacity=None, check_rows=None):
+    T, K = idx.shape
+    ref = oracle.permute(idx, w, hid, El, begin, pow2)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    p = ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), El, begin, pow2, capacity, dev_error=err)
+    assert host(err)[0] == 0
+    np.testing.assert_array_equal(host(p.counts), ref["counts"])
+    np.testing.assert_array_equal(host(p.cu_seqlens), ref["cu_seqlens"])
+    np.testing.assert_array_equal(host(p.row_of), ref["row_of"])
+    used = int(ref["cu_seqlens"][-1])
+    np.testing.assert_array_equal(host(p.src_of)[:used], ref["src_of"])
+    np.testing.assert_array_equal(host(p.w_perm)[:used], ref["w_perm"])
+    valid = np.nonzero(ref["src_of"] >= 0)[0]
+    if check_rows is not None and len(valid) > check_rows:
+        valid = np.sort(np.random.default_rng(0).choice(valid, check_rows, replace=False))
+    got = host_bits(p.x_perm[torch.from_numpy(valid).cuda()]) if len(valid) else np.zeros((0, hid.shape[1]), np.uint16)
+    np.testing.assert_array_equal(got, ref["x_perm"][valid])
+    return ref
+
+
+@pytest.mark.parametrize("name", list(workloads.CONFIGS))
+def test_permute_workloads(name):
+    cfg = workloads.CONFIGS[name]
+    idx, w = oracle.route(workloads.logits(cfg), workloads.row_valid(cfg), cfg.K)
+    hid = workloads.hidden(cfg)
+    ref = _permute_case(idx, w, hid, cfg.E, 0, cfg.pad_pow2,
+                        check_rows=None if cfg.T <= 512 else 4096)
+    if name == "prefill":
+        assert int(ref["cu_seqlens"][-1]) == 131072
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_permute_edge_cases(seed):
+    rng = np.random.default_rng(seed)
+    T = [1, 2, 37, 100, 513, 1025, 3000, 0][seed]
+    K = [1, 2, 4, 8, 3, 8, 6, 2][seed]
+    E = [1, 3, 32, 64, 7, 256, 1024, 4][seed]
+    idx = rng.integers(-1, E, size=(T, K)).astype(np.int32)
+    if seed == 3:
+        idx[:] = 5                                   # one expert gets everything
+    if seed == 4:
+        idx[:] = -1                                  # all padding
+    w = rng.random((T, K)).astype(np.float32)
+    hid = rng.integers(0, 2 ** 16, size=(T, 128), dtype=np.uint64).astype(np.uint16)
+    for pow2 in (False, True):
+        _permute_case(idx, w, hid, E, 0, pow2)
+    if E > 2:                                         # an expert-parallel share
+        _permute_case(idx, w, hid, E // 2, E // 4, True)
+
+
+def test_permute_capacity_overflow_is_flagged_not_written():
+    rng = np.random.default_rng(9)
+    T, K, E, H = 64, 4, 8, 128
+    idx = rng.integers(0, E, size=(T, K)).astype(np.int32)
+    w = rng.random((T, K)).astype(np.float32)
+    hid = rng.integers(0, 2 ** 16, size=(T, H), dtype=np.uint64).astype(np.uint16)
+    cap = 100                                        # 256 rows are needed
+    guard = 16
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = ops.alloc_permuted(T, K, H, E, cap + guard, "cuda")
+    out.x_perm.fill_(0)
+    out.src_of.fill_(-7)
+    ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), E, 0, False, cap, out, dev_error=err)
+    assert host(err)[0] == ops.MOE_DEVERR_CAPACITY
+    assert np.all(host(out.src_of)[cap:] == -7)       # nothing written past capacity
+    assert np.all(host_bits(out.x_perm[cap:]) == 0)
+    ro = host(out.row_of)
+    assert ro.max() < cap
+
+
+# -------------------------------------------------------------------- combine
+
+def _combine_case(rows, row_of, T, K, shared=None, scale=None):
+    rows_q = rows
+    if scale is not None:
+        mask = np.zeros(len(rows), bool)
+        mask[row_of[row_of >= 0]] = True
+        rows_q = oracle.fake_quant_per_tensor(rows, np.float32(scale), row_mask=mask)
+    ref = oracle.combine(rows_q, row_of, T, K, shared)
+    out = ops.moe_combine(dev_bf16(rows), dev(row_of), T, K,
+                          None if shared is None else dev_bf16(shared),
+                          None if scale is None else torch.tensor([scale], dtype=torch.float32, device="cuda"))
+    np.testing.assert_array_equal(host_bits(out), ref)
+
+
+def test_combine_golden_cases():
+    with open(os.path.join(GOLDEN, "combine_order.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        n = len(case["rows"])
+        H = 128
+        K = max(n, 1)
+        rows = np.zeros((K, H), np.uint16)
+        for i, h in enumerate(case["rows"]):
+            rows[i, :] = int(h, 16)
+        row_of = np.array(list(range(n)) + [-1] * (K - n), np.int32)
+        shared = None if case["shared"] is None else np.full((1, H), int(case["shared"], 16), np.uint16)
+        out = ops.moe_combine(dev_bf16(rows), dev(row_of), 1, K, None if shared is None else dev_bf16(shared))
+        assert np.all(host_bits(out) == int(case["out"], 16)), case["what"]
+
+
+@pytest.mark.parametrize("T,K,H", [(1, 1, 128), (50, 8, 256), (512, 8, 2048), (37, 3, 7168)])
+def test_combine_random_rows(T, K, H):
+    rng = np.random.default_rng(T + K + H)
+    R = T * K + 5
+    vals = rng.standard_normal((R, H)).astype(np.float32) * rng.choice([1e-3, 1.0, 1e3], (R, 1)).astype(np.float32)
+    rows = f32_to_bf16_bits(vals)
+    rows[0, :16] = np.arange(1, 17, dtype=np.uint16)          # subnormals
+    rows[1, :16] = np.arange(0x8001, 0x8011, dtype=np.uint16)
+    perm = rng.permutation(R)[: T * K].astype(np.int32)
+    row_of = np.where(rng.random(T * K) < 0.2, -1, perm).astype(np.int32)
+    shared = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    _combine_case(rows, row_of, T, K)
+    _combine_case(rows, row_of, T, K, shared)
+    _combine_case(rows, row_of, T, K, shared, scale=float(np.float32(3.0 / 448)))
+    # slot-major [K, T, H] layout: row_of[t*K + k] = k*T + t
+    t_idx, k_idx = np.divmod(np.arange(T * K), K)
+    _combine_case(rows, (k_idx * T + t_idx).astype(np.int32), T, K, shared)
+
+
+def test_combine_row_out_of_range_flagged():
+    rows = np.zeros((4, 128), np.uint16)
+    row_of = np.array([0, 9, 1, -1], np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ops.moe_combine(dev_bf16(rows), dev(row_of), 2, 2, dev_error=err)
+    assert host(err)[0] == ops.MOE_DEVERR_ROW_RANGE
+
+
+# ---------------------------------------------------------------- grouped FFN
+
+def _ffn_case(cfg, idx, w, hid, host_w, w13, w2, pow2=False, experts=None, tol=FFN_TOL):
+    ref = oracle.permute(idx, w, hid, cfg.E, 0, pow2)
+    p = ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), cfg.E, 0, pow2)
+    y = torch.zeros(p.x_perm.shape, dtype=torch.bfloat16, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13, w2, p.w_perm, y, dev_error=err)
+    assert host(err)[0] == 0
+    cu, cnt = ref["cu_seqlens"], ref["counts"]
+    experts = range(cfg.E) if experts is None else experts
+    worst = 0.0
+    for e in experts:
+        n = int(cnt[e])
+        if n == 0:
+            continue
+        r0 = int(cu[e])
+        x = oracle.bf16_bits_to_f64(ref["x_perm"][r0:r0 + n])
+        want = oracle.expert_ffn(x, *host_w[e]) * ref["w_perm"][r0:r0 + n, None].astype(np.float64)
+        got = bf16_bits_to_f32(host_bits(y[r0:r0 + n]))
+        err_e = rel_err(got, want)
+        worst = max(worst, err_e)
+        assert err_e <= tol, (e, n, err_e)
+        seg_end = int(cu[e + 1])
+        if seg_end > r0 + n:                          # pow2 padding rows are never written
+            assert np.all(host_bits(y[r0 + n:seg_end]) == 0)
+    return worst
+
+
+@pytest.mark.parametrize("m,skew", [(1, 1.0), (37, 1.0), (100, 8.0), (512, 8.0), (512, 1.0)])
+def test_ffn_page_shapes(m, skew):
+    """The MoonEP test's shapes: m tokens, top-4 of 32 experts, router skew."""
+    cfg = workloads.MoEConfig("t", 9, T=m, H=256, E=32, K=4, I=128, hot_experts=8 if skew > 1 else 0)
+    lg = workloads.logits(cfg)
+    idx, w = oracle.route(lg, None, 4)
+    hid = workloads.hidden(cfg)
+    w13, w2, host_w = stacked_weights(cfg)
+    _ffn_case(cfg, idx, w, hid, host_w, w13, w2)
+    _ffn_case(cfg, idx, w, hid, host_w, w13, w2, pow2=True)
+
+
+@pytest.mark.parametrize("name", ["tiny", "balanced", "skewed"])
+def test_ffn_workloads(name):
+    cfg = workloads.CONFIGS[name]
+    idx, w = oracle.route(workloads.logits(cfg), None, cfg.K)
+    hid = workloads.hidden(cfg)
+    w13, w2, host_w = stacked_weights(cfg)
+    worst = _ffn_case(cfg, idx, w, hid, host_w, w13, w2)
+    print(f"{name}: worst per-expert rel err {worst:.3e}")
+
+
+def test_ffn_one_big_segment_many_tiles():
+    """One expert with 1000 rows: 8 m-tiles, ragged tail."""
+    cfg = workloads.MoEConfig("t", 11, T=1000, H=512, E=4, K=1, I=256)
+    idx = np.full((1000, 1), 2, np.int32)
+    w = np.ones((1000, 1), np.float32)
+    hid = workloads.hidden(cfg)
+    w13, w2, host_w = stacked_weights(cfg)
+    _ffn_case(cfg, idx, w, hid, host_w, w13, w2)
+
+
+def test_ffn_stage_split_equals_all():
+    cfg = workloads.MoEConfig("t", 12, T=200, H=256, E=8, K=2, I=256)
+    idx, w = oracle.route(workloads.logits(cfg), None, 2)
+    hid = workloads.hidden(cfg)
+    w13, w2, _ = stacked_weights(cfg)
+    p = ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), cfg.E)
+    ws = torch.empty(ops.moe_grouped_ffn_workspace_bytes(p.x_perm.shape[0], 8, 256, 256), dtype=torch.uint8, device="cuda")
+    y1 = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13, w2, p.w_perm)
+    y2 = torch.empty_like(y1)
+    ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13, w2, p.w_perm, y2, ops.MOE_FFN_GATE_UP, ws)
+    ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13, w2, p.w_perm, y2, ops.MOE_FFN_DOWN, ws)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_ffn_deterministic():
+    cfg = workloads.CONFIGS["tiny"]
+    idx, w = oracle.route(workloads.logits(cfg), None, cfg.K)
+    w13, w2, _ = stacked_weights(cfg)
+    p = ops.moe_permute(dev(idx), dev(w), dev_bf16(workloads.hidden(cfg)), cfg.E)
+    a = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13, w2, p.w_perm)
+    b = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13, w2, p.w_perm)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))

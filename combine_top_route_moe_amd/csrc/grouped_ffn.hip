@@ -29,9 +29,9 @@
 // m-tiles), and each workgroup decodes its tile from the device-side
 // counts (no host sync): tiles are numbered expert by expert, n-tile by
 // n-tile, m-tile fastest, so the m-tiles that share one weight panel run
-// back to back.  Consecutive tile numbers are mapped to the same XCD
-// (workgroup ids are dealt round-robin over the 8 XCDs) so that a weight
-// panel and an activation panel are fetched once into that XCD's L2.
+// back to back, and runs of consecutive tile numbers are mapped to one XCD
+// so that a weight panel and an activation panel are fetched once into that
+// XCD's L2.
 // Workgroups past the last tile exit at once.  MFMA sub-tiles lying wholly
 // past the segment's last row are skipped.
 #include "common.h"
@@ -40,6 +40,7 @@ namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 16-byte staging
 
 constexpr int kBM = 128;
 constexpr int kBN = 128;
@@ -48,10 +49,16 @@ constexpr int kLdsStride = kBK + 8;  // bf16 elements per LDS row
 constexpr int kThreads = 256;
 constexpr int kNumXcd = 8;
 
-__device__ __forceinline__ int xcd_remap(int bid, int nb) {
+// Workgroup ids are dealt round-robin over the 8 XCDs.  Remap them so that
+// runs of kXcdChunk consecutive tile numbers land on one XCD (they share
+// weight and activation panels through its L2) while successive runs go to
+// successive XCDs (the work, including the empty tail, stays balanced).
+// The grid is a multiple of 8 * kXcdChunk, which makes this a bijection.
+constexpr int kXcdChunk = 16;
+__device__ __forceinline__ int xcd_remap(int bid) {
   const int xcd = bid % kNumXcd, local = bid / kNumXcd;
-  const int per = nb / kNumXcd, rem = nb % kNumXcd;
-  return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  const int chunk = local / kXcdChunk, off = local % kXcdChunk;
+  return (chunk * kNumXcd + xcd) * kXcdChunk + off;
 }
 
 // Decode tile number `pid` into (group, m-tile, n-tile).  Every lane of the
@@ -100,7 +107,7 @@ __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kLdsStride];
 
   const int n_tiles = GATE_UP ? Nout / (kBN / 2) : Nout / kBN;
-  const int pid = xcd_remap(blockIdx.x, gridDim.x);
+  const int pid = xcd_remap(blockIdx.x);
   int g, mt, nt;
   if (!decode_tile(pid, counts, G, n_tiles, g, mt, nt)) return;
 
@@ -117,28 +124,29 @@ __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
 
   const uint16_t* Wg = W + (int64_t)g * Nw * Kdim;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wid >> 1, wn = wid & 1;
 
   // global -> register staging: each thread moves 4 A and 4 B 16-byte vectors
   // per K-slab (a slab row is 64 bf16 = 8 vectors)
-  const uint4* a_src[4];
-  const uint4* b_src[4];
-  bool a_ok[4];
+  const u32x4_t* a_src[4];
+  const u32x4_t* b_src[4];
   int lds_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int v = tid + j * kThreads;  // 0..1023
     const int r = v >> 3, c = v & 7;
     lds_off[j] = r * kLdsStride + c * 8;
-    a_ok[j] = r < valid;
-    a_src[j] = reinterpret_cast<const uint4*>(A + (row_base + (a_ok[j] ? r : 0)) * Kdim) + c;
+    // rows past the segment re-read its last row: their results are never
+    // stored, and an unconditional load keeps the staging in registers
+    a_src[j] = reinterpret_cast<const u32x4_t*>(A + (row_base + min(r, valid - 1)) * Kdim) + c;
     int wrow;
     if (GATE_UP)
       wrow = (r < kBN / 2) ? nt * (kBN / 2) + r : Nout + nt * (kBN / 2) + (r - kBN / 2);
     else
       wrow = nt * kBN + r;
-    b_src[j] = reinterpret_cast<const uint4*>(Wg + (int64_t)wrow * Kdim) + c;
+    b_src[j] = reinterpret_cast<const u32x4_t*>(Wg + (int64_t)wrow * Kdim) + c;
   }
 
   f32x4_t acc[4][4];
@@ -160,26 +168,25 @@ __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
       b_row[j] = wn * 64 + j * 16;
   }
 
-  uint4 ra[4], rb[4];
-  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+  u32x4_t ra[4], rb[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    ra[j] = a_ok[j] ? a_src[j][0] : zero4;
+    ra[j] = a_src[j][0];
     rb[j] = b_src[j][0];
   }
   const int nk = Kdim / kBK;
   for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<uint4*>(&As[lds_off[j]]) = ra[j];
-      *reinterpret_cast<uint4*>(&Bs[lds_off[j]]) = rb[j];
+      *reinterpret_cast<u32x4_t*>(&As[lds_off[j]]) = ra[j];
+      *reinterpret_cast<u32x4_t*>(&Bs[lds_off[j]]) = rb[j];
     }
     __syncthreads();
     if (kt + 1 < nk) {
       const int adv = (kt + 1) * (kBK / 8);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        ra[j] = a_ok[j] ? a_src[j][adv] : zero4;
+        ra[j] = a_src[j][adv];
         rb[j] = b_src[j][adv];
       }
     }
@@ -241,16 +248,17 @@ int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32
                        void* workspace, int32_t* dev_error, hipStream_t stream) {
   uint16_t* act = static_cast<uint16_t*>(workspace);
   const int64_t m_tiles = (capacity + kBM - 1) / kBM + G;
+  const int64_t grid_unit = (int64_t)kNumXcd * kXcdChunk;
   if (capacity == 0) return MOE_OK;
   if (stages & MOE_FFN_GATE_UP) {
-    const int64_t blocks = m_tiles * (I / (kBN / 2));
+    const int64_t blocks = (m_tiles * (I / (kBN / 2)) + grid_unit - 1) / grid_unit * grid_unit;
     if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0,
                        stream, x, w13, cu_seqlens, counts, G, H, 2 * I, I, nullptr, act, capacity,
                        dev_error);
   }
   if (stages & MOE_FFN_DOWN) {
-    const int64_t blocks = m_tiles * (H / kBN);
+    const int64_t blocks = (m_tiles * (H / kBN) + grid_unit - 1) / grid_unit * grid_unit;
     if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0,
                        stream, act, w2, cu_seqlens, counts, G, I, H, H, row_scale, y, capacity,

@@ -55,23 +55,31 @@ def algorithmic(cfg, counts: np.ndarray) -> dict:
     return st
 
 
-def kernel_source_hash() -> str:
+STAGE_SOURCES = {
+    "route": ["route.hip"], "dispatch_qdq": ["fake_quant.hip"], "permute": ["permute.hip"],
+    "ffn_gate_up": ["grouped_ffn.hip"], "ffn_down": ["grouped_ffn.hip"],
+    "shared_ffn": ["grouped_ffn.hip"], "combine": ["combine.hip"],
+}
+
+
+def kernel_source_hash(stage: str) -> str:
+    """Hash of the sources a stage's kernels are built from (plus common.h)."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(os.path.join(ROOT, "combine_top_route_moe_amd", "csrc"))):
+    for name in STAGE_SOURCES[stage] + ["common.h"]:
         with open(os.path.join(ROOT, "combine_top_route_moe_amd", "csrc", name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic(kernel: str, workload: str):
+def committed_traffic(stage: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
-    taken on the kernels as they are now (same source hash); else None."""
-    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
+    taken on the kernel as it is now (same source hash); else None."""
+    path = os.path.join(PROFILES, f"hbm_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        d = json.load(f)
-    if d.get("source_hash") != kernel_source_hash():
+        d = json.load(f).get(stage)
+    if not d or d.get("source_hash") != kernel_source_hash(stage):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -121,6 +129,31 @@ def cpu_baseline(cfg, logits, hidden, row_valid, budget_s: float):
                       f"({tv} routed), whole layer, float64 numpy, {dt:.2f} s"}
 
 
+def copy_calibration(steps: int, warmup: int) -> None:
+    """Time moe_copy_bytes over 1 GiB: the plain streaming kernel whose
+    measured bandwidth and FETCH_SIZE / WRITE_SIZE counters calibrate the
+    other kernels' figures (it reads and writes exactly 1 GiB per launch)."""
+    import torch
+    from combine_top_route_moe_amd import ops
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(warmup):
+        ops.moe_copy_bytes(src, dst)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        ops.moe_copy_bytes(src, dst)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    print(json.dumps({"kernel": "copy_kernel", "bytes_read_per_launch": n,
+                      "bytes_written_per_launch": n, "ms_per_launch": round(ms, 4),
+                      "GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +163,9 @@ def main():
                     help="tiny | balanced | skewed | deepseek | prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run the reference copy kernel (1 GiB -> 1 GiB) and report its "
+                         "bandwidth; its byte counters scale the PMC traffic figures")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -140,8 +176,11 @@ def main():
     import workloads
     from combine_top_route_moe_amd import MoELayer, ops
 
-    cfg = workloads.CONFIGS[args.config]
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        copy_calibration(args.steps, args.warmup)
+        return
+    cfg = workloads.CONFIGS[args.config]
     if ops.moe_device_check(0) != 0:
         raise SystemExit("device 0 is not a gfx950 GPU")
     dev = torch.device("cuda:0")

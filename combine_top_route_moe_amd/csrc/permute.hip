@@ -20,7 +20,8 @@
 //      rows (src_of = -1, w_perm = 0) and checks the capacity.
 //   3. scatter: one workgroup per token group computes row_of / src_of /
 //      w_perm for its slots and copies each token row once from HBM into
-//      its K destination rows with 16-byte vector loads and stores.
+//      its K destination rows with 16-byte vector loads and stores; the
+//      workgroups also mark the unused rows up to `capacity`.
 #include "common.h"
 
 namespace moe {
@@ -128,9 +129,17 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
     const uint16_t* __restrict__ hidden, int T, int K, int H, int expert_begin, int El,
     int tok_per_block, int64_t capacity, const int32_t* __restrict__ table,
     const int32_t* __restrict__ rank, uint16_t* __restrict__ x_perm, int32_t* __restrict__ row_of,
-    int32_t* __restrict__ src_of, float* __restrict__ w_perm, int32_t* __restrict__ dev_error) {
+    int32_t* __restrict__ src_of, float* __restrict__ w_perm, int32_t* __restrict__ dev_error,
+    const int32_t* __restrict__ cu_seqlens) {
   __shared__ int32_t dest[256];
   const int tid = threadIdx.x;
+  // rows past the last segment are unused: mark them as well, so that every
+  // row of the caller's buffer has a defined src_of and w_perm
+  for (int64_t r = (int64_t)cu_seqlens[El] + (int64_t)blockIdx.x * blockDim.x + tid; r < capacity;
+       r += (int64_t)gridDim.x * blockDim.x) {
+    src_of[r] = -1;
+    w_perm[r] = 0.0f;
+  }
   const int t0 = blockIdx.x * tok_per_block;
   const int nslots = tok_per_block * K;
   if (tid < nslots) {
@@ -199,15 +208,15 @@ int launch_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t*
                        TK, expert_begin, El, nbits, table, rank);
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, stream, table, nchunks, El,
                      pad_pow2, capacity, counts, cu_seqlens, src_of, w_perm, dev_error);
-  if (T > 0) {
+  if (T > 0 || capacity > 0) {
     const int nvec = H / 8;
     int tpb = 256 / nvec;
     if (tpb < 1) tpb = 1;
     if (tpb * K > 256) tpb = 256 / K;
-    const int grid = (T + tpb - 1) / tpb;
+    const int grid = T > 0 ? (T + tpb - 1) / tpb : 1;
     hipLaunchKernelGGL(permute_scatter_kernel, dim3(grid), dim3(256), 0, stream, topk_idx, topk_w,
                        hidden, T, K, H, expert_begin, El, tpb, capacity, table, rank, x_perm,
-                       row_of, src_of, w_perm, dev_error);
+                       row_of, src_of, w_perm, dev_error, cu_seqlens);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

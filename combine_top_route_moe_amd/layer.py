@@ -72,8 +72,11 @@ class MoELayer:
     def set_weights(self, w13: torch.Tensor, w2: torch.Tensor,
                     shared_w13: Optional[torch.Tensor] = None,
                     shared_w2: Optional[torch.Tensor] = None) -> None:
-        """Device bf16 weights: w13 [E_l, 2I, H], w2 [E_l, H, I] (local experts)."""
+        """Device bf16 weights: w13 [E_l, 2I, H], w2 [E_l, H, I] (local experts);
+        the shared expert's [2Is, H] and [H, Is] (run as a single group)."""
         self.w13, self.w2 = w13, w2
+        if shared_w13 is not None and shared_w13.dim() == 2:
+            shared_w13, shared_w2 = shared_w13.unsqueeze(0), shared_w2.unsqueeze(0)
         self.shared_w13, self.shared_w2 = shared_w13, shared_w2
 
     # ------------------------------------------------------------------ stages

@@ -116,9 +116,11 @@ int moe_route(const float* logits, const uint8_t* row_valid, int T, int E, int K
  *   rows of a segment: its routed slots in ascending flat index i, then the
  *                  pow2 padding rows
  *   row_of[i]      permuted row of slot i, or -1 when not routed here
- *   src_of[r]      flat slot index of row r, or -1 for a padding row
- *   w_perm[r]      topk_w[src_of[r]], 0 for a padding row
- *   x_perm[r, :]   hidden[src_of[r] / K, :]; padding rows are not written
+ *   src_of[r]      flat slot index of row r, or -1 for a padding row and for
+ *                  every unused row in [cu_seqlens[num_local_experts], capacity)
+ *   w_perm[r]      topk_w[src_of[r]], 0 for padding and unused rows
+ *   x_perm[r, :]   hidden[src_of[r] / K, :]; padding and unused rows are not
+ *                  written
  *
  *   topk_idx [T, K] int32   topk_w [T, K] float32   hidden [T, H] bf16
  *   counts [E_l] int32, cu_seqlens [E_l + 1] int32, row_of [T*K] int32,

@@ -129,7 +129,12 @@ def _permute_case(idx, w, hid, El, begin=0, pow2=False, capacity=None, check_row
     T, K = idx.shape
     ref = oracle.permute(idx, w, hid, El, begin, pow2)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    p = ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), El, begin, pow2, capacity, dev_error=err)
+    cap = ops.moe_permute_capacity(T, K, El, pow2) if capacity is None else capacity
+    out = ops.alloc_permuted(T, K, hid.shape[1], El, cap, "cuda")
+    for t in (out.counts, out.cu_seqlens, out.row_of, out.src_of):
+        t.fill_(12345)                               # stale contents must not leak
+    out.w_perm.fill_(7.0)
+    p = ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), El, begin, pow2, cap, out, dev_error=err)
     assert host(err)[0] == 0
     np.testing.assert_array_equal(host(p.counts), ref["counts"])
     np.testing.assert_array_equal(host(p.cu_seqlens), ref["cu_seqlens"])
@@ -137,6 +142,7 @@ def _permute_case(idx, w, hid, El, begin=0, pow2=False, capacity=None, check_row
     used = int(ref["cu_seqlens"][-1])
     np.testing.assert_array_equal(host(p.src_of)[:used], ref["src_of"])
     np.testing.assert_array_equal(host(p.w_perm)[:used], ref["w_perm"])
+    assert np.all(host(p.src_of)[used:] == -1) and np.all(host(p.w_perm)[used:] == 0)
     valid = np.nonzero(ref["src_of"] >= 0)[0]
     if check_rows is not None and len(valid) > check_rows:
         valid = np.sort(np.random.default_rng(0).choice(valid, check_rows, replace=False))

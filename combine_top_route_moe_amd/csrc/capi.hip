@@ -21,6 +21,8 @@ size_t grouped_ffn_workspace_bytes(int64_t, int);
 int launch_grouped_ffn(const uint16_t*, const int32_t*, const int32_t*, int, int, int,
                        const uint16_t*, const uint16_t*, const float*, uint16_t*, int64_t, int,
                        void*, int32_t*, hipStream_t);
+int launch_pack_weights(const uint16_t*, const uint16_t*, int, int, int, uint16_t*, uint16_t*,
+                        hipStream_t);
 
 __global__ void __launch_bounds__(256) copy_kernel(const uint4* __restrict__ src,
                                                    uint4* __restrict__ dst, int64_t n) {
@@ -116,10 +118,12 @@ size_t moe_grouped_ffn_workspace_bytes(int64_t capacity, int num_groups, int H, 
 
 int moe_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32_t* counts,
                     int num_groups, int H, int I, const uint16_t* w13, const uint16_t* w2,
-                    const float* row_scale, uint16_t* y, int64_t capacity, int stages,
+                    const float* row_scale, uint16_t* y, int64_t capacity, int flags,
                     void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream) {
   if (num_groups < 1 || H < 1 || I < 1 || capacity < 0) return MOE_ERR_INVALID_ARG;
-  if (stages < 1 || stages > MOE_FFN_ALL) return MOE_ERR_INVALID_ARG;
+  if ((flags & ~(MOE_FFN_ALL | MOE_FFN_PACKED_WEIGHTS)) || !(flags & MOE_FFN_ALL))
+    return MOE_ERR_INVALID_ARG;
+  const int stages = flags & MOE_FFN_ALL;
   if (H % 128 || I % 128 || num_groups > 1024) return MOE_ERR_UNSUPPORTED;
   if (capacity > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
   if (!cu_seqlens || !counts) return MOE_ERR_INVALID_ARG;
@@ -132,7 +136,19 @@ int moe_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32_t*
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return MOE_ERR_WORKSPACE;
   return launch_grouped_ffn(x, cu_seqlens, counts, num_groups, H, I, w13, w2, row_scale, y,
-                            capacity, stages, workspace, dev_error, as_stream(stream));
+                            capacity, flags, workspace, dev_error, as_stream(stream));
+}
+
+int moe_pack_ffn_weights(const uint16_t* w13, const uint16_t* w2, int num_groups, int H, int I,
+                         uint16_t* w13_packed, uint16_t* w2_packed, void* stream) {
+  if (num_groups < 1 || H < 1 || I < 1) return MOE_ERR_INVALID_ARG;
+  if (H % 128 || I % 128) return MOE_ERR_UNSUPPORTED;
+  if (!w13 != !w13_packed || !w2 != !w2_packed) return MOE_ERR_INVALID_ARG;
+  if ((w13 && (!aligned16(w13) || !aligned16(w13_packed))) ||
+      (w2 && (!aligned16(w2) || !aligned16(w2_packed))))
+    return MOE_ERR_INVALID_ARG;
+  if ((w13 && w13 == w13_packed) || (w2 && w2 == w2_packed)) return MOE_ERR_INVALID_ARG;
+  return launch_pack_weights(w13, w2, num_groups, H, I, w13_packed, w2_packed, as_stream(stream));
 }
 
 int moe_fake_quant_rows(const uint16_t* in, uint16_t* out, int64_t n_rows, int H,

@@ -34,6 +34,8 @@
 // XCD's L2.
 // Workgroups past the last tile exit at once.  MFMA sub-tiles lying wholly
 // past the segment's last row are skipped.
+#include <algorithm>
+
 #include "common.h"
 
 namespace moe {
@@ -47,6 +49,7 @@ constexpr int kBN = 128;
 constexpr int kBK = 64;
 constexpr int kLdsStride = kBK + 8;  // bf16 elements per LDS row
 constexpr int kThreads = 256;
+constexpr int kTileVecs = kBN * kBK / 8;  // 16-byte vectors in one packed weight tile
 constexpr int kNumXcd = 8;
 
 // Workgroup ids are dealt round-robin over the 8 XCDs.  Remap them so that
@@ -96,7 +99,7 @@ __device__ __forceinline__ bool decode_tile(int pid, const int32_t* __restrict__
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-template <bool GATE_UP>
+template <bool GATE_UP, bool PACKED>
 __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ counts, int G,
@@ -141,12 +144,19 @@ __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
     // rows past the segment re-read its last row: their results are never
     // stored, and an unconditional load keeps the staging in registers
     a_src[j] = reinterpret_cast<const u32x4_t*>(A + (row_base + min(r, valid - 1)) * Kdim) + c;
-    int wrow;
-    if (GATE_UP)
-      wrow = (r < kBN / 2) ? nt * (kBN / 2) + r : Nout + nt * (kBN / 2) + (r - kBN / 2);
-    else
-      wrow = nt * kBN + r;
-    b_src[j] = reinterpret_cast<const u32x4_t*>(Wg + (int64_t)wrow * Kdim) + c;
+    if (PACKED) {
+      // tile (nt, kt) is one contiguous [kBN][kBK] block; chunk v of it is
+      // exactly what this thread stages
+      b_src[j] = reinterpret_cast<const u32x4_t*>(Wg) +
+                 (int64_t)nt * (Kdim / kBK) * kTileVecs + v;
+    } else {
+      int wrow;
+      if (GATE_UP)
+        wrow = (r < kBN / 2) ? nt * (kBN / 2) + r : Nout + nt * (kBN / 2) + (r - kBN / 2);
+      else
+        wrow = nt * kBN + r;
+      b_src[j] = reinterpret_cast<const u32x4_t*>(Wg + (int64_t)wrow * Kdim) + c;
+    }
   }
 
   f32x4_t acc[4][4];
@@ -174,6 +184,7 @@ __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
     ra[j] = a_src[j][0];
     rb[j] = b_src[j][0];
   }
+  const int b_step = PACKED ? kTileVecs : kBK / 8;  // 16-byte vectors per K-slab
   const int nk = Kdim / kBK;
   for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
@@ -184,10 +195,11 @@ __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
     __syncthreads();
     if (kt + 1 < nk) {
       const int adv = (kt + 1) * (kBK / 8);
+      const int badv = (kt + 1) * b_step;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         ra[j] = a_src[j][adv];
-        rb[j] = b_src[j][adv];
+        rb[j] = b_src[j][badv];
       }
     }
 #pragma unroll
@@ -238,31 +250,91 @@ __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
   }
 }
 
+// Packed weight layout: for each group, n-tile and K-slab, the kBN x kBK
+// block the GEMM stages in one step, stored contiguously (row-major inside
+// the block).  For w13 an n-tile's kBN rows are its kBN/2 gate rows followed
+// by the matching kBN/2 up rows.  One thread moves one 16-byte vector.
+__global__ void __launch_bounds__(256) pack_weights_kernel(const uint16_t* __restrict__ W,
+                                                           uint16_t* __restrict__ P, int G,
+                                                           int N, int Kdim, int gate_up) {
+  const int64_t nvec = (int64_t)G * N * Kdim / 8;
+  const int kt_n = Kdim / kBK;
+  const int nt_n = N / kBN;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec;
+       v += (int64_t)gridDim.x * blockDim.x) {
+    const int in_tile = (int)(v % kTileVecs);
+    int64_t t = v / kTileVecs;
+    const int kt = (int)(t % kt_n);
+    t /= kt_n;
+    const int nt = (int)(t % nt_n);
+    const int64_t g = t / nt_n;
+    const int r = in_tile >> 3, c = in_tile & 7;
+    int row;
+    if (gate_up) {
+      const int half = N / 2;  // I
+      row = (r < kBN / 2) ? nt * (kBN / 2) + r : half + nt * (kBN / 2) + (r - kBN / 2);
+    } else {
+      row = nt * kBN + r;
+    }
+    const uint4 val =
+        reinterpret_cast<const uint4*>(W + (g * N + row) * (int64_t)Kdim + kt * kBK)[c];
+    reinterpret_cast<uint4*>(P)[v] = val;
+  }
+}
+
+int launch_pack_weights(const uint16_t* w13, const uint16_t* w2, int G, int H, int I,
+                        uint16_t* w13p, uint16_t* w2p, hipStream_t stream) {
+  if (w13 && w13p) {
+    const int64_t nvec = (int64_t)G * 2 * I * H / 8;
+    const unsigned grid = (unsigned)std::min<int64_t>((nvec + 255) / 256, 65536);
+    hipLaunchKernelGGL(pack_weights_kernel, dim3(grid), dim3(256), 0, stream, w13, w13p, G, 2 * I,
+                       H, 1);
+  }
+  if (w2 && w2p) {
+    const int64_t nvec = (int64_t)G * H * I / 8;
+    const unsigned grid = (unsigned)std::min<int64_t>((nvec + 255) / 256, 65536);
+    hipLaunchKernelGGL(pack_weights_kernel, dim3(grid), dim3(256), 0, stream, w2, w2p, G, H, I, 0);
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 size_t grouped_ffn_workspace_bytes(int64_t capacity, int I) {
   return (((size_t)capacity * I * sizeof(uint16_t)) + 255) & ~(size_t)255;
 }
 
+template <bool GATE_UP>
+static void launch_gemm(bool packed, dim3 grid, hipStream_t stream, const uint16_t* A,
+                        const uint16_t* W, const int32_t* cu, const int32_t* cnt, int G, int Kdim,
+                        int Nw, int Nout, const float* row_scale, uint16_t* Out, int64_t capacity,
+                        int32_t* dev_error) {
+  if (packed)
+    hipLaunchKernelGGL((grouped_gemm_kernel<GATE_UP, true>), grid, dim3(kThreads), 0, stream, A,
+                       W, cu, cnt, G, Kdim, Nw, Nout, row_scale, Out, capacity, dev_error);
+  else
+    hipLaunchKernelGGL((grouped_gemm_kernel<GATE_UP, false>), grid, dim3(kThreads), 0, stream, A,
+                       W, cu, cnt, G, Kdim, Nw, Nout, row_scale, Out, capacity, dev_error);
+}
+
 int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32_t* counts, int G,
                        int H, int I, const uint16_t* w13, const uint16_t* w2,
-                       const float* row_scale, uint16_t* y, int64_t capacity, int stages,
+                       const float* row_scale, uint16_t* y, int64_t capacity, int flags,
                        void* workspace, int32_t* dev_error, hipStream_t stream) {
   uint16_t* act = static_cast<uint16_t*>(workspace);
+  const bool packed = (flags & MOE_FFN_PACKED_WEIGHTS) != 0;
   const int64_t m_tiles = (capacity + kBM - 1) / kBM + G;
   const int64_t grid_unit = (int64_t)kNumXcd * kXcdChunk;
   if (capacity == 0) return MOE_OK;
-  if (stages & MOE_FFN_GATE_UP) {
+  if (flags & MOE_FFN_GATE_UP) {
     const int64_t blocks = (m_tiles * (I / (kBN / 2)) + grid_unit - 1) / grid_unit * grid_unit;
     if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, x, w13, cu_seqlens, counts, G, H, 2 * I, I, nullptr, act, capacity,
-                       dev_error);
+    launch_gemm<true>(packed, dim3((unsigned)blocks), stream, x, w13, cu_seqlens, counts, G, H,
+                      2 * I, I, nullptr, act, capacity, dev_error);
   }
-  if (stages & MOE_FFN_DOWN) {
+  if (flags & MOE_FFN_DOWN) {
     const int64_t blocks = (m_tiles * (H / kBN) + grid_unit - 1) / grid_unit * grid_unit;
     if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, act, w2, cu_seqlens, counts, G, I, H, H, row_scale, y, capacity,
-                       dev_error);
+    launch_gemm<false>(packed, dim3((unsigned)blocks), stream, act, w2, cu_seqlens, counts, G, I,
+                       H, H, row_scale, y, capacity, dev_error);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -67,16 +67,26 @@ class MoELayer:
         else:
             self.shared_out = None
         self.w13 = self.w2 = self.shared_w13 = self.shared_w2 = None
+        self.packed = False
 
     # ------------------------------------------------------------------ weights
     def set_weights(self, w13: torch.Tensor, w2: torch.Tensor,
                     shared_w13: Optional[torch.Tensor] = None,
-                    shared_w2: Optional[torch.Tensor] = None) -> None:
+                    shared_w2: Optional[torch.Tensor] = None, pack: bool = True) -> None:
         """Device bf16 weights: w13 [E_l, 2I, H], w2 [E_l, H, I] (local experts);
-        the shared expert's [2Is, H] and [H, Is] (run as a single group)."""
-        self.w13, self.w2 = w13, w2
+        the shared expert's [2Is, H] and [H, Is] (run as a single group).
+
+        With ``pack`` (the default) the weights are copied once into the
+        grouped GEMM's packed layout (``moe_pack_ffn_weights``) and the
+        row-major tensors are not referenced afterwards."""
         if shared_w13 is not None and shared_w13.dim() == 2:
             shared_w13, shared_w2 = shared_w13.unsqueeze(0), shared_w2.unsqueeze(0)
+        self.packed = pack
+        if pack:
+            w13, w2 = ops.moe_pack_ffn_weights(w13, w2)
+            if shared_w13 is not None:
+                shared_w13, shared_w2 = ops.moe_pack_ffn_weights(shared_w13, shared_w2)
+        self.w13, self.w2 = w13, w2
         self.shared_w13, self.shared_w2 = shared_w13, shared_w2
 
     # ------------------------------------------------------------------ stages
@@ -98,15 +108,16 @@ class MoELayer:
         ops.moe_permute(self.topk_idx, self.topk_w, x, self.El, self.expert_begin, self.pad_pow2,
                         self.capacity, p, self.perm_ws, self.dev_error)
         m("permute")
+        layout = ops.MOE_FFN_PACKED_WEIGHTS if self.packed else 0
         ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, self.w13, self.w2, p.w_perm,
-                            self.y_perm, ops.MOE_FFN_GATE_UP, self.ffn_ws, self.dev_error)
+                            self.y_perm, ops.MOE_FFN_GATE_UP | layout, self.ffn_ws, self.dev_error)
         m("ffn_gate_up")
         ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, self.w13, self.w2, p.w_perm,
-                            self.y_perm, ops.MOE_FFN_DOWN, self.ffn_ws, self.dev_error)
+                            self.y_perm, ops.MOE_FFN_DOWN | layout, self.ffn_ws, self.dev_error)
         m("ffn_down")
         if self.shared_I:
             ops.moe_grouped_ffn(hidden, self.shared_cu, self.shared_counts, self.shared_w13,
-                                self.shared_w2, None, self.shared_out, ops.MOE_FFN_ALL,
+                                self.shared_w2, None, self.shared_out, ops.MOE_FFN_ALL | layout,
                                 self.shared_ws, self.dev_error)
             m("shared_ffn")
         ops.moe_combine(self.y_perm, p.row_of, self.T, self.K, self.shared_out,

@@ -17,7 +17,7 @@ from ._lib import load, check
 
 MOE_ROUTE_RENORM = 1
 MOE_PERMUTE_PAD_POW2 = 1
-MOE_FFN_GATE_UP, MOE_FFN_DOWN, MOE_FFN_ALL = 1, 2, 3
+MOE_FFN_GATE_UP, MOE_FFN_DOWN, MOE_FFN_ALL, MOE_FFN_PACKED_WEIGHTS = 1, 2, 3, 4
 MOE_FQ_PER_TENSOR, MOE_FQ_BLOCK = 0, 1
 MOE_DEVERR_ROW_RANGE, MOE_DEVERR_CAPACITY = 1, 2
 
@@ -127,7 +127,7 @@ def moe_grouped_ffn_workspace_bytes(capacity: int, num_groups: int, H: int, I: i
 
 def moe_grouped_ffn(x: torch.Tensor, cu_seqlens: torch.Tensor, counts: torch.Tensor,
                     w13: torch.Tensor, w2: torch.Tensor, row_scale: Optional[torch.Tensor] = None,
-                    y: Optional[torch.Tensor] = None, stages: int = MOE_FFN_ALL,
+                    y: Optional[torch.Tensor] = None, flags: int = MOE_FFN_ALL,
                     workspace: Optional[torch.Tensor] = None,
                     dev_error: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     _want(x, torch.bfloat16, "x")
@@ -151,9 +151,30 @@ def moe_grouped_ffn(x: torch.Tensor, cu_seqlens: torch.Tensor, counts: torch.Ten
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     check("moe_grouped_ffn", lib.moe_grouped_ffn(
         _ptr(x), _ptr(cu_seqlens), _ptr(counts), G, H, I, _ptr(w13), _ptr(w2), _ptr(row_scale),
-        _ptr(y), capacity, stages, _ptr(workspace), workspace.numel(), _ptr(dev_error),
+        _ptr(y), capacity, flags, _ptr(workspace), workspace.numel(), _ptr(dev_error),
         _stream(stream)))
     return y
+
+
+def moe_pack_ffn_weights(w13: Optional[torch.Tensor], w2: Optional[torch.Tensor],
+                         w13_packed: Optional[torch.Tensor] = None,
+                         w2_packed: Optional[torch.Tensor] = None, stream=None):
+    """Copy w13 [G,2I,H] / w2 [G,H,I] into the grouped GEMM's packed layout."""
+    if w13 is not None:
+        _want(w13, torch.bfloat16, "w13")
+        G, two_i, H = w13.shape
+        I = two_i // 2
+    else:
+        _want(w2, torch.bfloat16, "w2")
+        G, H, I = w2.shape
+    if w13 is not None and w13_packed is None:
+        w13_packed = torch.empty_like(w13)
+    if w2 is not None and w2_packed is None:
+        w2_packed = torch.empty_like(w2)
+    check("moe_pack_ffn_weights", load().moe_pack_ffn_weights(
+        _ptr(w13), _ptr(w2), G, H, I, _ptr(w13_packed), _ptr(w2_packed),
+        _stream(stream)))
+    return w13_packed, w2_packed
 
 
 def moe_fake_quant_rows(inp: torch.Tensor, out: Optional[torch.Tensor] = None,

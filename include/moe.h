@@ -64,9 +64,10 @@ enum {
 /* ---- flags -------------------------------------------------------------- */
 enum { MOE_ROUTE_RENORM = 1 };        /* moe_route: renormalise over top-k */
 enum { MOE_PERMUTE_PAD_POW2 = 1 };    /* moe_permute: pow2 segment buckets */
-enum { MOE_FFN_GATE_UP = 1,           /* moe_grouped_ffn stages            */
+enum { MOE_FFN_GATE_UP = 1,           /* moe_grouped_ffn flags: stages ... */
        MOE_FFN_DOWN = 2,
-       MOE_FFN_ALL = 3 };
+       MOE_FFN_ALL = 3,
+       MOE_FFN_PACKED_WEIGHTS = 4 };  /* ... and the weight layout          */
 enum { MOE_FQ_PER_TENSOR = 0,         /* moe_fake_quant_rows modes         */
        MOE_FQ_BLOCK = 1 };
 
@@ -156,16 +157,30 @@ int moe_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t* hi
  *   x [capacity, H] bf16;  w13 [G, 2I, H] bf16 (gate rows [0, I), up rows
  *   [I, 2I)); w2 [G, H, I] bf16; row_scale [capacity] float32 or NULL;
  *   y [capacity, H] bf16 (out); cu_seqlens [G + 1], counts [G] int32.
- * `stages` selects MOE_FFN_GATE_UP (writes `a` into the workspace),
- * MOE_FFN_DOWN (reads it) or MOE_FFN_ALL; a DOWN-only call must get the
- * workspace a GATE_UP call with the same segments filled.  Segments that
- * reach past `capacity` are skipped and raise MOE_DEVERR_ROW_RANGE.
+ * `flags` selects the stages — MOE_FFN_GATE_UP (writes `a` into the
+ * workspace), MOE_FFN_DOWN (reads it) or MOE_FFN_ALL; a DOWN-only call must
+ * get the workspace a GATE_UP call with the same segments filled — and, with
+ * MOE_FFN_PACKED_WEIGHTS, says that w13 and w2 are in the packed layout
+ * moe_pack_ffn_weights() produces.  Segments that reach past `capacity` are
+ * skipped and raise MOE_DEVERR_ROW_RANGE.
  * Requires H % 128 == 0, I % 128 == 0, 1 <= G <= 1024. */
 size_t moe_grouped_ffn_workspace_bytes(int64_t capacity, int num_groups, int H, int I);
 int moe_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32_t* counts,
                     int num_groups, int H, int I, const uint16_t* w13, const uint16_t* w2,
-                    const float* row_scale, uint16_t* y, int64_t capacity, int stages,
+                    const float* row_scale, uint16_t* y, int64_t capacity, int flags,
                     void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream);
+
+/* Rearrange expert weights, once, into the layout the grouped GEMM streams
+ * best: for every group, n-tile and 64-wide K-slab, the 128 x 64 block one
+ * GEMM step consumes is stored contiguously (16 KB), so each step reads one
+ * contiguous run of HBM instead of 128 short pieces of rows 2*H or 2*I bytes
+ * apart.  A w13 n-tile holds 64 gate rows followed by the 64 matching up
+ * rows.  w13 [G, 2I, H] -> w13_packed (same size); w2 [G, H, I] -> w2_packed
+ * (same size); either pair may be NULL.  Outputs must not alias inputs.
+ * Weights are static, so this runs at load time, not per layer call.
+ * Requires H % 128 == 0, I % 128 == 0. */
+int moe_pack_ffn_weights(const uint16_t* w13, const uint16_t* w2, int num_groups, int H, int I,
+                         uint16_t* w13_packed, uint16_t* w2_packed, void* stream);
 
 /* ---- FP8 fake-quant of bf16 rows ---------------------------------------
  * QDQ to OCP E4M3FN and back ([P1] PR summary and "How it works": the

@@ -342,3 +342,30 @@ def test_ffn_deterministic():
     a = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13, w2, p.w_perm)
     b = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13, w2, p.w_perm)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_ffn_packed_weights_equal_row_major():
+    """The packed layout is only a different order of the same weights: the
+    packed GEMM gives the row-major GEMM's bits exactly, and unpacking by
+    the documented tile order recovers the input."""
+    cfg = workloads.MoEConfig("t", 13, T=300, H=512, E=6, K=2, I=256, hot_experts=2)
+    idx, w = oracle.route(workloads.logits(cfg), None, 2)
+    w13, w2, host_w = stacked_weights(cfg)
+    p = ops.moe_permute(dev(idx), dev(w), dev_bf16(workloads.hidden(cfg)), cfg.E)
+    w13p, w2p = ops.moe_pack_ffn_weights(w13, w2)
+    a = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13, w2, p.w_perm)
+    b = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13p, w2p, p.w_perm,
+                            flags=ops.MOE_FFN_ALL | ops.MOE_FFN_PACKED_WEIGHTS)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # w2 [G, H, I]: tile (g, nt, kt) = rows nt*128.., cols kt*64..
+    G, H, I = cfg.E, cfg.H, cfg.I
+    got = host_bits(w2p).reshape(G, H // 128, I // 64, 128, 64)
+    want = host_bits(w2).reshape(G, H // 128, 128, I // 64, 64).transpose(0, 1, 3, 2, 4)
+    np.testing.assert_array_equal(got, want)
+    # w13: tile rows = 64 gate rows then the 64 matching up rows
+    g13 = host_bits(w13p).reshape(G, I // 64, H // 64, 128, 64)
+    w13h = host_bits(w13)
+    gate = w13h[:, :I].reshape(G, I // 64, 64, H // 64, 64).transpose(0, 1, 3, 2, 4)
+    up = w13h[:, I:].reshape(G, I // 64, 64, H // 64, 64).transpose(0, 1, 3, 2, 4)
+    np.testing.assert_array_equal(g13[:, :, :, :64], gate)
+    np.testing.assert_array_equal(g13[:, :, :, 64:], up)

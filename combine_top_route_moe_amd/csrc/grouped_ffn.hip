@@ -49,7 +49,6 @@ constexpr int kBN = 128;
 constexpr int kBK = 64;
 constexpr int kLdsStride = kBK + 8;  // bf16 elements per LDS row
 constexpr int kThreads = 256;
-constexpr int kTileVecs = kBN * kBK / 8;  // 16-byte vectors in one packed weight tile
 constexpr int kNumXcd = 8;
 
 // Workgroup ids are dealt round-robin over the 8 XCDs.  Remap them so that
@@ -99,7 +98,7 @@ __device__ __forceinline__ bool decode_tile(int pid, const int32_t* __restrict__
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-template <bool GATE_UP, bool PACKED>
+template <bool GATE_UP>
 __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ counts, int G,
@@ -144,19 +143,12 @@ __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
     // rows past the segment re-read its last row: their results are never
     // stored, and an unconditional load keeps the staging in registers
     a_src[j] = reinterpret_cast<const u32x4_t*>(A + (row_base + min(r, valid - 1)) * Kdim) + c;
-    if (PACKED) {
-      // tile (nt, kt) is one contiguous [kBN][kBK] block; chunk v of it is
-      // exactly what this thread stages
-      b_src[j] = reinterpret_cast<const u32x4_t*>(Wg) +
-                 (int64_t)nt * (Kdim / kBK) * kTileVecs + v;
-    } else {
-      int wrow;
-      if (GATE_UP)
-        wrow = (r < kBN / 2) ? nt * (kBN / 2) + r : Nout + nt * (kBN / 2) + (r - kBN / 2);
-      else
-        wrow = nt * kBN + r;
-      b_src[j] = reinterpret_cast<const u32x4_t*>(Wg + (int64_t)wrow * Kdim) + c;
-    }
+    int wrow;
+    if (GATE_UP)
+      wrow = (r < kBN / 2) ? nt * (kBN / 2) + r : Nout + nt * (kBN / 2) + (r - kBN / 2);
+    else
+      wrow = nt * kBN + r;
+    b_src[j] = reinterpret_cast<const u32x4_t*>(Wg + (int64_t)wrow * Kdim) + c;
   }
 
   f32x4_t acc[4][4];
@@ -184,7 +176,6 @@ __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
     ra[j] = a_src[j][0];
     rb[j] = b_src[j][0];
   }
-  const int b_step = PACKED ? kTileVecs : kBK / 8;  // 16-byte vectors per K-slab
   const int nk = Kdim / kBK;
   for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
@@ -195,11 +186,10 @@ __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
     __syncthreads();
     if (kt + 1 < nk) {
       const int adv = (kt + 1) * (kBK / 8);
-      const int badv = (kt + 1) * b_step;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         ra[j] = a_src[j][adv];
-        rb[j] = b_src[j][badv];
+        rb[j] = b_src[j][adv];
       }
     }
 #pragma unroll
@@ -250,35 +240,204 @@ __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
   }
 }
 
-// Packed weight layout: for each group, n-tile and K-slab, the kBN x kBK
-// block the GEMM stages in one step, stored contiguously (row-major inside
-// the block).  For w13 an n-tile's kBN rows are its kBN/2 gate rows followed
-// by the matching kBN/2 up rows.  One thread moves one 16-byte vector.
+// ---------------------------------------------------------------------------
+// Packed weights and the fragment-streaming GEMM.
+//
+// Packed layout ("fragment order"): for every group, every column tile of 64
+// weight rows and every 32-wide K-step, the four 16x32 MFMA B-fragments of
+// that tile are stored back to back, each as 64 lanes x 16 bytes in lane
+// order: lane l holds W[row0 + l%16][k0 + 8*(l/16) .. +8].  A w13 column tile
+// is 32 gate rows (fragments 0, 1) and the 32 matching up rows (fragments 2,
+// 3); a w2 column tile is 64 consecutive rows.  A wave therefore streams its
+// weights as consecutive, perfectly coalesced 1 KB loads straight into the
+// registers the MFMA reads, with no LDS round trip and no barrier.
+//
+// The kernel: a workgroup of 4 waves covers up to 128 rows of one segment
+// (8 m-subtiles; the ones past the segment end are skipped) and 4 column
+// tiles (wave w owns tile 4*cb + w).  Weights are prefetched kPrefetch
+// K-steps ahead in registers.  The activation rows are shared by the four
+// waves: they go into LDS by direct-to-LDS DMA (global_load_lds_dwordx4), in
+// the same fragment order so every LDS read is one contiguous, conflict-free
+// 1 KB, through a two-stage ring of kChunkSteps K-steps per stage.
+constexpr int kPrefetch = 4;     // weight K-steps in flight per wave
+constexpr int kChunkSteps = 2;   // activation K-steps per LDS stage
+constexpr int kMsub = 8;         // 16-row m-subtiles per workgroup (128 rows)
+constexpr int kFrags = 4;        // B fragments per wave (one column tile)
+constexpr int kStageBlocks = kMsub * kChunkSteps;  // 1 KB blocks per LDS stage
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (and for nothing else)
+__device__ __forceinline__ constexpr int vmcnt_imm(int n) {
+  return (n & 0xf) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xf << 8);
+}
+
+template <bool GATE_UP>
+__global__ void __launch_bounds__(kThreads, 2) frag_gemm_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Wf,
+    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ counts, int G,
+    int Kdim, int Nw /* weight rows per group */, int Nout, const float* __restrict__ row_scale,
+    uint16_t* __restrict__ Out, int64_t capacity, int32_t* __restrict__ dev_error) {
+  __shared__ __attribute__((aligned(16))) u32x4_t As[2][kStageBlocks][kWave];
+
+  const int n_ct = Nw / 64;              // column tiles per group
+  const int n_cb = (n_ct + 3) / 4;       // column blocks (workgroups) per m-tile
+  const int pid = xcd_remap(blockIdx.x);
+  int g, mt, cb;
+  if (!decode_tile(pid, counts, G, n_cb, g, mt, cb)) return;
+  const int seg0 = cu_seqlens[g];
+  const int nrows = counts[g];
+  if ((int64_t)seg0 + nrows > capacity || seg0 < 0) {
+    if ((threadIdx.x & 63) == 0) raise_error(dev_error, MOE_DEVERR_ROW_RANGE);
+    return;
+  }
+  const int m0 = mt * kBM;
+  const int valid = min(kBM, nrows - m0);
+  if (valid <= 0) return;
+  const int64_t row_base = (int64_t)seg0 + m0;
+  const int nlive = (valid + 15) >> 4;   // m-subtiles holding real rows
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // the last column block may hold fewer than 4 tiles (w2 with H/64 odd
+  // multiples of 2): the spare waves stream a real tile and store nothing
+  const bool ct_ok = cb * 4 + w < n_ct;
+  const int ct = ct_ok ? cb * 4 + w : n_ct - 1;
+  const int nks = Kdim / 32;
+
+  // this wave's weight stream: step ks, fragment f at wp[(ks * 4 + f) * 64]
+  const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(Wf) +
+                      ((int64_t)g * n_ct + ct) * nks * (kFrags * kWave) + lane;
+  // the activation DMA: this wave fills LDS blocks b = 4w .. 4w+3 of a stage;
+  // block b is m-subtile b / kChunkSteps, K-step b % kChunkSteps of the chunk
+  const uint16_t* a_src[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int b = w * 4 + q;
+    const int ms = b / kChunkSteps, sub = b % kChunkSteps;
+    const int r = min(ms * 16 + (lane & 15), valid - 1);
+    a_src[q] = A + (row_base + r) * Kdim + sub * 32 + 8 * (lane >> 4);
+  }
+  auto issue_chunk = [&](int chunk, int stage) {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds(a_src[q] + chunk * (kChunkSteps * 32),
+                                       &As[stage][w * 4 + q][0], 16, 0, 0);
+    asm volatile("" ::: "memory");
+  };
+
+  f32x4_t acc[kMsub][kFrags];
+#pragma unroll
+  for (int i = 0; i < kMsub; ++i)
+#pragma unroll
+    for (int f = 0; f < kFrags; ++f) acc[i][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nchunks = nks / kChunkSteps;
+  issue_chunk(0, 0);
+  u32x4_t bq[kPrefetch][kFrags];
+#pragma unroll
+  for (int s = 0; s < kPrefetch; ++s)
+#pragma unroll
+    for (int f = 0; f < kFrags; ++f) bq[s][f] = wp[(s * kFrags + f) * kWave];
+  asm volatile("" ::: "memory");
+
+  // nks is a multiple of 4 = kPrefetch (K is a multiple of 128)
+  for (int ks0 = 0; ks0 < nks; ks0 += kPrefetch) {
+#pragma unroll
+    for (int s = 0; s < kPrefetch; ++s) {
+      const int ks = ks0 + s;
+      if (s % kChunkSteps == 0) {
+        const int chunk = ks / kChunkSteps;
+        // the chunk's DMA was followed by kPrefetch * kFrags weight loads
+        // (the prologue) or by kChunkSteps * kFrags (steady state)
+        if (chunk == 0)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPrefetch * kFrags));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(kChunkSteps * kFrags));
+        __syncthreads();
+        // the other stage was last read in the previous chunk, which every
+        // wave has finished; past the last chunk this reloads a valid chunk
+        // so the number of outstanding loads stays the same
+        issue_chunk(min(chunk + 1, nchunks - 1), (chunk + 1) & 1);
+      }
+      const int stage = (ks / kChunkSteps) & 1;
+      const int sub = ks % kChunkSteps;
+#pragma unroll
+      for (int i = 0; i < kMsub; ++i) {
+        if (i >= nlive) break;
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, As[stage][i * kChunkSteps + sub][lane]);
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f)
+          acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              af, __builtin_bit_cast(bf16x8_t, bq[s][f]), acc[i][f], 0, 0, 0);
+      }
+      // refill this slot kPrefetch steps ahead (past the end: the last step
+      // again, which keeps the outstanding-load count constant)
+      const int nxt = min(ks + kPrefetch, nks - 1);
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int f = 0; f < kFrags; ++f) bq[s][f] = wp[(nxt * kFrags + f) * kWave];
+      asm volatile("" ::: "memory");
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA may outlive the workgroup
+  if (!ct_ok) return;
+
+  // epilogue: lane holds D[4*(lane/16) + q][lane%16] of every 16x16 tile
+#pragma unroll
+  for (int i = 0; i < kMsub; ++i) {
+    if (i >= nlive) break;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = i * 16 + 4 * (lane >> 4) + q;
+      if (r >= valid) continue;
+      const int64_t orow = row_base + r;
+      if (GATE_UP) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const int col = ct * 32 + f * 16 + (lane & 15);
+          Out[orow * Nout + col] =
+              (uint16_t)f32_to_bf16(silu_f(acc[i][f][q]) * acc[i][f + 2][q]);
+        }
+      } else {
+        const float sc = row_scale ? row_scale[orow] : 1.0f;
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f) {
+          const int col = ct * 64 + f * 16 + (lane & 15);
+          Out[orow * Nout + col] = (uint16_t)f32_to_bf16(sc * acc[i][f][q]);
+        }
+      }
+    }
+  }
+}
+
+// Packing: one thread per 16-byte vector of the packed layout.
 __global__ void __launch_bounds__(256) pack_weights_kernel(const uint16_t* __restrict__ W,
                                                            uint16_t* __restrict__ P, int G,
                                                            int N, int Kdim, int gate_up) {
   const int64_t nvec = (int64_t)G * N * Kdim / 8;
-  const int kt_n = Kdim / kBK;
-  const int nt_n = N / kBN;
+  const int nks = Kdim / 32;
+  const int n_ct = N / 64;
   for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec;
        v += (int64_t)gridDim.x * blockDim.x) {
-    const int in_tile = (int)(v % kTileVecs);
-    int64_t t = v / kTileVecs;
-    const int kt = (int)(t % kt_n);
-    t /= kt_n;
-    const int nt = (int)(t % nt_n);
-    const int64_t g = t / nt_n;
-    const int r = in_tile >> 3, c = in_tile & 7;
+    const int lane = (int)(v % kWave);
+    int64_t t = v / kWave;
+    const int f = (int)(t % kFrags);
+    t /= kFrags;
+    const int ks = (int)(t % nks);
+    t /= nks;
+    const int ct = (int)(t % n_ct);
+    const int64_t g = t / n_ct;
     int row;
     if (gate_up) {
       const int half = N / 2;  // I
-      row = (r < kBN / 2) ? nt * (kBN / 2) + r : half + nt * (kBN / 2) + (r - kBN / 2);
+      row = (f < 2) ? ct * 32 + f * 16 + (lane & 15) : half + ct * 32 + (f - 2) * 16 + (lane & 15);
     } else {
-      row = nt * kBN + r;
+      row = ct * 64 + f * 16 + (lane & 15);
     }
-    const uint4 val =
-        reinterpret_cast<const uint4*>(W + (g * N + row) * (int64_t)Kdim + kt * kBK)[c];
-    reinterpret_cast<uint4*>(P)[v] = val;
+    const int k = ks * 32 + 8 * (lane >> 4);
+    reinterpret_cast<uint4*>(P)[v] =
+        *reinterpret_cast<const uint4*>(W + (g * N + row) * (int64_t)Kdim + k);
   }
 }
 
@@ -302,19 +461,6 @@ size_t grouped_ffn_workspace_bytes(int64_t capacity, int I) {
   return (((size_t)capacity * I * sizeof(uint16_t)) + 255) & ~(size_t)255;
 }
 
-template <bool GATE_UP>
-static void launch_gemm(bool packed, dim3 grid, hipStream_t stream, const uint16_t* A,
-                        const uint16_t* W, const int32_t* cu, const int32_t* cnt, int G, int Kdim,
-                        int Nw, int Nout, const float* row_scale, uint16_t* Out, int64_t capacity,
-                        int32_t* dev_error) {
-  if (packed)
-    hipLaunchKernelGGL((grouped_gemm_kernel<GATE_UP, true>), grid, dim3(kThreads), 0, stream, A,
-                       W, cu, cnt, G, Kdim, Nw, Nout, row_scale, Out, capacity, dev_error);
-  else
-    hipLaunchKernelGGL((grouped_gemm_kernel<GATE_UP, false>), grid, dim3(kThreads), 0, stream, A,
-                       W, cu, cnt, G, Kdim, Nw, Nout, row_scale, Out, capacity, dev_error);
-}
-
 int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32_t* counts, int G,
                        int H, int I, const uint16_t* w13, const uint16_t* w2,
                        const float* row_scale, uint16_t* y, int64_t capacity, int flags,
@@ -323,18 +469,33 @@ int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32
   const bool packed = (flags & MOE_FFN_PACKED_WEIGHTS) != 0;
   const int64_t m_tiles = (capacity + kBM - 1) / kBM + G;
   const int64_t grid_unit = (int64_t)kNumXcd * kXcdChunk;
+  auto grid_for = [&](int64_t n_tiles) {
+    return (m_tiles * n_tiles + grid_unit - 1) / grid_unit * grid_unit;
+  };
   if (capacity == 0) return MOE_OK;
   if (flags & MOE_FFN_GATE_UP) {
-    const int64_t blocks = (m_tiles * (I / (kBN / 2)) + grid_unit - 1) / grid_unit * grid_unit;
+    const int64_t blocks = grid_for(packed ? (2 * I / 64) / 4 : I / (kBN / 2));
     if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-    launch_gemm<true>(packed, dim3((unsigned)blocks), stream, x, w13, cu_seqlens, counts, G, H,
-                      2 * I, I, nullptr, act, capacity, dev_error);
+    if (packed)
+      hipLaunchKernelGGL(frag_gemm_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                         x, w13, cu_seqlens, counts, G, H, 2 * I, I, nullptr, act, capacity,
+                         dev_error);
+    else
+      hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                         stream, x, w13, cu_seqlens, counts, G, H, 2 * I, I, nullptr, act,
+                         capacity, dev_error);
   }
   if (flags & MOE_FFN_DOWN) {
-    const int64_t blocks = (m_tiles * (H / kBN) + grid_unit - 1) / grid_unit * grid_unit;
+    const int64_t blocks = grid_for(packed ? (H / 64 + 3) / 4 : H / kBN);
     if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-    launch_gemm<false>(packed, dim3((unsigned)blocks), stream, act, w2, cu_seqlens, counts, G, I,
-                       H, H, row_scale, y, capacity, dev_error);
+    if (packed)
+      hipLaunchKernelGGL(frag_gemm_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                         stream, act, w2, cu_seqlens, counts, G, I, H, H, row_scale, y, capacity,
+                         dev_error);
+    else
+      hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                         stream, act, w2, cu_seqlens, counts, G, I, H, H, row_scale, y, capacity,
+                         dev_error);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

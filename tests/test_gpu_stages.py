@@ -344,28 +344,43 @@ def test_ffn_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_ffn_packed_weights_equal_row_major():
-    """The packed layout is only a different order of the same weights: the
-    packed GEMM gives the row-major GEMM's bits exactly, and unpacking by
-    the documented tile order recovers the input."""
-    cfg = workloads.MoEConfig("t", 13, T=300, H=512, E=6, K=2, I=256, hot_experts=2)
+@pytest.mark.parametrize("H,I,T", [(512, 256, 300), (128, 128, 40), (384, 256, 700)])
+def test_ffn_packed_weights(H, I, T):
+    """Packed weights in MFMA fragment order: the packing is the documented
+    permutation of the input, and the fragment-streaming GEMM matches the
+    oracle (including a partial column block when H/64 is not a multiple
+    of 4, and several m-tiles per expert)."""
+    cfg = workloads.MoEConfig("t", 13, T=T, H=H, E=6, K=2, I=I, hot_experts=2)
     idx, w = oracle.route(workloads.logits(cfg), None, 2)
+    hid = workloads.hidden(cfg)
     w13, w2, host_w = stacked_weights(cfg)
-    p = ops.moe_permute(dev(idx), dev(w), dev_bf16(workloads.hidden(cfg)), cfg.E)
     w13p, w2p = ops.moe_pack_ffn_weights(w13, w2)
-    a = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13, w2, p.w_perm)
-    b = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13p, w2p, p.w_perm,
-                            flags=ops.MOE_FFN_ALL | ops.MOE_FFN_PACKED_WEIGHTS)
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
-    # w2 [G, H, I]: tile (g, nt, kt) = rows nt*128.., cols kt*64..
-    G, H, I = cfg.E, cfg.H, cfg.I
-    got = host_bits(w2p).reshape(G, H // 128, I // 64, 128, 64)
-    want = host_bits(w2).reshape(G, H // 128, 128, I // 64, 64).transpose(0, 1, 3, 2, 4)
+    G = cfg.E
+    # w2 [G, H, I]: column tile ct = rows 64ct.., fragment f = rows +16f..,
+    # k-step ks, lane l -> row + l%16, cols 32ks + 8(l/16) .. +8
+    got = host_bits(w2p).reshape(G, H // 64, I // 32, 4, 4, 16, 8)     # g ct ks f (l/16) (l%16) 8
+    want = host_bits(w2).reshape(G, H // 64, 4, 16, I // 32, 4, 8).transpose(0, 1, 4, 2, 5, 3, 6)
     np.testing.assert_array_equal(got, want)
-    # w13: tile rows = 64 gate rows then the 64 matching up rows
-    g13 = host_bits(w13p).reshape(G, I // 64, H // 64, 128, 64)
+    # w13: column tile ct = gate rows 32ct.. (fragments 0, 1) then up rows
+    g13 = host_bits(w13p).reshape(G, I // 32, H // 32, 4, 4, 16, 8)
     w13h = host_bits(w13)
-    gate = w13h[:, :I].reshape(G, I // 64, 64, H // 64, 64).transpose(0, 1, 3, 2, 4)
-    up = w13h[:, I:].reshape(G, I // 64, 64, H // 64, 64).transpose(0, 1, 3, 2, 4)
-    np.testing.assert_array_equal(g13[:, :, :, :64], gate)
-    np.testing.assert_array_equal(g13[:, :, :, 64:], up)
+    gate = w13h[:, :I].reshape(G, I // 32, 2, 16, H // 32, 4, 8).transpose(0, 1, 4, 2, 5, 3, 6)
+    up = w13h[:, I:].reshape(G, I // 32, 2, 16, H // 32, 4, 8).transpose(0, 1, 4, 2, 5, 3, 6)
+    np.testing.assert_array_equal(g13[:, :, :, :2], gate)
+    np.testing.assert_array_equal(g13[:, :, :, 2:], up)
+    # the GEMM on packed weights against the oracle
+    ref = oracle.permute(idx, w, hid, G, 0, False)
+    p = ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), G)
+    y = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13p, w2p, p.w_perm,
+                            flags=ops.MOE_FFN_ALL | ops.MOE_FFN_PACKED_WEIGHTS)
+    for e in range(G):
+        n, r0 = int(ref["counts"][e]), int(ref["cu_seqlens"][e])
+        if n == 0:
+            continue
+        x = oracle.bf16_bits_to_f64(ref["x_perm"][r0:r0 + n])
+        want_y = oracle.expert_ffn(x, *host_w[e]) * ref["w_perm"][r0:r0 + n, None].astype(np.float64)
+        assert rel_err(bf16_bits_to_f32(host_bits(y[r0:r0 + n])), want_y) <= FFN_TOL, e
+    # and it agrees closely with the row-major kernel (different summation order)
+    y2 = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13, w2, p.w_perm)
+    used = int(ref["cu_seqlens"][-1])
+    assert rel_err(bf16_bits_to_f32(host_bits(y[:used])), bf16_bits_to_f32(host_bits(y2[:used]))) < 1e-2

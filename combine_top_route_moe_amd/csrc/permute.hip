@@ -8,11 +8,12 @@
 //
 // Rows inside a segment are ordered by the flat slot index i = t*K + k, so
 // the result is unique and deterministic.  Three launches:
-//   1. chunk_rank: one wavefront per chunk of 1024 flat slots walks its
-//      chunk 64 slots at a time.  Lanes holding the same expert find each
-//      other with one ballot per bit of the expert id; a lane's rank is the
-//      number of same-expert lanes below it plus the running count of that
-//      expert in the chunk (kept in LDS).  Writes rank[i] and the chunk's
+//   1. chunk_rank: one workgroup per chunk of 1024 flat slots; each of its
+//      four wavefronts walks a quarter, 64 slots at a time.  Lanes holding
+//      the same expert find each other with one ballot per bit of the
+//      expert id; a lane's rank is the number of same-expert lanes below it
+//      plus the wave's running count of that expert (in LDS) plus the
+//      counts of the earlier waves.  Writes rank[i] and the chunk's
 //      per-expert totals.
 //   2. scan: one workgroup turns the chunk totals into per-expert counts,
 //      segment sizes (optionally next_pow2), cu_seqlens, and the absolute
@@ -28,21 +29,26 @@ namespace moe {
 
 constexpr int kChunk = 1024;
 
-__global__ void __launch_bounds__(64) permute_chunk_rank_kernel(
+__global__ void __launch_bounds__(256) permute_chunk_rank_kernel(
     const int32_t* __restrict__ topk_idx, int64_t TK, int expert_begin, int El, int nbits,
     int32_t* __restrict__ table /* [nchunks][El] */, int32_t* __restrict__ rank /* [TK] */) {
-  __shared__ int32_t running[1024];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < El; e += kWave) running[e] = 0;
-  __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * kChunk;
+  // wave w ranks slots [256 w, 256 w + 256) of the chunk, 64 at a time, with
+  // its own running per-expert counts; afterwards each slot adds the counts
+  // of the waves before it
+  __shared__ int32_t cnt[4][1024];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int e = lane; e < El; e += kWave) cnt[w][e] = 0;
+  const int64_t base = (int64_t)blockIdx.x * kChunk + w * (kChunk / 4);
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int step = 0; step < kChunk / kWave; ++step) {
+  constexpr int kSteps = kChunk / 4 / kWave;
+  int my_e[kSteps], my_r[kSteps];
+#pragma unroll
+  for (int step = 0; step < kSteps; ++step) {
     const int64_t i = base + step * kWave + lane;
     int e = -1;
     if (i < TK) {
-      int id = topk_idx[i];
-      int le = id - expert_begin;
+      const int id = topk_idx[i];
+      const int le = id - expert_begin;
       if (id >= 0 && le >= 0 && le < El) e = le;
     }
     uint64_t peers = __ballot(e >= 0);
@@ -53,15 +59,29 @@ __global__ void __launch_bounds__(64) permute_chunk_rank_kernel(
     }
     const int below = __popcll(peers & lt_mask);
     int before = 0;
-    if (e >= 0) before = running[e];
-    // all lanes have read running[] before any leader updates it (one wave,
-    // LDS operations retire in program order)
-    if (e >= 0 && below == 0) running[e] = before + __popcll(peers);
-    if (i < TK) rank[i] = e >= 0 ? before + below : -1;
+    if (e >= 0) before = cnt[w][e];
+    // every lane has read cnt[] before a leader updates it (one wave, LDS
+    // operations retire in program order)
+    if (e >= 0 && below == 0) cnt[w][e] = before + __popcll(peers);
+    my_e[step] = e;
+    my_r[step] = before + below;
   }
   __syncthreads();
+#pragma unroll
+  for (int step = 0; step < kSteps; ++step) {
+    const int64_t i = base + step * kWave + lane;
+    if (i >= TK) continue;
+    const int e = my_e[step];
+    int r = -1;
+    if (e >= 0) {
+      r = my_r[step];
+      for (int v = 0; v < w; ++v) r += cnt[v][e];
+    }
+    rank[i] = r;
+  }
   int32_t* trow = table + (int64_t)blockIdx.x * El;
-  for (int e = lane; e < El; e += kWave) trow[e] = running[e];
+  for (int e = threadIdx.x; e < El; e += blockDim.x)
+    trow[e] = cnt[0][e] + cnt[1][e] + cnt[2][e] + cnt[3][e];
 }
 
 __device__ __forceinline__ int next_pow2_dev(int n) {
@@ -204,7 +224,7 @@ int launch_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t*
   while ((1 << nbits) < El) ++nbits;
 
   if (nchunks > 0)
-    hipLaunchKernelGGL(permute_chunk_rank_kernel, dim3(nchunks), dim3(kWave), 0, stream, topk_idx,
+    hipLaunchKernelGGL(permute_chunk_rank_kernel, dim3(nchunks), dim3(256), 0, stream, topk_idx,
                        TK, expert_begin, El, nbits, table, rank);
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, stream, table, nchunks, El,
                      pad_pow2, capacity, counts, cu_seqlens, src_of, w_perm, dev_error);

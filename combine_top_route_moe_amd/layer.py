@@ -18,7 +18,7 @@ and never allocates, so it can be timed back to back or captured in a graph.
 
 from __future__ import annotations
 
-from typing import Callable, Dict, Optional
+from typing import Callable, Dict, List, Optional, Tuple
 
 import torch
 
@@ -90,40 +90,43 @@ class MoELayer:
         self.shared_w13, self.shared_w2 = shared_w13, shared_w2
 
     # ------------------------------------------------------------------ stages
-    def forward(self, logits: torch.Tensor, hidden: torch.Tensor,
-                row_valid: Optional[torch.Tensor] = None,
-                mark: Optional[Callable[[str], None]] = None) -> torch.Tensor:
-        """Run the whole layer; ``mark(name)`` is called after each stage is
-        enqueued (the bench records events there)."""
-        m = mark or (lambda name: None)
-        ops.moe_route(logits, self.K, row_valid, self.renormalize, self.topk_idx, self.topk_w)
-        m("route")
-        x = hidden
-        if self.dispatch_block:
-            ops.moe_fake_quant_rows(hidden, self.hidden_q, None, ops.MOE_FQ_BLOCK,
-                                    self.dispatch_block)
-            x = self.hidden_q
-            m("dispatch_qdq")
+    def stages(self, logits: torch.Tensor, hidden: torch.Tensor,
+               row_valid: Optional[torch.Tensor] = None) -> List[Tuple[str, Callable[[], None]]]:
+        """The layer as an ordered list of ``(name, enqueue)`` stages.  Each
+        enqueue only launches kernels on the current stream; running a stage
+        again with the same inputs rewrites the same outputs."""
         p = self.perm
-        ops.moe_permute(self.topk_idx, self.topk_w, x, self.El, self.expert_begin, self.pad_pow2,
-                        self.capacity, p, self.perm_ws, self.dev_error)
-        m("permute")
         layout = ops.MOE_FFN_PACKED_WEIGHTS if self.packed else 0
-        ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, self.w13, self.w2, p.w_perm,
-                            self.y_perm, ops.MOE_FFN_GATE_UP | layout, self.ffn_ws, self.dev_error)
-        m("ffn_gate_up")
-        ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, self.w13, self.w2, p.w_perm,
-                            self.y_perm, ops.MOE_FFN_DOWN | layout, self.ffn_ws, self.dev_error)
-        m("ffn_down")
+        x = self.hidden_q if self.dispatch_block else hidden
+        st = [("route", lambda: ops.moe_route(logits, self.K, row_valid, self.renormalize,
+                                               self.topk_idx, self.topk_w))]
+        if self.dispatch_block:
+            st.append(("dispatch_qdq", lambda: ops.moe_fake_quant_rows(
+                hidden, self.hidden_q, None, ops.MOE_FQ_BLOCK, self.dispatch_block)))
+        st.append(("permute", lambda: ops.moe_permute(
+            self.topk_idx, self.topk_w, x, self.El, self.expert_begin, self.pad_pow2,
+            self.capacity, p, self.perm_ws, self.dev_error)))
+        st.append(("ffn_gate_up", lambda: ops.moe_grouped_ffn(
+            p.x_perm, p.cu_seqlens, p.counts, self.w13, self.w2, p.w_perm, self.y_perm,
+            ops.MOE_FFN_GATE_UP | layout, self.ffn_ws, self.dev_error)))
+        st.append(("ffn_down", lambda: ops.moe_grouped_ffn(
+            p.x_perm, p.cu_seqlens, p.counts, self.w13, self.w2, p.w_perm, self.y_perm,
+            ops.MOE_FFN_DOWN | layout, self.ffn_ws, self.dev_error)))
         if self.shared_I:
-            ops.moe_grouped_ffn(hidden, self.shared_cu, self.shared_counts, self.shared_w13,
-                                self.shared_w2, None, self.shared_out, ops.MOE_FFN_ALL | layout,
-                                self.shared_ws, self.dev_error)
-            m("shared_ffn")
-        ops.moe_combine(self.y_perm, p.row_of, self.T, self.K, self.shared_out,
-                        self.combine_scale if self.combine_qdq else None, self.out,
-                        self.dev_error)
-        m("combine")
+            st.append(("shared_ffn", lambda: ops.moe_grouped_ffn(
+                hidden, self.shared_cu, self.shared_counts, self.shared_w13, self.shared_w2,
+                None, self.shared_out, ops.MOE_FFN_ALL | layout, self.shared_ws,
+                self.dev_error)))
+        st.append(("combine", lambda: ops.moe_combine(
+            self.y_perm, p.row_of, self.T, self.K, self.shared_out,
+            self.combine_scale if self.combine_qdq else None, self.out, self.dev_error)))
+        return st
+
+    def forward(self, logits: torch.Tensor, hidden: torch.Tensor,
+                row_valid: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Run the whole layer (enqueue only; no sync, no allocation)."""
+        for _, enqueue in self.stages(logits, hidden, row_valid):
+            enqueue()
         return self.out
 
     def calibrate_combine_scale(self, logits, hidden, row_valid=None) -> torch.Tensor:

@@ -133,6 +133,20 @@ def cpu_baseline(cfg, logits, hidden, row_valid, budget_s: float):
                       f"whole layer, float64 numpy, median of {len(times)} runs: {dt:.2f} s"}
 
 
+def calibrate_spin(stream, target_ms: float = 1.0) -> int:
+    """Cycles for torch.cuda._sleep to keep the GPU busy about target_ms."""
+    import torch
+
+    cycles = 1 << 20
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    torch.cuda._sleep(cycles)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = max(a.elapsed_time(b), 1e-3)
+    return int(cycles * target_ms / ms)
+
+
 def copy_calibration(steps: int, warmup: int) -> None:
     """Time moe_copy_bytes over 1 GiB: the plain streaming kernel whose
     measured bandwidth and FETCH_SIZE / WRITE_SIZE counters calibrate the
@@ -252,25 +266,25 @@ def main():
     elapsed = time.perf_counter() - t0
     assert layer.dev_error.item() == 0, "device error word set during the timed run"
 
-    # Timed region 2 (stages, roofline): each stage's launches captured R times
-    # back to back into a HIP graph; K replays between two HIP events on the
-    # launch stream give the GPU time of one launch of the stage, free of
-    # host launch gaps.
-    reps = 10
-    stage_ms = {}
-    for name, enqueue in layer.stages(logits, hidden, row_valid):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(reps):
-                enqueue()
-        g.replay()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(args.steps):
-            g.replay()
-        b.record(stream)
+    # Timed region 2 (stages, roofline): K eager steps with HIP events between
+    # the stages on the launch stream.  Each step is preceded by a short GPU
+    # spin kernel, so the host has enqueued the whole step (and its events)
+    # before the GPU reaches it: the stages then run back to back, with the
+    # cache state of a real step, and the events time GPU work only.
+    stages = layer.stages(logits, hidden, row_valid)
+    spin_cycles = calibrate_spin(stream)
+    per_stage = {name: [] for name, _ in stages}
+    for _ in range(args.steps):
+        torch.cuda._sleep(spin_cycles)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+        evs[0].record(stream)
+        for i, (name, enqueue) in enumerate(stages):
+            enqueue()
+            evs[i + 1].record(stream)
         torch.cuda.synchronize()
-        stage_ms[name] = a.elapsed_time(b) / (args.steps * reps)
+        for i, (name, _) in enumerate(stages):
+            per_stage[name].append(evs[i].elapsed_time(evs[i + 1]))
+    stage_ms = {k: float(np.median(v)) for k, v in per_stage.items()}
     assert layer.dev_error.item() == 0, "device error word set during the stage timing"
 
     counts = layer.perm.counts.cpu().numpy()
@@ -332,8 +346,8 @@ def main():
         "roofline": roof,
         "timing": {"value": ("HIP-graph replay of the whole layer" if graph is not None
                              else "eager launches of the whole layer"),
-                   "stages": "per stage: HIP graph of 10 back-to-back launches, replayed "
-                             "`steps` times between HIP events on the launch stream"},
+                   "stages": "eager steps queued behind a GPU spin kernel, HIP events between "
+                             "stages on the launch stream, median over steps"},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -252,18 +252,23 @@ __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
 // weights as consecutive, perfectly coalesced 1 KB loads straight into the
 // registers the MFMA reads, with no LDS round trip and no barrier.
 //
-// The kernel: a workgroup of 4 waves covers up to 128 rows of one segment
-// (8 m-subtiles; the ones past the segment end are skipped) and 4 column
-// tiles (wave w owns tile 4*cb + w).  Weights are prefetched kPrefetch
-// K-steps ahead in registers.  The activation rows are shared by the four
+// The kernel: a workgroup of NW waves covers up to 128 rows of one segment
+// (8 m-subtiles; the ones past the segment end are skipped) and NW column
+// tiles (wave w owns tile NW*cb + w).  Weights are prefetched kPrefetch
+// K-steps ahead in registers.  The activation rows are shared by all the
 // waves: they go into LDS by direct-to-LDS DMA (global_load_lds_dwordx4), in
 // the same fragment order so every LDS read is one contiguous, conflict-free
-// 1 KB, through a two-stage ring of kChunkSteps K-steps per stage.
+// 1 KB, through a ring of kStages stages of kChunkSteps K-steps, the DMA
+// running two chunks ahead so that its latency hides behind compute.
 constexpr int kPrefetch = 4;     // weight K-steps in flight per wave
 constexpr int kChunkSteps = 2;   // activation K-steps per LDS stage
+constexpr int kStages = 3;       // activation LDS ring: DMA runs kStages-1 chunks ahead
 constexpr int kMsub = 8;         // 16-row m-subtiles per workgroup (128 rows)
 constexpr int kFrags = 4;        // B fragments per wave (one column tile)
 constexpr int kStageBlocks = kMsub * kChunkSteps;  // 1 KB blocks per LDS stage
+// Waves (= column tiles) per workgroup, NW: 8 when segments are long (the
+// activation tile is then shared by more columns), 4 when they are short (more,
+// smaller workgroups balance skewed segment sizes better).
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (and for nothing else)
@@ -271,59 +276,28 @@ __device__ __forceinline__ constexpr int vmcnt_imm(int n) {
   return (n & 0xf) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xf << 8);
 }
 
-template <bool GATE_UP>
-__global__ void __launch_bounds__(kThreads, 2) frag_gemm_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Wf,
-    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ counts, int G,
-    int Kdim, int Nw /* weight rows per group */, int Nout, const float* __restrict__ row_scale,
-    uint16_t* __restrict__ Out, int64_t capacity, int32_t* __restrict__ dev_error) {
-  __shared__ __attribute__((aligned(16))) u32x4_t As[2][kStageBlocks][kWave];
-
-  const int n_ct = Nw / 64;              // column tiles per group
-  const int n_cb = (n_ct + 3) / 4;       // column blocks (workgroups) per m-tile
-  const int pid = xcd_remap(blockIdx.x);
-  int g, mt, cb;
-  if (!decode_tile(pid, counts, G, n_cb, g, mt, cb)) return;
-  const int seg0 = cu_seqlens[g];
-  const int nrows = counts[g];
-  if ((int64_t)seg0 + nrows > capacity || seg0 < 0) {
-    if ((threadIdx.x & 63) == 0) raise_error(dev_error, MOE_DEVERR_ROW_RANGE);
-    return;
-  }
-  const int m0 = mt * kBM;
-  const int valid = min(kBM, nrows - m0);
-  if (valid <= 0) return;
-  const int64_t row_base = (int64_t)seg0 + m0;
-  const int nlive = (valid + 15) >> 4;   // m-subtiles holding real rows
-
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // the last column block may hold fewer than 4 tiles (w2 with H/64 odd
-  // multiples of 2): the spare waves stream a real tile and store nothing
-  const bool ct_ok = cb * 4 + w < n_ct;
-  const int ct = ct_ok ? cb * 4 + w : n_ct - 1;
-  const int nks = Kdim / 32;
-
-  // this wave's weight stream: step ks, fragment f at wp[(ks * 4 + f) * 64]
-  const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(Wf) +
-                      ((int64_t)g * n_ct + ct) * nks * (kFrags * kWave) + lane;
-  // the activation DMA: this wave fills LDS blocks b = 4w .. 4w+3 of a stage;
-  // block b is m-subtile b / kChunkSteps, K-step b % kChunkSteps of the chunk
-  const uint16_t* a_src[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int b = w * 4 + q;
-    const int ms = b / kChunkSteps, sub = b % kChunkSteps;
-    const int r = min(ms * 16 + (lane & 15), valid - 1);
-    a_src[q] = A + (row_base + r) * Kdim + sub * 32 + 8 * (lane >> 4);
-  }
+template <bool GATE_UP, bool NT, int NW>
+__device__ __forceinline__ void frag_gemm_body(
+    u32x4_t (*As)[kStageBlocks][kWave], const u32x4_t* __restrict__ wp,
+    const uint16_t* const* a_src, int w, int lane, int nks, int nlive, int valid, int ct,
+    bool ct_ok, int64_t row_base, int Nout, const float* __restrict__ row_scale,
+    uint16_t* __restrict__ Out) {
+  constexpr int kDmaPerWave = kStageBlocks / NW;  // DMA instructions per wave per stage
+  // LDS blocks of m-subtiles past the segment end are never read: skip them
   auto issue_chunk = [&](int chunk, int stage) {
     asm volatile("" ::: "memory");
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < kDmaPerWave; ++q) {
+      if ((w * kDmaPerWave + q) / kChunkSteps >= nlive) break;
       __builtin_amdgcn_global_load_lds(a_src[q] + chunk * (kChunkSteps * 32),
-                                       &As[stage][w * 4 + q][0], 16, 0, 0);
+                                       &As[stage][w * kDmaPerWave + q][0], 16, 0, 0);
+    }
     asm volatile("" ::: "memory");
+  };
+  // weights read exactly once stream past the caches (non-temporal)
+  auto load_w = [&](int idx) -> u32x4_t {
+    if (NT) return __builtin_nontemporal_load(&wp[idx]);
+    return wp[idx];
   };
 
   f32x4_t acc[kMsub][kFrags];
@@ -334,33 +308,39 @@ __global__ void __launch_bounds__(kThreads, 2) frag_gemm_kernel(
 
   const int nchunks = nks / kChunkSteps;
   issue_chunk(0, 0);
+  issue_chunk(min(1, nchunks - 1), 1);
   u32x4_t bq[kPrefetch][kFrags];
 #pragma unroll
   for (int s = 0; s < kPrefetch; ++s)
 #pragma unroll
-    for (int f = 0; f < kFrags; ++f) bq[s][f] = wp[(s * kFrags + f) * kWave];
+    for (int f = 0; f < kFrags; ++f) bq[s][f] = load_w((s * kFrags + f) * kWave);
   asm volatile("" ::: "memory");
 
+  // Loads complete in issue order, so waiting until at most n are
+  // outstanding, with n no larger than the number issued after the chunk's
+  // DMA, guarantees that DMA has landed.  After the DMA of chunk c (issued
+  // at the start of chunk c-2) come at least the weight loads of two chunks
+  // (the DMA of chunk c+1 may be empty for this wave); the prologue issues
+  // more than that.
+  constexpr int kAfterDma = (kStages - 1) * kChunkSteps * kFrags;
+  static_assert(kAfterDma <= kPrefetch * kFrags, "prologue count");
   // nks is a multiple of 4 = kPrefetch (K is a multiple of 128)
+  int stage = 0;  // ring slot of the current chunk
   for (int ks0 = 0; ks0 < nks; ks0 += kPrefetch) {
 #pragma unroll
     for (int s = 0; s < kPrefetch; ++s) {
       const int ks = ks0 + s;
       if (s % kChunkSteps == 0) {
         const int chunk = ks / kChunkSteps;
-        // the chunk's DMA was followed by kPrefetch * kFrags weight loads
-        // (the prologue) or by kChunkSteps * kFrags (steady state)
-        if (chunk == 0)
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPrefetch * kFrags));
-        else
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(kChunkSteps * kFrags));
+        if (chunk > 0) stage = (stage + 1 == kStages) ? 0 : stage + 1;
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAfterDma));
         __syncthreads();
-        // the other stage was last read in the previous chunk, which every
-        // wave has finished; past the last chunk this reloads a valid chunk
-        // so the number of outstanding loads stays the same
-        issue_chunk(min(chunk + 1, nchunks - 1), (chunk + 1) & 1);
+        // the slot two ahead was last read in the previous chunk, which every
+        // wave has finished; past the end this reloads a valid chunk so the
+        // number of outstanding loads stays the same
+        const int ahead = (stage + 2) % kStages;
+        issue_chunk(min(chunk + 2, nchunks - 1), ahead);
       }
-      const int stage = (ks / kChunkSteps) & 1;
       const int sub = ks % kChunkSteps;
 #pragma unroll
       for (int i = 0; i < kMsub; ++i) {
@@ -376,7 +356,7 @@ __global__ void __launch_bounds__(kThreads, 2) frag_gemm_kernel(
       const int nxt = min(ks + kPrefetch, nks - 1);
       asm volatile("" ::: "memory");
 #pragma unroll
-      for (int f = 0; f < kFrags; ++f) bq[s][f] = wp[(nxt * kFrags + f) * kWave];
+      for (int f = 0; f < kFrags; ++f) bq[s][f] = load_w((nxt * kFrags + f) * kWave);
       asm volatile("" ::: "memory");
     }
   }
@@ -409,6 +389,64 @@ __global__ void __launch_bounds__(kThreads, 2) frag_gemm_kernel(
       }
     }
   }
+}
+
+template <bool GATE_UP, int NW>
+__global__ void __launch_bounds__(NW * kWave, 2 * 4 / NW) frag_gemm_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Wf,
+    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ counts, int G,
+    int Kdim, int Nw /* weight rows per group */, int Nout, const float* __restrict__ row_scale,
+    uint16_t* __restrict__ Out, int64_t capacity, int32_t* __restrict__ dev_error) {
+  __shared__ __attribute__((aligned(16))) u32x4_t As[kStages][kStageBlocks][kWave];
+
+  const int n_ct = Nw / 64;              // column tiles per group
+  const int n_cb = (n_ct + NW - 1) / NW;  // workgroups per m-tile
+  const int pid = xcd_remap(blockIdx.x);
+  int g, mt, cb;
+  if (!decode_tile(pid, counts, G, n_cb, g, mt, cb)) return;
+  const int seg0 = cu_seqlens[g];
+  const int nrows = counts[g];
+  if ((int64_t)seg0 + nrows > capacity || seg0 < 0) {
+    if ((threadIdx.x & 63) == 0) raise_error(dev_error, MOE_DEVERR_ROW_RANGE);
+    return;
+  }
+  const int m0 = mt * kBM;
+  const int valid = min(kBM, nrows - m0);
+  if (valid <= 0) return;
+  const int64_t row_base = (int64_t)seg0 + m0;
+  const int nlive = (valid + 15) >> 4;   // m-subtiles holding real rows
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // the last column block may hold fewer than NW tiles: the spare
+  // waves stream a real tile and store nothing
+  const bool ct_ok = cb * NW + w < n_ct;
+  const int ct = ct_ok ? cb * NW + w : n_ct - 1;
+  const int nks = Kdim / 32;
+
+  // this wave's weight stream: step ks, fragment f at wp[(ks * 4 + f) * 64]
+  const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(Wf) +
+                      ((int64_t)g * n_ct + ct) * nks * (kFrags * kWave) + lane;
+  // the activation DMA: this wave fills LDS blocks kDmaPerWave*w .. of a
+  // stage; block b is m-subtile b / kChunkSteps, K-step b % kChunkSteps
+  constexpr int kDmaPerWave = kStageBlocks / NW;
+  const uint16_t* a_src[kDmaPerWave];
+#pragma unroll
+  for (int q = 0; q < kDmaPerWave; ++q) {
+    const int b = w * kDmaPerWave + q;
+    const int ms = b / kChunkSteps, sub = b % kChunkSteps;
+    const int r = min(ms * 16 + (lane & 15), valid - 1);
+    a_src[q] = A + (row_base + r) * Kdim + sub * 32 + 8 * (lane >> 4);
+  }
+
+  // an expert whose rows fit in one m-tile reads each weight byte once
+  const bool once = nrows <= kBM;
+  if (once)
+    frag_gemm_body<GATE_UP, true, NW>(As, wp, a_src, w, lane, nks, nlive, valid, ct, ct_ok, row_base,
+                                  Nout, row_scale, Out);
+  else
+    frag_gemm_body<GATE_UP, false, NW>(As, wp, a_src, w, lane, nks, nlive, valid, ct, ct_ok, row_base,
+                                   Nout, row_scale, Out);
 }
 
 // Packing: one thread per 16-byte vector of the packed layout.
@@ -473,29 +511,50 @@ int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32
     return (m_tiles * n_tiles + grid_unit - 1) / grid_unit * grid_unit;
   };
   if (capacity == 0) return MOE_OK;
+  // long segments (mean >= one m-tile) share each activation tile across 8
+  // column tiles; short ones use 4-wave workgroups
+  const bool wide = capacity >= (int64_t)G * kBM;
   if (flags & MOE_FFN_GATE_UP) {
-    const int64_t blocks = grid_for(packed ? (2 * I / 64) / 4 : I / (kBN / 2));
-    if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-    if (packed)
-      hipLaunchKernelGGL(frag_gemm_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                         x, w13, cu_seqlens, counts, G, H, 2 * I, I, nullptr, act, capacity,
-                         dev_error);
-    else
+    if (packed) {
+      const int nw = wide ? 8 : 4;
+      const int64_t blocks = grid_for((2 * I / 64 + nw - 1) / nw);
+      if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+      if (wide)
+        hipLaunchKernelGGL((frag_gemm_kernel<true, 8>), dim3((unsigned)blocks), dim3(8 * kWave), 0,
+                           stream, x, w13, cu_seqlens, counts, G, H, 2 * I, I, nullptr, act,
+                           capacity, dev_error);
+      else
+        hipLaunchKernelGGL((frag_gemm_kernel<true, 4>), dim3((unsigned)blocks), dim3(4 * kWave), 0,
+                           stream, x, w13, cu_seqlens, counts, G, H, 2 * I, I, nullptr, act,
+                           capacity, dev_error);
+    } else {
+      const int64_t blocks = grid_for(I / (kBN / 2));
+      if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
       hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0,
                          stream, x, w13, cu_seqlens, counts, G, H, 2 * I, I, nullptr, act,
                          capacity, dev_error);
+    }
   }
   if (flags & MOE_FFN_DOWN) {
-    const int64_t blocks = grid_for(packed ? (H / 64 + 3) / 4 : H / kBN);
-    if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-    if (packed)
-      hipLaunchKernelGGL(frag_gemm_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                         stream, act, w2, cu_seqlens, counts, G, I, H, H, row_scale, y, capacity,
-                         dev_error);
-    else
+    if (packed) {
+      const int nw = wide ? 8 : 4;
+      const int64_t blocks = grid_for((H / 64 + nw - 1) / nw);
+      if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+      if (wide)
+        hipLaunchKernelGGL((frag_gemm_kernel<false, 8>), dim3((unsigned)blocks), dim3(8 * kWave),
+                           0, stream, act, w2, cu_seqlens, counts, G, I, H, H, row_scale, y,
+                           capacity, dev_error);
+      else
+        hipLaunchKernelGGL((frag_gemm_kernel<false, 4>), dim3((unsigned)blocks), dim3(4 * kWave),
+                           0, stream, act, w2, cu_seqlens, counts, G, I, H, H, row_scale, y,
+                           capacity, dev_error);
+    } else {
+      const int64_t blocks = grid_for(H / kBN);
+      if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
       hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0,
                          stream, act, w2, cu_seqlens, counts, G, I, H, H, row_scale, y, capacity,
                          dev_error);
+    }
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

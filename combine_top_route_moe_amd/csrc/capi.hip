@@ -17,7 +17,7 @@ size_t permute_workspace_bytes(int64_t, int);
 int launch_permute(const int32_t*, const float*, const uint16_t*, int, int, int, int, int, int,
                    int64_t, int32_t*, int32_t*, uint16_t*, int32_t*, int32_t*, float*, void*,
                    int32_t*, hipStream_t);
-size_t grouped_ffn_workspace_bytes(int64_t, int);
+size_t grouped_ffn_workspace_bytes(int64_t, int, int);
 int launch_grouped_ffn(const uint16_t*, const int32_t*, const int32_t*, int, int, int,
                        const uint16_t*, const uint16_t*, const float*, uint16_t*, int64_t, int,
                        void*, int32_t*, hipStream_t);
@@ -110,10 +110,9 @@ int moe_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t* hi
 }
 
 size_t moe_grouped_ffn_workspace_bytes(int64_t capacity, int num_groups, int H, int I) {
-  (void)num_groups;
   (void)H;
-  if (capacity < 0 || I < 1) return 0;
-  return grouped_ffn_workspace_bytes(capacity, I);
+  if (capacity < 0 || I < 1 || num_groups < 1) return 0;
+  return grouped_ffn_workspace_bytes(capacity, num_groups, I);
 }
 
 int moe_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32_t* counts,
@@ -132,7 +131,7 @@ int moe_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32_t*
   if ((x && !aligned16(x)) || (y && !aligned16(y)) || (w13 && !aligned16(w13)) ||
       (w2 && !aligned16(w2)))
     return MOE_ERR_INVALID_ARG;
-  const size_t need = grouped_ffn_workspace_bytes(capacity, I);
+  const size_t need = grouped_ffn_workspace_bytes(capacity, num_groups, I);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return MOE_ERR_WORKSPACE;
   return launch_grouped_ffn(x, cu_seqlens, counts, num_groups, H, I, w13, w2, row_scale, y,

@@ -66,7 +66,8 @@ __device__ __forceinline__ int xcd_remap(int bid) {
 // Decode tile number `pid` into (group, m-tile, n-tile).  Every lane of the
 // calling wave returns the same answer; returns false past the last tile.
 __device__ __forceinline__ bool decode_tile(int pid, const int32_t* __restrict__ counts, int G,
-                                            int n_tiles, int& g, int& mt, int& nt) {
+                                            int n_tiles, int& g, int& mt, int& nt,
+                                            int* mt_base = nullptr) {
   const int lane = threadIdx.x & 63;
   int carry = 0;
   for (int base = 0; base < G; base += kWave) {
@@ -85,10 +86,12 @@ __device__ __forceinline__ bool decode_tile(int pid, const int32_t* __restrict__
     if (hit) {
       const int src = __ffsll((unsigned long long)hit) - 1;
       g = base + src;
-      const int local = pid - __shfl(excl, src, kWave);
+      const int ex = __shfl(excl, src, kWave);
+      const int local = pid - ex;
       const int mtiles = (__shfl(c, src, kWave) + kBM - 1) / kBM;
       nt = local / mtiles;
       mt = local - nt * mtiles;
+      if (mt_base) *mt_base = ex / n_tiles;  // m-tiles of the groups before g
       return true;
     }
     carry = __shfl(incl, 63, kWave);
@@ -279,17 +282,24 @@ __device__ __forceinline__ constexpr int vmcnt_imm(int n) {
 template <bool GATE_UP, bool NT, int NW>
 __device__ __forceinline__ void frag_gemm_body(
     u32x4_t (*As)[kStageBlocks][kWave], const u32x4_t* __restrict__ wp,
-    const uint16_t* const* a_src, int w, int lane, int nks, int nlive, int valid, int ct,
-    bool ct_ok, int64_t row_base, int Nout, const float* __restrict__ row_scale,
-    uint16_t* __restrict__ Out) {
-  constexpr int kDmaPerWave = kStageBlocks / NW;  // DMA instructions per wave per stage
+    const uint16_t* const* a_src, int a_chunk_stride, int w, int lane, int nks, int nlive,
+    int valid, int ct, bool ct_ok, int64_t row_base, int64_t mt_glob, int Nout,
+    const float* __restrict__ row_scale, uint16_t* __restrict__ Out, int crot) {
+  constexpr int kDmaPerWave = kStageBlocks / NW;
+  // every workgroup walks K from its own starting chunk (crot) and wraps
+  // around, so the many weight streams do not all hit the same offsets —
+  // and so the same HBM channels — at the same time
+  const int nch = nks / kChunkSteps;
+  const int krot = crot * kChunkSteps;
+  // x in [0, 2n) -> x mod n, without a division in the inner loop
+  auto wrap = [](int x, int n) { return x >= n ? x - n : x; };
   // LDS blocks of m-subtiles past the segment end are never read: skip them
   auto issue_chunk = [&](int chunk, int stage) {
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q) {
       if ((w * kDmaPerWave + q) / kChunkSteps >= nlive) break;
-      __builtin_amdgcn_global_load_lds(a_src[q] + chunk * (kChunkSteps * 32),
+      __builtin_amdgcn_global_load_lds(a_src[q] + (int64_t)wrap(chunk + crot, nch) * a_chunk_stride,
                                        &As[stage][w * kDmaPerWave + q][0], 16, 0, 0);
     }
     asm volatile("" ::: "memory");
@@ -313,7 +323,7 @@ __device__ __forceinline__ void frag_gemm_body(
 #pragma unroll
   for (int s = 0; s < kPrefetch; ++s)
 #pragma unroll
-    for (int f = 0; f < kFrags; ++f) bq[s][f] = load_w((s * kFrags + f) * kWave);
+    for (int f = 0; f < kFrags; ++f) bq[s][f] = load_w((wrap(s + krot, nks) * kFrags + f) * kWave);
   asm volatile("" ::: "memory");
 
   // Loads complete in issue order, so waiting until at most n are
@@ -356,7 +366,7 @@ __device__ __forceinline__ void frag_gemm_body(
       const int nxt = min(ks + kPrefetch, nks - 1);
       asm volatile("" ::: "memory");
 #pragma unroll
-      for (int f = 0; f < kFrags; ++f) bq[s][f] = load_w((nxt * kFrags + f) * kWave);
+      for (int f = 0; f < kFrags; ++f) bq[s][f] = load_w((wrap(nxt + krot, nks) * kFrags + f) * kWave);
       asm volatile("" ::: "memory");
     }
   }
@@ -373,12 +383,18 @@ __device__ __forceinline__ void frag_gemm_body(
       if (r >= valid) continue;
       const int64_t orow = row_base + r;
       if (GATE_UP) {
+        // a is written in the down GEMM's activation fragment order: block
+        // (m-tile, m-subtile i, K-step ct) of 64 lanes x 8 values, where lane
+        // L = row%16 + 16*(col%32 / 8) holds columns 8*(col%32 / 8) .. +8
+        uint16_t* blk = Out + ((mt_glob * kMsub + i) * (int64_t)(Nout / 32) + ct) * (kWave * 8);
+        const int rr = 4 * (lane >> 4) + q;
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-          const int col = ct * 32 + f * 16 + (lane & 15);
-          Out[orow * Nout + col] =
+          const int c32 = f * 16 + (lane & 15);
+          blk[(rr + 16 * (c32 >> 3)) * 8 + (c32 & 7)] =
               (uint16_t)f32_to_bf16(silu_f(acc[i][f][q]) * acc[i][f + 2][q]);
         }
+        (void)orow;
       } else {
         const float sc = row_scale ? row_scale[orow] : 1.0f;
 #pragma unroll
@@ -402,8 +418,8 @@ __global__ void __launch_bounds__(NW * kWave, 2 * 4 / NW) frag_gemm_kernel(
   const int n_ct = Nw / 64;              // column tiles per group
   const int n_cb = (n_ct + NW - 1) / NW;  // workgroups per m-tile
   const int pid = xcd_remap(blockIdx.x);
-  int g, mt, cb;
-  if (!decode_tile(pid, counts, G, n_cb, g, mt, cb)) return;
+  int g, mt, cb, mt_base;
+  if (!decode_tile(pid, counts, G, n_cb, g, mt, cb, &mt_base)) return;
   const int seg0 = cu_seqlens[g];
   const int nrows = counts[g];
   if ((int64_t)seg0 + nrows > capacity || seg0 < 0) {
@@ -430,23 +446,36 @@ __global__ void __launch_bounds__(NW * kWave, 2 * 4 / NW) frag_gemm_kernel(
   // the activation DMA: this wave fills LDS blocks kDmaPerWave*w .. of a
   // stage; block b is m-subtile b / kChunkSteps, K-step b % kChunkSteps
   constexpr int kDmaPerWave = kStageBlocks / NW;
+  // gate/up reads the permuted rows (row-major); down reads the gate/up
+  // output, which that kernel wrote in fragment order per m-tile
   const uint16_t* a_src[kDmaPerWave];
+  const int64_t mt_glob = (int64_t)mt_base + mt;
 #pragma unroll
   for (int q = 0; q < kDmaPerWave; ++q) {
     const int b = w * kDmaPerWave + q;
     const int ms = b / kChunkSteps, sub = b % kChunkSteps;
-    const int r = min(ms * 16 + (lane & 15), valid - 1);
-    a_src[q] = A + (row_base + r) * Kdim + sub * 32 + 8 * (lane >> 4);
+    if (GATE_UP) {
+      const int r = min(ms * 16 + (lane & 15), valid - 1);
+      a_src[q] = A + (row_base + r) * Kdim + sub * 32 + 8 * (lane >> 4);
+    } else {
+      a_src[q] = A + ((mt_glob * kMsub + ms) * (int64_t)nks + sub) * (kWave * 8) + lane * 8;
+    }
   }
+  const int a_chunk_stride = GATE_UP ? kChunkSteps * 32 : kChunkSteps * kWave * 8;
 
   // an expert whose rows fit in one m-tile reads each weight byte once
   const bool once = nrows <= kBM;
+  // K rotation for experts read once; experts with several m-tiles keep every
+  // workgroup in step, so that their m-tiles share the weights and their
+  // column blocks share the activation tiles through L2
+  const int crot =
+      once ? (int)(((uint32_t)(g * 977 + cb) * 2654435761u) >> 8) % (nks / kChunkSteps) : 0;
   if (once)
-    frag_gemm_body<GATE_UP, true, NW>(As, wp, a_src, w, lane, nks, nlive, valid, ct, ct_ok, row_base,
-                                  Nout, row_scale, Out);
+    frag_gemm_body<GATE_UP, true, NW>(As, wp, a_src, a_chunk_stride, w, lane, nks, nlive, valid,
+                                      ct, ct_ok, row_base, mt_glob, Nout, row_scale, Out, crot);
   else
-    frag_gemm_body<GATE_UP, false, NW>(As, wp, a_src, w, lane, nks, nlive, valid, ct, ct_ok, row_base,
-                                   Nout, row_scale, Out);
+    frag_gemm_body<GATE_UP, false, NW>(As, wp, a_src, a_chunk_stride, w, lane, nks, nlive, valid,
+                                       ct, ct_ok, row_base, mt_glob, Nout, row_scale, Out, crot);
 }
 
 // Packing: one thread per 16-byte vector of the packed layout.
@@ -495,8 +524,12 @@ int launch_pack_weights(const uint16_t* w13, const uint16_t* w2, int G, int H, i
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-size_t grouped_ffn_workspace_bytes(int64_t capacity, int I) {
-  return (((size_t)capacity * I * sizeof(uint16_t)) + 255) & ~(size_t)255;
+// The intermediate a: row-major [capacity, I] for row-major weights; with
+// packed weights, fragment order per m-tile (at most ceil(capacity/128) + G
+// m-tiles of 128 rows).  The workspace covers both.
+size_t grouped_ffn_workspace_bytes(int64_t capacity, int G, int I) {
+  const int64_t rows = std::max<int64_t>(capacity, ((capacity + kBM - 1) / kBM + G) * kBM);
+  return (((size_t)rows * I * sizeof(uint16_t)) + 255) & ~(size_t)255;
 }
 
 int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32_t* counts, int G,

@@ -104,11 +104,95 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
   }
 }
 
+// Rank form for E <= 64: every lane counts how many logits precede its own
+// in the (larger value, then lower index) order — reading the row back from
+// LDS as broadcasts — and the lanes whose rank is below K write that slot
+// directly, with no serial argmax rounds.  The count costs E^2/64 compares
+// per lane, so wider rows use the argmax kernel above.
+template <int EPL>
+__global__ void __launch_bounds__(256) route_rank_kernel(const float* __restrict__ logits,
+                                                         const uint8_t* __restrict__ row_valid,
+                                                         int T, int E, int K, int renorm,
+                                                         int32_t* __restrict__ topk_idx,
+                                                         float* __restrict__ topk_w) {
+  constexpr int kMaxE = EPL * kWave;
+  __shared__ __attribute__((aligned(16))) float row_lds[4][kMaxE];
+  __shared__ float sel_lds[4][32];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wv;
+  if (t >= T) return;
+  int32_t* out_idx = topk_idx + (int64_t)t * K;
+  float* out_w = topk_w + (int64_t)t * K;
+  if (row_valid && !row_valid[t]) {
+    for (int k = lane; k < K; k += kWave) {
+      out_idx[k] = -1;
+      out_w[k] = 0.0f;
+    }
+    return;
+  }
+  const float* row = logits + (int64_t)t * E;
+  float v[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + j * kWave;
+    v[j] = e < E ? row[e] : 0.0f;
+    row_lds[wv][e] = v[j];
+  }
+  // one wave owns row_lds[wv]; its writes are visible to its own later reads
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  int rank[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) rank[j] = 0;
+  for (int c = 0; c < E; c += 4) {
+    const float4 q = *reinterpret_cast<const float4*>(&row_lds[wv][c]);
+    const float qv[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ej = c + u;
+      if (ej >= E) break;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = lane + j * kWave;
+        rank[j] += (qv[u] > v[j]) || (qv[u] == v[j] && ej < e);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + j * kWave;
+    if (e < E && rank[j] < K) {
+      out_idx[rank[j]] = e;
+      sel_lds[wv][rank[j]] = v[j];
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  // weights: exp(l_k - l_max) / sum, in double; lane k < K holds slot k
+  const double lmax = (double)sel_lds[wv][0];
+  double num = 0.0;
+  if (lane < K) num = exp((double)sel_lds[wv][lane] - lmax);
+  double den = 0.0;
+  if (renorm) {
+    den = num;
+  } else {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (lane + j * kWave < E) den += exp((double)v[j] - lmax);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, kWave);
+  if (lane < K) out_w[lane] = (float)(num / den);
+}
+
 int launch_route(const float* logits, const uint8_t* row_valid, int T, int E, int K, int renorm,
                  int32_t* topk_idx, float* topk_w, hipStream_t stream) {
   const int waves = 4;
   dim3 grid((T + waves - 1) / waves), block(waves * kWave);
   int epl = (E + kWave - 1) / kWave;
+  if (E % 4 == 0 && epl <= 1) {
+    hipLaunchKernelGGL(route_rank_kernel<1>, grid, block, 0, stream, logits, row_valid, T, E, K,
+                       renorm, topk_idx, topk_w);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
 #define MOE_ROUTE_CASE(N)                                                                  \
   if (epl <= N) {                                                                          \
     hipLaunchKernelGGL(route_kernel<N>, grid, block, 0, stream, logits, row_valid, T, E, K, \

@@ -246,14 +246,17 @@ __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
 // ---------------------------------------------------------------------------
 // Packed weights and the fragment-streaming GEMM.
 //
-// Packed layout ("fragment order"): for every group, every column tile of 64
-// weight rows and every 32-wide K-step, the four 16x32 MFMA B-fragments of
-// that tile are stored back to back, each as 64 lanes x 16 bytes in lane
-// order: lane l holds W[row0 + l%16][k0 + 8*(l/16) .. +8].  A w13 column tile
-// is 32 gate rows (fragments 0, 1) and the 32 matching up rows (fragments 2,
-// 3); a w2 column tile is 64 consecutive rows.  A wave therefore streams its
-// weights as consecutive, perfectly coalesced 1 KB loads straight into the
-// registers the MFMA reads, with no LDS round trip and no barrier.
+// Packed layout ("fragment order", K-major): for every group and every
+// 32-wide K-step, the column tiles of 64 weight rows follow one another, and
+// each holds its four 16x32 MFMA B-fragments back to back, each as 64 lanes x
+// 16 bytes in lane order: lane l holds W[row0 + l%16][k0 + 8*(l/16) .. +8].
+// A w13 column tile is 32 gate rows (fragments 0, 1) and the 32 matching up
+// rows (fragments 2, 3); a w2 column tile is 64 consecutive rows.  A wave
+// therefore streams its weights as perfectly coalesced 1 KB loads straight
+// into the registers the MFMA reads, with no LDS round trip and no barrier;
+// and all the workgroups of one expert, kept in step, read one compact
+// window of memory at a time (better DRAM row locality than one stream per
+// column tile).
 //
 // The kernel: a workgroup of NW waves covers up to 128 rows of one segment
 // (8 m-subtiles; the ones past the segment end are skipped) and NW column
@@ -281,7 +284,7 @@ __device__ __forceinline__ constexpr int vmcnt_imm(int n) {
 
 template <bool GATE_UP, bool NT, int NW>
 __device__ __forceinline__ void frag_gemm_body(
-    u32x4_t (*As)[kStageBlocks][kWave], const u32x4_t* __restrict__ wp,
+    u32x4_t (*As)[kStageBlocks][kWave], const u32x4_t* __restrict__ wp, int kstride,
     const uint16_t* const* a_src, int a_chunk_stride, int w, int lane, int nks, int nlive,
     int valid, int ct, bool ct_ok, int64_t row_base, int64_t mt_glob, int Nout,
     const float* __restrict__ row_scale, uint16_t* __restrict__ Out, int crot) {
@@ -323,7 +326,7 @@ __device__ __forceinline__ void frag_gemm_body(
 #pragma unroll
   for (int s = 0; s < kPrefetch; ++s)
 #pragma unroll
-    for (int f = 0; f < kFrags; ++f) bq[s][f] = load_w((wrap(s + krot, nks) * kFrags + f) * kWave);
+    for (int f = 0; f < kFrags; ++f) bq[s][f] = load_w(wrap(s + krot, nks) * kstride + f * kWave);
   asm volatile("" ::: "memory");
 
   // Loads complete in issue order, so waiting until at most n are
@@ -366,7 +369,7 @@ __device__ __forceinline__ void frag_gemm_body(
       const int nxt = min(ks + kPrefetch, nks - 1);
       asm volatile("" ::: "memory");
 #pragma unroll
-      for (int f = 0; f < kFrags; ++f) bq[s][f] = load_w((wrap(nxt + krot, nks) * kFrags + f) * kWave);
+      for (int f = 0; f < kFrags; ++f) bq[s][f] = load_w(wrap(nxt + krot, nks) * kstride + f * kWave);
       asm volatile("" ::: "memory");
     }
   }
@@ -440,9 +443,11 @@ __global__ void __launch_bounds__(NW * kWave, 2 * 4 / NW) frag_gemm_kernel(
   const int ct = ct_ok ? cb * NW + w : n_ct - 1;
   const int nks = Kdim / 32;
 
-  // this wave's weight stream: step ks, fragment f at wp[(ks * 4 + f) * 64]
+  // this wave's weight stream: step ks, fragment f at wp[ks * kstride + f * 64]
+  // (16-byte units)
+  const int kstride = n_ct * kFrags * kWave;
   const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(Wf) +
-                      ((int64_t)g * n_ct + ct) * nks * (kFrags * kWave) + lane;
+                      ((int64_t)g * nks * n_ct + ct) * (kFrags * kWave) + lane;
   // the activation DMA: this wave fills LDS blocks kDmaPerWave*w .. of a
   // stage; block b is m-subtile b / kChunkSteps, K-step b % kChunkSteps
   constexpr int kDmaPerWave = kStageBlocks / NW;
@@ -465,46 +470,52 @@ __global__ void __launch_bounds__(NW * kWave, 2 * 4 / NW) frag_gemm_kernel(
 
   // an expert whose rows fit in one m-tile reads each weight byte once
   const bool once = nrows <= kBM;
-  // K rotation for experts read once; experts with several m-tiles keep every
+  // K rotation for experts read once, so that the experts in flight do not
+  // all read the same K offsets (the same HBM channels) at the same time:
+  // per expert with 8-wave workgroups (the expert's workgroups stay in step
+  // and read one compact window), per workgroup with 4-wave ones (measured
+  // faster for short segments).  Experts with several m-tiles keep every
   // workgroup in step, so that their m-tiles share the weights and their
-  // column blocks share the activation tiles through L2
-  const int crot =
-      once ? (int)(((uint32_t)(g * 977 + cb) * 2654435761u) >> 8) % (nks / kChunkSteps) : 0;
+  // column blocks share the activation tiles through L2.
+  const uint32_t rkey = NW == 8 ? (uint32_t)g * 977u : (uint32_t)g * 977u + (uint32_t)cb;
+  const int crot = once ? (int)((rkey * 2654435761u) >> 8) % (nks / kChunkSteps) : 0;
   if (once)
-    frag_gemm_body<GATE_UP, true, NW>(As, wp, a_src, a_chunk_stride, w, lane, nks, nlive, valid,
+    frag_gemm_body<GATE_UP, true, NW>(As, wp, kstride, a_src, a_chunk_stride, w, lane, nks, nlive, valid,
                                       ct, ct_ok, row_base, mt_glob, Nout, row_scale, Out, crot);
   else
-    frag_gemm_body<GATE_UP, false, NW>(As, wp, a_src, a_chunk_stride, w, lane, nks, nlive, valid,
+    frag_gemm_body<GATE_UP, false, NW>(As, wp, kstride, a_src, a_chunk_stride, w, lane, nks, nlive, valid,
                                        ct, ct_ok, row_base, mt_glob, Nout, row_scale, Out, crot);
 }
 
-// Packing: one thread per 16-byte vector of the packed layout.
+// Packing: one thread per 16-byte vector of the source (coalesced reads),
+// each written to its place in the packed layout.
 __global__ void __launch_bounds__(256) pack_weights_kernel(const uint16_t* __restrict__ W,
                                                            uint16_t* __restrict__ P, int G,
                                                            int N, int Kdim, int gate_up) {
   const int64_t nvec = (int64_t)G * N * Kdim / 8;
   const int nks = Kdim / 32;
   const int n_ct = N / 64;
+  const int kvec = Kdim / 8;
   for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec;
        v += (int64_t)gridDim.x * blockDim.x) {
-    const int lane = (int)(v % kWave);
-    int64_t t = v / kWave;
-    const int f = (int)(t % kFrags);
-    t /= kFrags;
-    const int ks = (int)(t % nks);
-    t /= nks;
-    const int ct = (int)(t % n_ct);
-    const int64_t g = t / n_ct;
-    int row;
+    const int k8 = (int)(v % kvec);
+    const int64_t gr = v / kvec;
+    const int row = (int)(gr % N);
+    const int64_t g = gr / N;
+    int ct, f;
     if (gate_up) {
-      const int half = N / 2;  // I
-      row = (f < 2) ? ct * 32 + f * 16 + (lane & 15) : half + ct * 32 + (f - 2) * 16 + (lane & 15);
+      const int half = N / 2;  // I: gate rows, then up rows
+      const int r = row < half ? row : row - half;
+      ct = r / 32;
+      f = (row < half ? 0 : 2) + (r % 32) / 16;
     } else {
-      row = ct * 64 + f * 16 + (lane & 15);
+      ct = row / 64;
+      f = (row % 64) / 16;
     }
-    const int k = ks * 32 + 8 * (lane >> 4);
-    reinterpret_cast<uint4*>(P)[v] =
-        *reinterpret_cast<const uint4*>(W + (g * N + row) * (int64_t)Kdim + k);
+    const int ks = k8 / 4;
+    const int lane = (row & 15) + 16 * (k8 & 3);
+    const int64_t dst = (((g * nks + ks) * n_ct + ct) * kFrags + f) * kWave + lane;
+    reinterpret_cast<uint4*>(P)[dst] = reinterpret_cast<const uint4*>(W)[v];
   }
 }
 

@@ -171,14 +171,17 @@ int moe_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32_t*
                     void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream);
 
 /* Rearrange expert weights, once, into the layout the grouped GEMM streams
- * best: for every group, n-tile and 64-wide K-slab, the 128 x 64 block one
- * GEMM step consumes is stored contiguously (16 KB), so each step reads one
- * contiguous run of HBM instead of 128 short pieces of rows 2*H or 2*I bytes
- * apart.  A w13 n-tile holds 64 gate rows followed by the 64 matching up
- * rows.  w13 [G, 2I, H] -> w13_packed (same size); w2 [G, H, I] -> w2_packed
- * (same size); either pair may be NULL.  Outputs must not alias inputs.
- * Weights are static, so this runs at load time, not per layer call.
- * Requires H % 128 == 0, I % 128 == 0. */
+ * straight into its matrix-core registers ("fragment order", K-major).  For
+ * group g, K-step ks (32 columns of the reduction dimension) and column tile
+ * ct (64 weight rows), the tile's four 16 x 32 fragments f = 0..3 sit at
+ * 16-byte unit ((g * (Kdim/32) + ks) * n_ct + ct) * 256 + f * 64 + l, where
+ * lane l = 0..63 holds the 8 values W[row0(ct, f) + l % 16][32 ks + 8 (l / 16)
+ * .. +8].  For w2 [G, H, I] (Kdim = I, n_ct = H/64) row0 = 64 ct + 16 f; for
+ * w13 [G, 2I, H] (Kdim = H, n_ct = I/32) fragments 0, 1 are gate rows
+ * 32 ct + 16 f and fragments 2, 3 the matching up rows I + 32 ct + 16 (f - 2).
+ * Outputs have the inputs' sizes; either pair may be NULL; outputs must not
+ * alias inputs.  Weights are static, so this runs at load time, not per
+ * layer call.  Requires H % 128 == 0, I % 128 == 0. */
 int moe_pack_ffn_weights(const uint16_t* w13, const uint16_t* w2, int num_groups, int H, int I,
                          uint16_t* w13_packed, uint16_t* w2_packed, void* stream);
 

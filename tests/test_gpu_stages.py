@@ -344,28 +344,31 @@ def test_ffn_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("H,I,T", [(512, 256, 300), (128, 128, 40), (384, 256, 700)])
+@pytest.mark.parametrize("H,I,T", [(512, 256, 300), (128, 128, 40), (384, 256, 700),
+                                   (256, 256, 2000)])
 def test_ffn_packed_weights(H, I, T):
     """Packed weights in MFMA fragment order: the packing is the documented
     permutation of the input, and the fragment-streaming GEMM matches the
-    oracle (including a partial column block when H/64 is not a multiple
-    of 4, and several m-tiles per expert)."""
+    oracle.  The cases cover both workgroup widths (4 waves when segments
+    average under 128 rows, 8 above), a partial column block (H/64 not a
+    multiple of the column tiles per workgroup) and several m-tiles per
+    expert."""
     cfg = workloads.MoEConfig("t", 13, T=T, H=H, E=6, K=2, I=I, hot_experts=2)
     idx, w = oracle.route(workloads.logits(cfg), None, 2)
     hid = workloads.hidden(cfg)
     w13, w2, host_w = stacked_weights(cfg)
     w13p, w2p = ops.moe_pack_ffn_weights(w13, w2)
     G = cfg.E
-    # w2 [G, H, I]: column tile ct = rows 64ct.., fragment f = rows +16f..,
-    # k-step ks, lane l -> row + l%16, cols 32ks + 8(l/16) .. +8
-    got = host_bits(w2p).reshape(G, H // 64, I // 32, 4, 4, 16, 8)     # g ct ks f (l/16) (l%16) 8
-    want = host_bits(w2).reshape(G, H // 64, 4, 16, I // 32, 4, 8).transpose(0, 1, 4, 2, 5, 3, 6)
+    # w2 [G, H, I]: K-step ks, column tile ct = rows 64ct.., fragment f =
+    # rows +16f.., lane l -> row + l%16, cols 32ks + 8(l/16) .. +8
+    got = host_bits(w2p).reshape(G, I // 32, H // 64, 4, 4, 16, 8)     # g ks ct f (l/16) (l%16) 8
+    want = host_bits(w2).reshape(G, H // 64, 4, 16, I // 32, 4, 8).transpose(0, 4, 1, 2, 5, 3, 6)
     np.testing.assert_array_equal(got, want)
     # w13: column tile ct = gate rows 32ct.. (fragments 0, 1) then up rows
-    g13 = host_bits(w13p).reshape(G, I // 32, H // 32, 4, 4, 16, 8)
+    g13 = host_bits(w13p).reshape(G, H // 32, I // 32, 4, 4, 16, 8)
     w13h = host_bits(w13)
-    gate = w13h[:, :I].reshape(G, I // 32, 2, 16, H // 32, 4, 8).transpose(0, 1, 4, 2, 5, 3, 6)
-    up = w13h[:, I:].reshape(G, I // 32, 2, 16, H // 32, 4, 8).transpose(0, 1, 4, 2, 5, 3, 6)
+    gate = w13h[:, :I].reshape(G, I // 32, 2, 16, H // 32, 4, 8).transpose(0, 4, 1, 2, 5, 3, 6)
+    up = w13h[:, I:].reshape(G, I // 32, 2, 16, H // 32, 4, 8).transpose(0, 4, 1, 2, 5, 3, 6)
     np.testing.assert_array_equal(g13[:, :, :, :2], gate)
     np.testing.assert_array_equal(g13[:, :, :, 2:], up)
     # the GEMM on packed weights against the oracle

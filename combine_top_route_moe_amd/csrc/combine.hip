@@ -27,26 +27,41 @@ __global__ void __launch_bounds__(256) combine_kernel(
   const int64_t t = v / vec_per_row;
   const int c = (int)(v - t * vec_per_row);
   const float s = QDQ ? *qdq_scale : 1.0f;
+  const float inv_s = QDQ ? 1.0f / s : 1.0f;
+  const bool rcp_ok = QDQ && rcp_scale_ok(s);
 
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
   const int32_t* ro = row_of + t * K;
-  for (int k = 0; k < K; ++k) {
-    const int32_t r = ro[k];
-    if (r < 0) continue;
-    if (r >= num_rows) {
-      raise_error(dev_error, MOE_DEVERR_ROW_RANGE);
-      continue;
-    }
-    uint4 raw = reinterpret_cast<const uint4*>(rows + (int64_t)r * H)[c];
-    float f[8];
-    unpack8(raw, f);
+  // slots in groups of 8: the group's row gathers are all issued before its
+  // adds, which then run in slot order
+  for (int k0 = 0; k0 < K; k0 += 8) {
+    int32_t r[8];
+    uint4 raw[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float x = f[j];
-      if (QDQ) x = bf16_to_f32(qdq_e4m3(x, s));
-      acc[j] = acc[j] + x;
+      r[j] = k0 + j < K ? ro[k0 + j] : -1;
+      if (r[j] >= num_rows) {
+        raise_error(dev_error, MOE_DEVERR_ROW_RANGE);
+        r[j] = -1;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      raw[j] = r[j] >= 0 ? reinterpret_cast<const uint4*>(rows + (int64_t)r[j] * H)[c]
+                         : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (r[j] < 0) continue;
+      float f[8];
+      unpack8(raw[j], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float x = f[i];
+        if (QDQ) x = bf16_to_f32(qdq_e4m3_rcp(x, s, inv_s, rcp_ok));
+        acc[i] = acc[i] + x;
+      }
     }
   }
   if (shared) {

@@ -1,10 +1,11 @@
 // Device helpers shared by the gfx950 kernels of the MoE hot path.
 //
-// Number formats are implemented from their definitions with integer
-// operations so that every rounding is explicit:
-//   bf16  — the upper 16 bits of an IEEE binary32, rounded to nearest even;
+// Number formats:
+//   bf16  — the upper 16 bits of an IEEE binary32, rounded to nearest even
+//           (integer operations, so the rounding is explicit);
 //   e4m3  — OCP FP8 E4M3FN (bias 7, 3 mantissa bits, max 448, subnormal
-//           step 2^-9), rounded to nearest even; callers clamp to +-448.
+//           step 2^-9), rounded to nearest even by the gfx950 conversion
+//           instructions; callers clamp to +-448 first.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,29 +29,30 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
-// Nearest E4M3FN value (as a float) to v, |v| <= 448, ties to even.
-// Below 2^-6 the grid is uniform with step 2^-9, so scaling by 2^9 (exact)
-// and rounding to an integer (round-half-even) gives the code; above it the
-// 23-bit binary32 mantissa is rounded to 3 bits with the usual carry.
-__device__ __forceinline__ float e4m3_round(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = u & 0x80000000u;
-  uint32_t a = u & 0x7fffffffu;
-  if (a < 0x3c800000u) {  // |v| < 2^-6
-    float r = __builtin_rintf(__uint_as_float(a) * 512.0f) * (1.0f / 512.0f);
-    return __uint_as_float(__float_as_uint(r) | sign);
-  }
-  a += 0x7ffffu + ((a >> 20) & 1u);
-  a &= 0xfff00000u;
-  return __uint_as_float(a | sign);
+// FP8 fake-quant of one value with scale s > 0, given inv_s = 1.0f / s:
+//   bf16( e4m3( clamp(x / s, -448, 448) ) * s )
+// with the IEEE binary32 quotient x / s and product.  The quotient is formed
+// as x * inv_s where that is provably the same after E4M3 rounding: the
+// product lies within 3 ulp of the quotient (two roundings of at most 2^-24
+// relative against the quotient's one), and E4M3 rounding keeps 3 of the 23
+// mantissa bits, so wherever the product's 20 dropped bits are more than 16
+// ulp from the halfway point both round alike.  Elsewhere (near a halfway
+// point, in the E4M3 subnormal range below 2^-6, or when the scale is so
+// small or large that its reciprocal loses precision) the quotient itself is
+// computed.  The rounding to E4M3 is the hardware conversion
+// (v_cvt_pk_fp8_f32, OCP E4M3FN, round to nearest even on gfx950) and back
+// (v_cvt_f32_fp8, exact); the clamp keeps it away from overflow.
+__device__ __forceinline__ bool rcp_scale_ok(float s) {
+  return s >= 0x1p-125f && s <= 0x1p125f;
 }
-
-// Fake-quant of one value with scale s > 0 (IEEE division and product).
-__device__ __forceinline__ uint32_t qdq_e4m3(float x, float s) {
-  float r = x / s;
+__device__ __forceinline__ uint32_t qdq_e4m3_rcp(float x, float s, float inv_s, bool rcp_ok) {
+  float r = x * inv_s;
+  const uint32_t a = __float_as_uint(r) & 0x7fffffffu;
+  const int d = (int)(a & 0xfffffu) - 0x80000;
+  if (!rcp_ok || a < 0x3c800000u || (d > -16 && d < 16)) r = x / s;
   r = fminf(fmaxf(r, -448.0f), 448.0f);
-  float q = e4m3_round(r);
-  return f32_to_bf16(q * s);
+  const int p = __builtin_amdgcn_cvt_pk_fp8_f32(r, r, 0, false);
+  return f32_to_bf16(__builtin_amdgcn_cvt_f32_fp8(p, 0) * s);
 }
 
 __device__ __forceinline__ void raise_error(int32_t* err, int code) {

@@ -73,8 +73,10 @@ __global__ void __launch_bounds__(256) fake_quant_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) h[j] = 0;
     } else {
+      const float inv_s = 1.0f / s;
+      const bool rcp_ok = rcp_scale_ok(s);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) h[j] = qdq_e4m3(f[j], s);
+      for (int j = 0; j < 8; ++j) h[j] = qdq_e4m3_rcp(f[j], s, inv_s, rcp_ok);
     }
     res = pack8(h);
   }

@@ -282,12 +282,49 @@ __device__ __forceinline__ constexpr int vmcnt_imm(int n) {
   return (n & 0xf) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xf << 8);
 }
 
+// Workgroup barrier for the activation ring, without the memory fence that
+// __syncthreads() carries: with direct-to-LDS loads in flight that fence
+// becomes a wait for every outstanding load, weight prefetches included, and
+// drains the weight pipeline at every chunk.  The ordering it would give is
+// established explicitly instead: each wave first waits (vmcnt) until its own
+// DMA for the chunk has landed in LDS, so after the barrier the whole chunk
+// is there; and the slot the next DMA overwrites was last read for MFMAs the
+// waves had already issued, so those LDS reads were complete.  The empty asm
+// statements keep the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The activation DMA (global_load_lds_dwordx4: 64 lanes x 16 bytes from
+// global memory to LDS at M0), issued as inline assembly.  When the
+// compiler's wait-count insertion sees a direct-to-LDS load, it cannot tell
+// which ring slot it writes, so it makes the next LDS read (and any reuse of
+// the load's address registers) wait until no vector-memory operation is
+// outstanding, weight prefetches included, which drains the weight pipeline
+// at every chunk.  It does not model this statement; the DMA of a chunk is
+// waited for explicitly (vmcnt at the chunk barrier), and the compiler's own
+// waits for the weight loads, which do not count these DMAs, are only
+// stricter than needed, never looser.  The LDS reads stay ordinary loads, so
+// their waits and register hazards remain the compiler's; they cannot move
+// across lds_barrier(), whose empty asm statements clobber memory.
+__device__ __forceinline__ void dma16(const uint16_t* g, const u32x4_t* l) {
+  const uint32_t lds =
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) u32x4_t*)l;
+  // one wait state between the SALU write of M0 and the DMA that reads it
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "m0");
+}
+
 template <bool GATE_UP, bool NT, int NW>
 __device__ __forceinline__ void frag_gemm_body(
     u32x4_t (*As)[kStageBlocks][kWave], const u32x4_t* __restrict__ wp, int kstride,
     const uint16_t* const* a_src, int a_chunk_stride, int w, int lane, int nks, int nlive,
     int valid, int ct, bool ct_ok, int64_t row_base, int64_t mt_glob, int Nout,
-    const float* __restrict__ row_scale, uint16_t* __restrict__ Out, int crot) {
+    const float* tile_scale, uint16_t* __restrict__ Out, int crot) {
   constexpr int kDmaPerWave = kStageBlocks / NW;
   // every workgroup walks K from its own starting chunk (crot) and wraps
   // around, so the many weight streams do not all hit the same offsets —
@@ -302,8 +339,8 @@ __device__ __forceinline__ void frag_gemm_body(
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q) {
       if ((w * kDmaPerWave + q) / kChunkSteps >= nlive) break;
-      __builtin_amdgcn_global_load_lds(a_src[q] + (int64_t)wrap(chunk + crot, nch) * a_chunk_stride,
-                                       &As[stage][w * kDmaPerWave + q][0], 16, 0, 0);
+      dma16(a_src[q] + (int64_t)wrap(chunk + crot, nch) * a_chunk_stride,
+            &As[stage][w * kDmaPerWave + q][0]);
     }
     asm volatile("" ::: "memory");
   };
@@ -347,7 +384,7 @@ __device__ __forceinline__ void frag_gemm_body(
         const int chunk = ks / kChunkSteps;
         if (chunk > 0) stage = (stage + 1 == kStages) ? 0 : stage + 1;
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAfterDma));
-        __syncthreads();
+        lds_barrier();
         // the slot two ahead was last read in the previous chunk, which every
         // wave has finished; past the end this reloads a valid chunk so the
         // number of outstanding loads stays the same
@@ -399,7 +436,7 @@ __device__ __forceinline__ void frag_gemm_body(
         }
         (void)orow;
       } else {
-        const float sc = row_scale ? row_scale[orow] : 1.0f;
+        const float sc = tile_scale ? tile_scale[r] : 1.0f;
 #pragma unroll
         for (int f = 0; f < kFrags; ++f) {
           const int col = ct * 64 + f * 16 + (lane & 15);
@@ -468,6 +505,15 @@ __global__ void __launch_bounds__(NW * kWave, 2 * 4 / NW) frag_gemm_kernel(
   }
   const int a_chunk_stride = GATE_UP ? kChunkSteps * 32 : kChunkSteps * kWave * 8;
 
+  // down: the m-tile's row scales, staged in LDS once for the epilogue
+  __shared__ float rs[kBM];
+  const float* tile_scale = nullptr;
+  if (!GATE_UP && row_scale) {
+    for (int r = threadIdx.x; r < valid; r += NW * kWave) rs[r] = row_scale[row_base + r];
+    __syncthreads();
+    tile_scale = rs;
+  }
+
   // an expert whose rows fit in one m-tile reads each weight byte once
   const bool once = nrows <= kBM;
   // K rotation for experts read once, so that the experts in flight do not
@@ -481,10 +527,10 @@ __global__ void __launch_bounds__(NW * kWave, 2 * 4 / NW) frag_gemm_kernel(
   const int crot = once ? (int)((rkey * 2654435761u) >> 8) % (nks / kChunkSteps) : 0;
   if (once)
     frag_gemm_body<GATE_UP, true, NW>(As, wp, kstride, a_src, a_chunk_stride, w, lane, nks, nlive, valid,
-                                      ct, ct_ok, row_base, mt_glob, Nout, row_scale, Out, crot);
+                                      ct, ct_ok, row_base, mt_glob, Nout, tile_scale, Out, crot);
   else
     frag_gemm_body<GATE_UP, false, NW>(As, wp, kstride, a_src, a_chunk_stride, w, lane, nks, nlive, valid,
-                                       ct, ct_ok, row_base, mt_glob, Nout, row_scale, Out, crot);
+                                       ct, ct_ok, row_base, mt_glob, Nout, tile_scale, Out, crot);
 }
 
 // Packing: one thread per 16-byte vector of the source (coalesced reads),

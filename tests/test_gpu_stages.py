@@ -95,6 +95,37 @@ def test_fake_quant_per_tensor_exhaustive(s):
     np.testing.assert_array_equal(host_bits(out), ref)
 
 
+def _near_midpoint_scales(n_pairs=20, spread=3, seed=5):
+    """Scales s for which some bf16 value x0 has x0 / s within a few float32
+    ulps of a halfway point between two E4M3 values (where a quotient
+    computed as x * (1/s) could round the other way)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n_pairs):
+        e, m = int(rng.integers(-5, 8)), int(rng.integers(0, 7))
+        mid = (1.0 + (m + 0.5) / 8.0) * 2.0 ** e
+        x0 = np.float32(bf16_bits_to_f32(f32_to_bf16_bits(np.float32(rng.uniform(1, 100) * 10.0 ** rng.integers(-3, 3)))))
+        s0 = np.float32(np.float64(x0) / mid)
+        q = np.float32(x0) / s0                               # IEEE float32 quotient
+        assert abs(np.float64(q) - mid) <= 4 * np.spacing(np.float32(mid)), (x0, s0, q, mid)
+        for d in range(-spread, spread + 1):
+            out.append(np.array([s0]).view(np.uint32)[0] + np.uint32(d + 2 ** 31) - np.uint32(2 ** 31))
+    return np.array(out, np.uint32).view(np.float32)
+
+
+def test_fake_quant_near_rounding_midpoints():
+    """Per-tensor scales built so that quotients land within a few ulps of
+    E4M3 halfway points, every finite bf16 value each: bit-exact."""
+    rows = _all_finite_bf16_rows(128)
+    xd = dev_bf16(rows)
+    out = torch.empty_like(xd)
+    scale = torch.empty(1, dtype=torch.float32, device="cuda")
+    for s in _near_midpoint_scales():
+        scale.fill_(float(s))
+        ops.moe_fake_quant_rows(xd, out, None, ops.MOE_FQ_PER_TENSOR, scale=scale)
+        np.testing.assert_array_equal(host_bits(out), oracle.fake_quant_per_tensor(rows, s), err_msg=str(s))
+
+
 def test_fake_quant_row_skip_inplace_and_amax():
     rng = np.random.default_rng(1)
     x = f32_to_bf16_bits((rng.standard_normal((37, 256)) * 5).astype(np.float32))

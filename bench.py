@@ -124,7 +124,10 @@ def cpu_baseline(cfg, logits, hidden, row_valid, budget_s: float):
         n = min(cfg.T, n * 4)
         dt = run(n)
     times = [dt]
-    while sum(times) < budget_s / 2 and len(times) < 5:   # repeat the sample, keep the median
+    # repeat the sample (the median is kept) until about half the budget of
+    # CPU work has been done, so that a small batch is still timed over
+    # seconds, not one short run
+    while sum(times) < budget_s / 2 and len(times) < 50:
         times.append(run(n))
     dt = float(np.median(times))
     tv = n if row_valid is None else int(row_valid[:n].sum())

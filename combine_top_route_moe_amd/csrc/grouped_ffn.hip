@@ -16,8 +16,11 @@
 // reduction dimension — which is the layout the MFMA fragments want: a lane
 // reads 8 consecutive bf16 (16 bytes) of one row for both A and B.
 //
-// Tiling: a workgroup of 4 wavefronts owns a BM x BN output tile (BM = BN =
-// 128); wave (wm, wn) owns a 64 x 64 quarter as 4 x 4 MFMA 16x16 tiles.
+// Two kernels.  With weights packed once by moe_pack_ffn_weights (the
+// layer's path), the fragment-streaming kernel further down.  With row-major
+// weights, grouped_gemm_kernel: a workgroup of 4 wavefronts owns a BM x BN
+// output tile (BM = BN = 128); wave (wm, wn) owns a 64 x 64 quarter as 4 x 4
+// MFMA 16x16 tiles.
 // K advances 64 at a time through LDS (rows padded by 16 bytes to spread
 // banks), with the next K-slab prefetched into registers while the MFMAs
 // run on the current one.  For gate/up the 128 B-rows of a tile are 64 gate
@@ -265,7 +268,10 @@ __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
 // waves: they go into LDS by direct-to-LDS DMA (global_load_lds_dwordx4), in
 // the same fragment order so every LDS read is one contiguous, conflict-free
 // 1 KB, through a ring of kStages stages of kChunkSteps K-steps, the DMA
-// running two chunks ahead so that its latency hides behind compute.
+// running kStages-1 chunks ahead so that its latency hides behind compute.
+// Neither the DMA nor the chunk barrier may wait for the weight prefetches
+// (lds_barrier and dma16 below say how), or the weight pipeline would drain
+// at every chunk.
 constexpr int kPrefetch = 4;     // weight K-steps in flight per wave
 constexpr int kChunkSteps = 2;   // activation K-steps per LDS stage
 constexpr int kStages = 3;       // activation LDS ring: DMA runs kStages-1 chunks ahead
@@ -357,8 +363,8 @@ __device__ __forceinline__ void frag_gemm_body(
     for (int f = 0; f < kFrags; ++f) acc[i][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nchunks = nks / kChunkSteps;
-  issue_chunk(0, 0);
-  issue_chunk(min(1, nchunks - 1), 1);
+#pragma unroll
+  for (int c = 0; c < kStages - 1; ++c) issue_chunk(min(c, nchunks - 1), c);
   u32x4_t bq[kPrefetch][kFrags];
 #pragma unroll
   for (int s = 0; s < kPrefetch; ++s)
@@ -369,12 +375,13 @@ __device__ __forceinline__ void frag_gemm_body(
   // Loads complete in issue order, so waiting until at most n are
   // outstanding, with n no larger than the number issued after the chunk's
   // DMA, guarantees that DMA has landed.  After the DMA of chunk c (issued
-  // at the start of chunk c-2) come at least the weight loads of two chunks
-  // (the DMA of chunk c+1 may be empty for this wave); the prologue issues
-  // more than that.
+  // at the start of chunk c - (kStages-1)) come at least the weight loads of
+  // kStages-1 chunks (the later DMAs may be empty for this wave); the
+  // prologue issues at least as many.
   constexpr int kAfterDma = (kStages - 1) * kChunkSteps * kFrags;
   static_assert(kAfterDma <= kPrefetch * kFrags, "prologue count");
-  // nks is a multiple of 4 = kPrefetch (K is a multiple of 128)
+  static_assert(kPrefetch % kChunkSteps == 0, "chunk boundaries fall on prefetch slots");
+  // nks is a multiple of kPrefetch = 4 (K is a multiple of 128)
   int stage = 0;  // ring slot of the current chunk
   for (int ks0 = 0; ks0 < nks; ks0 += kPrefetch) {
 #pragma unroll
@@ -385,11 +392,11 @@ __device__ __forceinline__ void frag_gemm_body(
         if (chunk > 0) stage = (stage + 1 == kStages) ? 0 : stage + 1;
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAfterDma));
         lds_barrier();
-        // the slot two ahead was last read in the previous chunk, which every
-        // wave has finished; past the end this reloads a valid chunk so the
-        // number of outstanding loads stays the same
-        const int ahead = (stage + 2) % kStages;
-        issue_chunk(min(chunk + 2, nchunks - 1), ahead);
+        // the slot kStages-1 ahead was last read in the previous chunk, which
+        // every wave has finished; past the end this reloads a valid chunk so
+        // the number of outstanding loads stays the same
+        const int ahead = (stage + kStages - 1) % kStages;
+        issue_chunk(min(chunk + kStages - 1, nchunks - 1), ahead);
       }
       const int sub = ks % kChunkSteps;
 #pragma unroll

@@ -56,12 +56,13 @@ __global__ void __launch_bounds__(256) combine_kernel(
       if (r[j] < 0) continue;
       float f[8];
       unpack8(raw[j], f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float x = f[i];
-        if (QDQ) x = bf16_to_f32(qdq_e4m3_rcp(x, s, inv_s, rcp_ok));
-        acc[i] = acc[i] + x;
+      if (QDQ) {
+        uint32_t w[4];
+        qdq8_rcp(f, s, inv_s, rcp_ok, w);
+        unpack8(make_uint4(w[0], w[1], w[2], w[3]), f);
       }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = acc[i] + f[i];
     }
   }
   if (shared) {

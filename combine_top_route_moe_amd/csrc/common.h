@@ -2,7 +2,7 @@
 //
 // Number formats:
 //   bf16  — the upper 16 bits of an IEEE binary32, rounded to nearest even
-//           (integer operations, so the rounding is explicit);
+//           (the gfx950 conversion instruction);
 //   e4m3  — OCP FP8 E4M3FN (bias 7, 3 mantissa bits, max 448, subnormal
 //           step 2^-9), rounded to nearest even by the gfx950 conversion
 //           instructions; callers clamp to +-448 first.
@@ -21,15 +21,16 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
 }
 
-// binary32 -> bf16 bits, round to nearest, ties to even.  NaN -> quiet NaN.
+// binary32 -> bf16 bits, round to nearest, ties to even; NaN -> a quiet NaN.
+// The conversion is the gfx950 instruction (v_cvt_pk_bf16_f32), which was
+// checked on the GPU against the integer form (add 0x7fff plus the kept
+// lsb, keep the upper half) over all 2^32 binary32 patterns: identical for
+// every non-NaN input, denormals included.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-// FP8 fake-quant of one value with scale s > 0, given inv_s = 1.0f / s:
+// FP8 fake-quant with scale s > 0, given inv_s = 1.0f / s:
 //   bf16( e4m3( clamp(x / s, -448, 448) ) * s )
 // with the IEEE binary32 quotient x / s and product.  The quotient is formed
 // as x * inv_s where that is provably the same after E4M3 rounding: the
@@ -45,14 +46,39 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 __device__ __forceinline__ bool rcp_scale_ok(float s) {
   return s >= 0x1p-125f && s <= 0x1p125f;
 }
-__device__ __forceinline__ uint32_t qdq_e4m3_rcp(float x, float s, float inv_s, bool rcp_ok) {
-  float r = x * inv_s;
+// true where x * inv_s may round differently from x / s: within 16 ulp of
+// an E4M3 halfway point, or below 2^-6 (the E4M3 subnormal range)
+__device__ __forceinline__ bool qdq_needs_quotient(float r) {
   const uint32_t a = __float_as_uint(r) & 0x7fffffffu;
-  const int d = (int)(a & 0xfffffu) - 0x80000;
-  if (!rcp_ok || a < 0x3c800000u || (d > -16 && d < 16)) r = x / s;
-  r = fminf(fmaxf(r, -448.0f), 448.0f);
-  const int p = __builtin_amdgcn_cvt_pk_fp8_f32(r, r, 0, false);
-  return f32_to_bf16(__builtin_amdgcn_cvt_f32_fp8(p, 0) * s);
+  return a < 0x3c800000u || (uint32_t)((int)(a & 0xfffffu) - 0x80000 + 16) < 33u;
+}
+// 8 values at once; out[j] holds the bf16 results of values 2j and 2j+1
+// (low half first).  The exact quotients are computed only for the lanes and
+// values that need them.
+__device__ __forceinline__ void qdq8_rcp(const float* x, float s, float inv_s, bool rcp_ok,
+                                         uint32_t* out) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  float r[8];
+  bool slow = !rcp_ok;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    r[j] = x[j] * inv_s;
+    slow |= qdq_needs_quotient(r[j]);
+  }
+  if (slow) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (!rcp_ok || qdq_needs_quotient(r[j])) r[j] = x[j] / s;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const float r0 = fminf(fmaxf(r[j], -448.0f), 448.0f);
+    const float r1 = fminf(fmaxf(r[j + 1], -448.0f), 448.0f);
+    const int p = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+    const f32x2_t q = {__builtin_amdgcn_cvt_f32_fp8(p, 0) * s, __builtin_amdgcn_cvt_f32_fp8(p, 1) * s};
+    out[j / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(q, bf16x2_t));
+  }
 }
 
 __device__ __forceinline__ void raise_error(int32_t* err, int code) {

@@ -68,17 +68,13 @@ __global__ void __launch_bounds__(256) fake_quant_kernel(
     if (out == in) return;
     res = raw;
   } else {
-    uint32_t h[8];
     if (s == 0.0f) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) h[j] = 0;
+      res = make_uint4(0, 0, 0, 0);
     } else {
-      const float inv_s = 1.0f / s;
-      const bool rcp_ok = rcp_scale_ok(s);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) h[j] = qdq_e4m3_rcp(f[j], s, inv_s, rcp_ok);
+      uint32_t w[4];
+      qdq8_rcp(f, s, 1.0f / s, rcp_scale_ok(s), w);
+      res = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    res = pack8(h);
   }
   reinterpret_cast<uint4*>(out)[v] = res;
 }

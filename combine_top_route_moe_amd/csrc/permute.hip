@@ -15,7 +15,8 @@
 //      plus the wave's running count of that expert (in LDS) plus the
 //      counts of the earlier waves.  Writes rank[i] and the chunk's
 //      per-expert totals.
-//   2. scan: one workgroup turns the chunk totals into per-expert counts,
+//   2. scan: one workgroup (each expert's chunk column split over
+//      1024 / El threads) turns the chunk totals into per-expert counts,
 //      segment sizes (optionally next_pow2), cu_seqlens, and the absolute
 //      first row of every (chunk, expert) pair; it also marks pow2 padding
 //      rows (src_of = -1, w_perm = 0) and checks the capacity.
@@ -89,19 +90,34 @@ __device__ __forceinline__ int next_pow2_dev(int n) {
   return 1 << (32 - __clz(n - 1));
 }
 
+// One workgroup of 1024 threads.  Each expert's column of chunk counts is
+// split into P = 1024 / El contiguous blocks of chunks, one thread each
+// (thread p*El + e: reads stay coalesced across experts), so no thread walks
+// more than ceil(nchunks / P) chunks; the partial sums meet in LDS.
 __global__ void __launch_bounds__(1024) permute_scan_kernel(
     int32_t* __restrict__ table, int nchunks, int El, int pad_pow2, int64_t capacity,
     int32_t* __restrict__ counts, int32_t* __restrict__ cu_seqlens, int32_t* __restrict__ src_of,
     float* __restrict__ w_perm, int32_t* __restrict__ dev_error) {
+  __shared__ int32_t part[1024];   // [P][El] partial sums
+  __shared__ int32_t s_start[1024], s_total[1024], s_size[1024];
   __shared__ int32_t s_wave[16];
   const int tid = threadIdx.x;
-  const int e = tid;
-  int total = 0;
-  if (e < El) {
-    for (int c = 0; c < nchunks; ++c) total += table[(int64_t)c * El + e];
+  const int P = max(1, 1024 / El);
+  const bool act = tid < P * El;
+  const int e = act ? tid % El : 0, p = act ? tid / El : 0;
+  const int L = (nchunks + P - 1) / P;
+  const int c0 = min(p * L, nchunks), c1 = min(c0 + L, nchunks);
+  if (act) {
+    int sum = 0;
+    for (int c = c0; c < c1; ++c) sum += table[(int64_t)c * El + e];
+    part[tid] = sum;
   }
-  const int size = (e < El) ? (pad_pow2 ? next_pow2_dev(total) : total) : 0;
-  // block-wide inclusive scan of size over 1024 threads
+  __syncthreads();
+  int total = 0;
+  if (tid < El)
+    for (int q = 0; q < P; ++q) total += part[q * El + tid];
+  const int size = (tid < El) ? (pad_pow2 ? next_pow2_dev(total) : total) : 0;
+  // block-wide inclusive scan of size over 1024 threads (thread = expert)
   const int lane = tid & 63, wid = tid >> 6;
   int x = size;
 #pragma unroll
@@ -122,22 +138,32 @@ __global__ void __launch_bounds__(1024) permute_scan_kernel(
   }
   __syncthreads();
   const int incl = x + (wid > 0 ? s_wave[wid - 1] : 0);
-  const int start = incl - size;
-  if (e < El) {
-    counts[e] = total;
-    cu_seqlens[e] = start;
-    if (e == El - 1) {
+  if (tid < El) {
+    const int start = incl - size;
+    s_start[tid] = start;
+    s_total[tid] = total;
+    s_size[tid] = size;
+    counts[tid] = total;
+    cu_seqlens[tid] = start;
+    if (tid == El - 1) {
       cu_seqlens[El] = incl;
       if ((int64_t)incl > capacity) raise_error(dev_error, MOE_DEVERR_CAPACITY);
     }
-    int running = start;
-    for (int c = 0; c < nchunks; ++c) {
+  }
+  __syncthreads();
+  if (act) {
+    // absolute first row of every (chunk, expert) pair in this thread's block
+    int running = s_start[e];
+    for (int q = 0; q < p; ++q) running += part[q * El + e];
+    for (int c = c0; c < c1; ++c) {
       const int64_t k = (int64_t)c * El + e;
       const int cnt = table[k];
       table[k] = running;
       running += cnt;
     }
-    for (int r = start + total; r < start + size && (int64_t)r < capacity; ++r) {
+    // pow2 padding rows of expert e, shared among its P threads
+    const int pad0 = s_start[e] + s_total[e], pad1 = s_start[e] + s_size[e];
+    for (int r = pad0 + p; r < pad1 && (int64_t)r < capacity; r += P) {
       src_of[r] = -1;
       w_perm[r] = 0.0f;
     }

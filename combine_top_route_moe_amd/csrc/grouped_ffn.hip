@@ -315,20 +315,23 @@ __device__ __forceinline__ void lds_barrier() {
 // stricter than needed, never looser.  The LDS reads stay ordinary loads, so
 // their waits and register hazards remain the compiler's; they cannot move
 // across lds_barrier(), whose empty asm statements clobber memory.
-__device__ __forceinline__ void dma16(const uint16_t* g, const u32x4_t* l) {
+// The source address is a wave-uniform base (SGPRs) plus a 32-bit per-lane
+// byte offset, which keeps the per-lane state of the DMA small.
+__device__ __forceinline__ void dma16(const uint16_t* sbase, uint32_t voff, const u32x4_t* l) {
   const uint32_t lds =
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) u32x4_t*)l;
   // one wait state between the SALU write of M0 and the DMA that reads it
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "m0");
 }
 
 template <bool GATE_UP, bool NT, int NW>
 __device__ __forceinline__ void frag_gemm_body(
     u32x4_t (*As)[kStageBlocks][kWave], const u32x4_t* __restrict__ wp, int kstride,
-    const uint16_t* const* a_src, int a_chunk_stride, int w, int lane, int nks, int nlive,
+    const uint16_t* a_base, const int64_t* a_uoff, const uint32_t* a_voff, int a_chunk_stride,
+    int w, int lane, int nks, int nlive,
     int valid, int ct, bool ct_ok, int64_t row_base, int64_t mt_glob, int Nout,
     const float* tile_scale, uint16_t* __restrict__ Out, int crot) {
   constexpr int kDmaPerWave = kStageBlocks / NW;
@@ -345,7 +348,7 @@ __device__ __forceinline__ void frag_gemm_body(
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q) {
       if ((w * kDmaPerWave + q) / kChunkSteps >= nlive) break;
-      dma16(a_src[q] + (int64_t)wrap(chunk + crot, nch) * a_chunk_stride,
+      dma16(a_base + a_uoff[q] + (int64_t)wrap(chunk + crot, nch) * a_chunk_stride, a_voff[q],
             &As[stage][w * kDmaPerWave + q][0]);
     }
     asm volatile("" ::: "memory");
@@ -399,10 +402,20 @@ __device__ __forceinline__ void frag_gemm_body(
         issue_chunk(min(chunk + kStages - 1, nchunks - 1), ahead);
       }
       const int sub = ks % kChunkSteps;
+      // all of the step's activation fragments are read before the MFMAs
+      // (in two halves, so a segment of at most 64 rows reads only the
+      // first): one LDS latency per step instead of one per m-subtile
+      u32x4_t a[kMsub];
+#pragma unroll
+      for (int i = 0; i < kMsub / 2; ++i) a[i] = As[stage][i * kChunkSteps + sub][lane];
+      if (nlive > kMsub / 2) {
+#pragma unroll
+        for (int i = kMsub / 2; i < kMsub; ++i) a[i] = As[stage][i * kChunkSteps + sub][lane];
+      }
 #pragma unroll
       for (int i = 0; i < kMsub; ++i) {
         if (i >= nlive) break;
-        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, As[stage][i * kChunkSteps + sub][lane]);
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, a[i]);
 #pragma unroll
         for (int f = 0; f < kFrags; ++f)
           acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -454,8 +467,10 @@ __device__ __forceinline__ void frag_gemm_body(
   }
 }
 
+// Two waves per SIMD: an 8-wave workgroup needs them, a 4-wave one gets two
+// workgroups per CU; the register budget is 256 per lane either way.
 template <bool GATE_UP, int NW>
-__global__ void __launch_bounds__(NW * kWave, 2 * 4 / NW) frag_gemm_kernel(
+__global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Wf,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ counts, int G,
     int Kdim, int Nw /* weight rows per group */, int Nout, const float* __restrict__ row_scale,
@@ -467,6 +482,11 @@ __global__ void __launch_bounds__(NW * kWave, 2 * 4 / NW) frag_gemm_kernel(
   const int pid = xcd_remap(blockIdx.x);
   int g, mt, cb, mt_base;
   if (!decode_tile(pid, counts, G, n_cb, g, mt, cb, &mt_base)) return;
+  // the same in every lane: say so, so that addresses built from them stay scalar
+  g = __builtin_amdgcn_readfirstlane(g);
+  mt = __builtin_amdgcn_readfirstlane(mt);
+  cb = __builtin_amdgcn_readfirstlane(cb);
+  mt_base = __builtin_amdgcn_readfirstlane(mt_base);
   const int seg0 = cu_seqlens[g];
   const int nrows = counts[g];
   if ((int64_t)seg0 + nrows > capacity || seg0 < 0) {
@@ -496,18 +516,25 @@ __global__ void __launch_bounds__(NW * kWave, 2 * 4 / NW) frag_gemm_kernel(
   // stage; block b is m-subtile b / kChunkSteps, K-step b % kChunkSteps
   constexpr int kDmaPerWave = kStageBlocks / NW;
   // gate/up reads the permuted rows (row-major); down reads the gate/up
-  // output, which that kernel wrote in fragment order per m-tile
-  const uint16_t* a_src[kDmaPerWave];
+  // output, which that kernel wrote in fragment order per m-tile.  Source of
+  // block q: a_base + a_uoff[q] (+ the chunk's offset) in elements, uniform,
+  // plus a_voff[q] bytes per lane
   const int64_t mt_glob = (int64_t)mt_base + mt;
+  const uint16_t* a_base =
+      GATE_UP ? A + row_base * Kdim : A + mt_glob * kMsub * (int64_t)nks * (kWave * 8);
+  int64_t a_uoff[kDmaPerWave];
+  uint32_t a_voff[kDmaPerWave];
 #pragma unroll
   for (int q = 0; q < kDmaPerWave; ++q) {
     const int b = w * kDmaPerWave + q;
     const int ms = b / kChunkSteps, sub = b % kChunkSteps;
     if (GATE_UP) {
-      const int r = min(ms * 16 + (lane & 15), valid - 1);
-      a_src[q] = A + (row_base + r) * Kdim + sub * 32 + 8 * (lane >> 4);
+      const int r = min(ms * 16 + (lane & 15), valid - 1);   // rows past the end re-read the last
+      a_uoff[q] = 0;
+      a_voff[q] = (uint32_t)(r * Kdim + sub * 32 + 8 * (lane >> 4)) * 2u;
     } else {
-      a_src[q] = A + ((mt_glob * kMsub + ms) * (int64_t)nks + sub) * (kWave * 8) + lane * 8;
+      a_uoff[q] = ((int64_t)ms * nks + sub) * (kWave * 8);
+      a_voff[q] = (uint32_t)lane * 16u;
     }
   }
   const int a_chunk_stride = GATE_UP ? kChunkSteps * 32 : kChunkSteps * kWave * 8;
@@ -533,10 +560,10 @@ __global__ void __launch_bounds__(NW * kWave, 2 * 4 / NW) frag_gemm_kernel(
   const uint32_t rkey = NW == 8 ? (uint32_t)g * 977u : (uint32_t)g * 977u + (uint32_t)cb;
   const int crot = once ? (int)((rkey * 2654435761u) >> 8) % (nks / kChunkSteps) : 0;
   if (once)
-    frag_gemm_body<GATE_UP, true, NW>(As, wp, kstride, a_src, a_chunk_stride, w, lane, nks, nlive, valid,
+    frag_gemm_body<GATE_UP, true, NW>(As, wp, kstride, a_base, a_uoff, a_voff, a_chunk_stride, w, lane, nks, nlive, valid,
                                       ct, ct_ok, row_base, mt_glob, Nout, tile_scale, Out, crot);
   else
-    frag_gemm_body<GATE_UP, false, NW>(As, wp, kstride, a_src, a_chunk_stride, w, lane, nks, nlive, valid,
+    frag_gemm_body<GATE_UP, false, NW>(As, wp, kstride, a_base, a_uoff, a_voff, a_chunk_stride, w, lane, nks, nlive, valid,
                                        ct, ct_ok, row_base, mt_glob, Nout, tile_scale, Out, crot);
 }
 

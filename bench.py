@@ -350,7 +350,9 @@ def main():
         "timing": {"value": ("HIP-graph replay of the whole layer" if graph is not None
                              else "eager launches of the whole layer"),
                    "stages": "eager steps queued behind a GPU spin kernel, HIP events between "
-                             "stages on the launch stream, median over steps"},
+                             "stages on the launch stream, median over steps; stages run "
+                             "one after another (the layer itself runs the shared expert "
+                             "concurrently with the routed path)"},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -59,6 +59,10 @@ class MoELayer:
         self.combine_scale = torch.zeros(1, **f32) if combine_qdq else None
         self.amax = torch.zeros(1, **f32)
         if shared_I:
+            # the shared expert depends only on `hidden`: forward() runs it on
+            # a side stream, concurrently with the routed path (default
+            # priority), and joins it before the combine
+            self.side = torch.cuda.Stream(device=dev)
             self.shared_out = torch.empty(T, H, **bf)
             self.shared_cu = torch.tensor([0, T], **i32)
             self.shared_counts = torch.tensor([T], **i32)
@@ -91,10 +95,15 @@ class MoELayer:
 
     # ------------------------------------------------------------------ stages
     def stages(self, logits: torch.Tensor, hidden: torch.Tensor,
-               row_valid: Optional[torch.Tensor] = None) -> List[Tuple[str, Callable[[], None]]]:
+               row_valid: Optional[torch.Tensor] = None,
+               overlap_shared: bool = False) -> List[Tuple[str, Callable[[], None]]]:
         """The layer as an ordered list of ``(name, enqueue)`` stages.  Each
         enqueue only launches kernels on the current stream; running a stage
-        again with the same inputs rewrites the same outputs."""
+        again with the same inputs rewrites the same outputs.  With
+        ``overlap_shared`` the shared expert is the first stage instead and
+        runs on the side stream, which the current stream waits for before
+        the combine (the form ``forward`` uses; a graph capture of it holds
+        the two branches)."""
         p = self.perm
         layout = ops.MOE_FFN_PACKED_WEIGHTS if self.packed else 0
         x = self.hidden_q if self.dispatch_block else hidden
@@ -113,10 +122,21 @@ class MoELayer:
             p.x_perm, p.cu_seqlens, p.counts, self.w13, self.w2, p.w_perm, self.y_perm,
             ops.MOE_FFN_DOWN | layout, self.ffn_ws, self.dev_error)))
         if self.shared_I:
-            st.append(("shared_ffn", lambda: ops.moe_grouped_ffn(
-                hidden, self.shared_cu, self.shared_counts, self.shared_w13, self.shared_w2,
-                None, self.shared_out, ops.MOE_FFN_ALL | layout, self.shared_ws,
-                self.dev_error)))
+            def shared(stream=None):
+                ops.moe_grouped_ffn(hidden, self.shared_cu, self.shared_counts, self.shared_w13,
+                                    self.shared_w2, None, self.shared_out,
+                                    ops.MOE_FFN_ALL | layout, self.shared_ws, self.dev_error,
+                                    stream=stream)
+
+            if overlap_shared:
+                def fork():
+                    self.side.wait_stream(torch.cuda.current_stream())
+                    shared(self.side)
+
+                st.insert(0, ("shared_ffn", fork))
+                st.append(("join_shared", lambda: torch.cuda.current_stream().wait_stream(self.side)))
+            else:
+                st.append(("shared_ffn", shared))
         st.append(("combine", lambda: ops.moe_combine(
             self.y_perm, p.row_of, self.T, self.K, self.shared_out,
             self.combine_scale if self.combine_qdq else None, self.out, self.dev_error)))
@@ -124,8 +144,9 @@ class MoELayer:
 
     def forward(self, logits: torch.Tensor, hidden: torch.Tensor,
                 row_valid: Optional[torch.Tensor] = None) -> torch.Tensor:
-        """Run the whole layer (enqueue only; no sync, no allocation)."""
-        for _, enqueue in self.stages(logits, hidden, row_valid):
+        """Run the whole layer (enqueue only; no sync, no allocation), the
+        shared expert concurrently with the routed path."""
+        for _, enqueue in self.stages(logits, hidden, row_valid, overlap_shared=True):
             enqueue()
         return self.out
 

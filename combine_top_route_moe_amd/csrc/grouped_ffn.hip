@@ -635,9 +635,14 @@ int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32
     return (m_tiles * n_tiles + grid_unit - 1) / grid_unit * grid_unit;
   };
   if (capacity == 0) return MOE_OK;
-  // long segments (mean >= one m-tile) share each activation tile across 8
-  // column tiles; short ones use 4-wave workgroups
-  const bool wide = capacity >= (int64_t)G * kBM;
+  // Workgroup width (measured): gate/up uses 8 waves once the mean segment
+  // fills an m-tile (each activation tile then serves 8 column tiles), else
+  // 4 (smaller workgroups balance uneven segments).  The down projection
+  // uses 8 only for means between one and two m-tiles; with many m-tiles per
+  // expert the smaller workgroups balance better there.
+  const int64_t mean_x = capacity / G;  // mean rows per group, rounded down
+  const bool wide = mean_x >= kBM;
+  const bool wide_down = wide && mean_x < 2 * kBM;
   if (flags & MOE_FFN_GATE_UP) {
     if (packed) {
       const int nw = wide ? 8 : 4;
@@ -661,10 +666,10 @@ int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32
   }
   if (flags & MOE_FFN_DOWN) {
     if (packed) {
-      const int nw = wide ? 8 : 4;
+      const int nw = wide_down ? 8 : 4;
       const int64_t blocks = grid_for((H / 64 + nw - 1) / nw);
       if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-      if (wide)
+      if (wide_down)
         hipLaunchKernelGGL((frag_gemm_kernel<false, 8>), dim3((unsigned)blocks), dim3(8 * kWave),
                            0, stream, act, w2, cu_seqlens, counts, G, I, H, H, row_scale, y,
                            capacity, dev_error);

@@ -31,6 +31,8 @@ SIGNATURES = {
     "moe_scale_from_amax": (_c_int, [_vp, _vp, _vp]),
     "moe_combine": (_c_int, [_vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp,
                              _vp]),
+    "moe_combine_check": (_c_int, [_vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp,
+                                   _vp]),
     "moe_copy_bytes": (_c_int, [_vp, _vp, _c_size, _vp]),
 }
 

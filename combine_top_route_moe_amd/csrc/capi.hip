@@ -13,6 +13,8 @@ int launch_fake_quant(const uint16_t*, uint16_t*, int64_t, int, const int32_t*, 
 int launch_scale_from_amax(const float*, float*, hipStream_t);
 int launch_combine(const uint16_t*, int64_t, const int32_t*, const uint16_t*, int, int, int,
                    const float*, uint16_t*, int32_t*, hipStream_t);
+int launch_combine_check(const uint16_t*, int64_t, const int32_t*, const uint16_t*, int, int, int,
+                         const uint16_t*, int32_t*, int32_t*, hipStream_t);
 size_t permute_workspace_bytes(int64_t, int);
 int launch_permute(const int32_t*, const float*, const uint16_t*, int, int, int, int, int, int,
                    int64_t, int32_t*, int32_t*, uint16_t*, int32_t*, int32_t*, float*, void*,
@@ -180,6 +182,19 @@ int moe_combine(const uint16_t* rows, int64_t num_rows, const int32_t* row_of,
     return MOE_ERR_INVALID_ARG;
   return launch_combine(rows, num_rows, row_of, shared, T, K, H, row_qdq_scale, out, dev_error,
                         as_stream(stream));
+}
+
+int moe_combine_check(const uint16_t* rows, int64_t num_rows, const int32_t* row_of,
+                      const uint16_t* shared, int T, int K, int H, const uint16_t* kernel_out,
+                      int32_t* state, int32_t* dev_error, void* stream) {
+  if (T < 0 || K < 1 || H < 1 || num_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (H % 128) return MOE_ERR_UNSUPPORTED;
+  if (T > 0 && (!row_of || !kernel_out || (num_rows > 0 && !rows))) return MOE_ERR_INVALID_ARG;
+  if ((rows && !aligned16(rows)) || (kernel_out && !aligned16(kernel_out)) ||
+      (shared && !aligned16(shared)))
+    return MOE_ERR_INVALID_ARG;
+  return launch_combine_check(rows, num_rows, row_of, shared, T, K, H, kernel_out, state,
+                              dev_error, as_stream(stream));
 }
 
 int moe_copy_bytes(const void* src, void* dst, size_t bytes, void* stream) {

@@ -15,25 +15,18 @@
 
 namespace moe {
 
+// The ordered sum for one 16-byte vector (channels 8c .. 8c+7) of token t,
+// rounded once to bf16.  Returns whether the token has a valid routed slot.
 template <bool QDQ>
-__global__ void __launch_bounds__(256) combine_kernel(
-    const uint16_t* __restrict__ rows, int64_t num_rows, const int32_t* __restrict__ row_of,
-    const uint16_t* __restrict__ shared, int T, int K, int H,
-    const float* __restrict__ qdq_scale, uint16_t* __restrict__ out,
-    int32_t* __restrict__ dev_error) {
-  const int vec_per_row = H / 8;
-  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (v >= (int64_t)T * vec_per_row) return;
-  const int64_t t = v / vec_per_row;
-  const int c = (int)(v - t * vec_per_row);
-  const float s = QDQ ? *qdq_scale : 1.0f;
-  const float inv_s = QDQ ? 1.0f / s : 1.0f;
-  const bool rcp_ok = QDQ && rcp_scale_ok(s);
-
+__device__ __forceinline__ bool combine_vec(const uint16_t* __restrict__ rows, int64_t num_rows,
+                                            const int32_t* __restrict__ ro,
+                                            const uint16_t* __restrict__ shared, int K, int H,
+                                            int64_t t, int c, float s, float inv_s, bool rcp_ok,
+                                            int32_t* __restrict__ dev_error, uint4& out) {
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-  const int32_t* ro = row_of + t * K;
+  bool routed = false;
   // slots in groups of 8: the group's row gathers are all issued before its
   // adds, which then run in slot order
   for (int k0 = 0; k0 < K; k0 += 8) {
@@ -54,6 +47,7 @@ __global__ void __launch_bounds__(256) combine_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (r[j] < 0) continue;
+      routed = true;
       float f[8];
       unpack8(raw[j], f);
       if (QDQ) {
@@ -75,7 +69,77 @@ __global__ void __launch_bounds__(256) combine_kernel(
   uint32_t h[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) h[j] = f32_to_bf16(acc[j]);
-  reinterpret_cast<uint4*>(out + t * H)[c] = pack8(h);
+  out = pack8(h);
+  return routed;
+}
+
+template <bool QDQ>
+__global__ void __launch_bounds__(256) combine_kernel(
+    const uint16_t* __restrict__ rows, int64_t num_rows, const int32_t* __restrict__ row_of,
+    const uint16_t* __restrict__ shared, int T, int K, int H,
+    const float* __restrict__ qdq_scale, uint16_t* __restrict__ out,
+    int32_t* __restrict__ dev_error) {
+  const int vec_per_row = H / 8;
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= (int64_t)T * vec_per_row) return;
+  const int64_t t = v / vec_per_row;
+  const int c = (int)(v - t * vec_per_row);
+  const float s = QDQ ? *qdq_scale : 1.0f;
+  const float inv_s = QDQ ? 1.0f / s : 1.0f;
+  const bool rcp_ok = QDQ && rcp_scale_ok(s);
+  uint4 o;
+  combine_vec<QDQ>(rows, num_rows, row_of + t * K, shared, K, H, t, c, s, inv_s, rcp_ok,
+                   dev_error, o);
+  reinterpret_cast<uint4*>(out + t * H)[c] = o;
+}
+
+// Layout check: the same sum without QDQ, compared bit for bit with the
+// output a fused kernel produced.  `state` bits: 1 = checked (the call
+// returns at once), 2 = this call saw a routed slot, 4 = this call saw a
+// mismatch; combine_check_finish_kernel folds them into 0 or 1.
+__global__ void __launch_bounds__(256) combine_check_kernel(
+    const uint16_t* __restrict__ rows, int64_t num_rows, const int32_t* __restrict__ row_of,
+    const uint16_t* __restrict__ shared, int T, int K, int H,
+    const uint16_t* __restrict__ kernel_out, int32_t* state, int32_t* __restrict__ dev_error) {
+  if (state && *state == 1) return;
+  const int vec_per_row = H / 8;
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  bool routed = false, bad = false;
+  if (v < (int64_t)T * vec_per_row) {
+    const int64_t t = v / vec_per_row;
+    const int c = (int)(v - t * vec_per_row);
+    uint4 o;
+    routed = combine_vec<false>(rows, num_rows, row_of + t * K, shared, K, H, t, c, 1.0f, 1.0f,
+                                false, dev_error, o);
+    const uint4 k = reinterpret_cast<const uint4*>(kernel_out + t * H)[c];
+    bad = o.x != k.x || o.y != k.y || o.z != k.z || o.w != k.w;
+    if (bad) raise_error(dev_error, MOE_DEVERR_LAYOUT);
+  }
+  if (state) {
+    const uint64_t any_routed = __ballot(routed), any_bad = __ballot(bad);
+    if ((threadIdx.x & 63) == 0 && (any_routed || any_bad))
+      atomicOr(state, (any_routed ? 2 : 0) | (any_bad ? 4 : 0));
+  }
+}
+
+__global__ void combine_check_finish_kernel(int32_t* state) {
+  if (threadIdx.x != 0) return;
+  const int32_t s = *state;
+  if (s == 1) return;
+  *state = ((s & 2) && !(s & 4)) ? 1 : 0;
+}
+
+int launch_combine_check(const uint16_t* rows, int64_t num_rows, const int32_t* row_of,
+                         const uint16_t* shared, int T, int K, int H, const uint16_t* kernel_out,
+                         int32_t* state, int32_t* dev_error, hipStream_t stream) {
+  const int64_t nvec = (int64_t)T * (H / 8);
+  if (nvec > 0)
+    hipLaunchKernelGGL(combine_check_kernel, dim3((unsigned)((nvec + 255) / 256)), dim3(256), 0,
+                       stream, rows, num_rows, row_of, shared, T, K, H, kernel_out, state,
+                       dev_error);
+  if (state)
+    hipLaunchKernelGGL(combine_check_finish_kernel, dim3(1), dim3(64), 0, stream, state);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 int launch_combine(const uint16_t* rows, int64_t num_rows, const int32_t* row_of,

@@ -19,7 +19,7 @@ MOE_ROUTE_RENORM = 1
 MOE_PERMUTE_PAD_POW2 = 1
 MOE_FFN_GATE_UP, MOE_FFN_DOWN, MOE_FFN_ALL, MOE_FFN_PACKED_WEIGHTS = 1, 2, 3, 4
 MOE_FQ_PER_TENSOR, MOE_FQ_BLOCK = 0, 1
-MOE_DEVERR_ROW_RANGE, MOE_DEVERR_CAPACITY = 1, 2
+MOE_DEVERR_ROW_RANGE, MOE_DEVERR_CAPACITY, MOE_DEVERR_LAYOUT = 1, 2, 3
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -214,6 +214,25 @@ def moe_combine(rows: torch.Tensor, row_of: torch.Tensor, T: int, K: int,
         _ptr(rows), num_rows, _ptr(row_of), _ptr(shared), T, K, H, _ptr(qdq_scale), _ptr(out),
         _ptr(dev_error), _stream(stream)))
     return out
+
+
+def moe_combine_check(rows: torch.Tensor, row_of: torch.Tensor, T: int, K: int,
+                      kernel_out: torch.Tensor, shared: Optional[torch.Tensor] = None,
+                      state: Optional[torch.Tensor] = None,
+                      dev_error: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Check that ``rows`` re-summed in the combine order reproduce
+    ``kernel_out`` bit for bit (MOE_DEVERR_LAYOUT into dev_error otherwise);
+    ``state`` is an optional zero-initialised int32 device word that makes the
+    check happen once per buffer, on its first batch with routed rows."""
+    _want(rows, torch.bfloat16, "rows")
+    _want(row_of, torch.int32, "row_of")
+    _want(kernel_out, torch.bfloat16, "kernel_out")
+    if state is not None:
+        _want(state, torch.int32, "state")
+    num_rows, H = rows.shape
+    check("moe_combine_check", load().moe_combine_check(
+        _ptr(rows), num_rows, _ptr(row_of), _ptr(shared), T, K, H, _ptr(kernel_out), _ptr(state),
+        _ptr(dev_error), _stream(stream)))
 
 
 def moe_copy_bytes(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:

@@ -58,7 +58,9 @@ enum {
 /* ---- device error word codes (first error wins) ----------------------- */
 enum {
   MOE_DEVERR_ROW_RANGE = 1, /* a row index points outside its buffer       */
-  MOE_DEVERR_CAPACITY = 2   /* the segments need more rows than `capacity` */
+  MOE_DEVERR_CAPACITY = 2,  /* the segments need more rows than `capacity` */
+  MOE_DEVERR_LAYOUT = 3     /* moe_combine_check: rows do not reproduce the
+                               output they were checked against          */
 };
 
 /* ---- flags -------------------------------------------------------------- */
@@ -234,6 +236,31 @@ int moe_scale_from_amax(const float* amax, float* scale, void* stream);
 int moe_combine(const uint16_t* rows, int64_t num_rows, const int32_t* row_of,
                 const uint16_t* shared, int T, int K, int H, const float* row_qdq_scale,
                 uint16_t* out, int32_t* dev_error, void* stream);
+
+/* ---- layout check for a fused kernel's combine ---------------------------
+ * [P1] PR summary, "How it works" and the review thread on graph capture:
+ * where one fused kernel both combines and leaves its per-(token, slot) rows
+ * in a buffer, the quantizer relies on knowing that buffer's layout.  It
+ * checks, on the first batch that has routed rows, that the rows re-summed in
+ * the kernel's order reproduce the kernel's output bit for bit, and fails
+ * closed otherwise; a graph captured before that check carries the check
+ * itself, so replays perform it on the device.
+ *
+ * This call re-sums `rows` exactly as moe_combine does without QDQ (valid
+ * slots ascending, float32 from +0, `shared` last, one bf16 rounding) and
+ * compares every element with `kernel_out` [T, H] bit for bit; on any
+ * difference it stores MOE_DEVERR_LAYOUT into *dev_error (first error wins).
+ * rows, num_rows, row_of, shared, T, K, H mean what they mean for
+ * moe_combine.  `state` (nullable, one device int32, zero before the first
+ * call on a buffer): a call that finds 1 does nothing (the buffer has been
+ * checked); otherwise the call leaves 1 when the batch had at least one
+ * routed slot and everything matched, else 0 — so padding-only batches defer
+ * the check to the next batch with routed rows.  With state NULL every call
+ * checks.  No host sync; capturable (replays of a captured call keep reading
+ * and updating the state word).  Requires H % 128 == 0. */
+int moe_combine_check(const uint16_t* rows, int64_t num_rows, const int32_t* row_of,
+                      const uint16_t* shared, int T, int K, int H, const uint16_t* kernel_out,
+                      int32_t* state, int32_t* dev_error, void* stream);
 
 /* ---- streaming copy -----------------------------------------------------
  * dst[0:bytes) = src[0:bytes) with 16-byte vector loads and stores: the

@@ -282,6 +282,92 @@ def test_combine_random_rows(T, K, H):
     _combine_case(rows, (k_idx * T + t_idx).astype(np.int32), T, K, shared)
 
 
+def _check_case(seed=7, T=37, K=4, H=256):
+    rng = np.random.default_rng(seed)
+    rows = f32_to_bf16_bits(rng.standard_normal((T * K, H)).astype(np.float32))
+    row_of = rng.permutation(T * K).astype(np.int32)
+    row_of[rng.random(T * K) < 0.2] = -1
+    shared = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    return rows, row_of, shared
+
+
+def _run_check(rows, row_of, T, K, out, shared, state=None):
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ops.moe_combine_check(dev_bf16(rows), dev(row_of), T, K, dev_bf16(out), dev_bf16(shared),
+                          state, err)
+    torch.cuda.synchronize()
+    return int(err.item())
+
+
+def test_combine_check_layout():
+    """Page 1's layout check: rows that re-sum (in the combine order) to the
+    fused kernel's output pass and mark the buffer checked; any difference
+    raises MOE_DEVERR_LAYOUT; a checked buffer is not checked again; a
+    padding-only batch defers the check; without a state word every call
+    checks.  Expected outputs are the oracle's combine."""
+    T, K, H = 37, 4, 256
+    rows, row_of, shared = _check_case(T=T, K=K, H=H)
+    want = oracle.combine(rows, row_of, T, K, shared)
+    bad = want.copy()
+    bad[5, 17] ^= 1                                   # one bit of one element
+    # the same buffer read with another layout (every row one position on)
+    other = np.where(row_of >= 0, (row_of + 1) % (T * K), -1).astype(np.int32)
+    assert not np.array_equal(oracle.combine(rows, other, T, K, shared), want)
+    state = torch.zeros(1, dtype=torch.int32, device="cuda")
+    assert _run_check(rows, row_of, T, K, want, shared, state) == 0
+    assert int(state.item()) == 1
+    assert _run_check(rows, row_of, T, K, bad, shared, state) == 0      # checked once
+    assert int(state.item()) == 1
+    state.zero_()
+    assert _run_check(rows, row_of, T, K, bad, shared, state) == ops.MOE_DEVERR_LAYOUT
+    assert int(state.item()) == 0
+    assert _run_check(rows, other, T, K, want, shared, state) == ops.MOE_DEVERR_LAYOUT
+    assert int(state.item()) == 0
+    # padding-only batch (every slot -1): consistent output, but nothing routed
+    pad = np.full(T * K, -1, np.int32)
+    assert _run_check(rows, pad, T, K, oracle.combine(rows, pad, T, K, shared), shared, state) == 0
+    assert int(state.item()) == 0
+    # no state: every call checks
+    assert _run_check(rows, row_of, T, K, want, shared) == 0
+    assert _run_check(rows, row_of, T, K, bad, shared) == ops.MOE_DEVERR_LAYOUT
+
+
+@pytest.mark.parametrize("wrong", [False, True])
+def test_combine_check_in_graph_after_padding_warmup(wrong):
+    """A graph captured before any routed batch holds the check: the replay
+    over a padding-only batch defers it, the first replay with routed rows
+    performs it (raising on a changed layout), later replays skip it."""
+    T, K, H = 29, 3, 128
+    rows, row_of, shared = _check_case(seed=8, T=T, K=K, H=H)
+    want = oracle.combine(rows, row_of, T, K, shared)
+    layout = np.where(row_of >= 0, (row_of + 1) % (T * K), -1).astype(np.int32) if wrong else row_of
+    d_rows, d_shared = dev_bf16(rows), dev_bf16(shared)
+    d_row_of = torch.full((T * K,), -1, dtype=torch.int32, device="cuda")   # padding warmup
+    d_out = dev_bf16(oracle.combine(rows, np.full(T * K, -1, np.int32), T, K, shared))
+    state = torch.zeros(1, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ops.moe_combine_check(d_rows, d_row_of, T, K, d_out, d_shared, state, err)
+    g.replay()
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and int(state.item()) == 0          # deferred
+    d_row_of.copy_(dev(layout))
+    d_out.copy_(dev_bf16(want))
+    g.replay()
+    torch.cuda.synchronize()
+    if wrong:
+        assert int(err.item()) == ops.MOE_DEVERR_LAYOUT and int(state.item()) == 0
+    else:
+        assert int(err.item()) == 0 and int(state.item()) == 1
+        d_out.view(torch.int16)[0, 0] += 1                           # later corruption
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0 and int(state.item()) == 1      # checked once
+
+
 def test_combine_row_out_of_range_flagged():
     rows = np.zeros((4, 128), np.uint16)
     row_of = np.array([0, 9, 1, -1], np.int32)

@@ -156,11 +156,14 @@ int moe_fake_quant_rows(const uint16_t* in, uint16_t* out, int64_t n_rows, int H
                         const int32_t* row_src, int mode, int block, const float* scale,
                         float* block_scales, float* amax_out, void* stream) {
   if (n_rows < 0 || H < 1) return MOE_ERR_INVALID_ARG;
-  if (mode != MOE_FQ_PER_TENSOR && mode != MOE_FQ_BLOCK) return MOE_ERR_INVALID_ARG;
+  if (mode < MOE_FQ_PER_TENSOR || mode > MOE_FQ_MXFP4) return MOE_ERR_INVALID_ARG;
   if (H % 128) return MOE_ERR_UNSUPPORTED;
-  if (mode == MOE_FQ_BLOCK && block != 128) return MOE_ERR_UNSUPPORTED;
+  if ((mode == MOE_FQ_BLOCK && block != 128) || (mode == MOE_FQ_NVFP4 && block != 16) ||
+      (mode == MOE_FQ_MXFP4 && block != 32))
+    return MOE_ERR_UNSUPPORTED;
   if (n_rows == 0) return MOE_OK;
-  if (!in || (!out && (mode == MOE_FQ_BLOCK || scale))) return MOE_ERR_INVALID_ARG;
+  const bool writes = mode == MOE_FQ_BLOCK || mode == MOE_FQ_MXFP4 || scale;
+  if (!in || (!out && writes)) return MOE_ERR_INVALID_ARG;
   if (!aligned16(in) || (out && !aligned16(out))) return MOE_ERR_INVALID_ARG;
   return launch_fake_quant(in, out, n_rows, H, row_src, mode, scale, block_scales, amax_out,
                            as_stream(stream));

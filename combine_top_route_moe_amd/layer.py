@@ -20,17 +20,31 @@ from __future__ import annotations
 
 from typing import Callable, Dict, List, Optional, Tuple
 
+import numpy as np
 import torch
 
 from . import ops
+
+
+_FP4 = {"nvfp4": (ops.MOE_FQ_NVFP4, 16), "mxfp4": (ops.MOE_FQ_MXFP4, 32)}
 
 
 class MoELayer:
     def __init__(self, T: int, H: int, E: int, K: int, I: int, device="cuda",
                  shared_I: int = 0, dispatch_block: int = 0, combine_qdq: bool = False,
                  pad_pow2: bool = False, renormalize: bool = True, expert_begin: int = 0,
-                 num_local_experts: Optional[int] = None):
+                 num_local_experts: Optional[int] = None, dispatch_fp4: Optional[str] = None,
+                 combine_fp4: Optional[str] = None):
+        """``dispatch_block`` (128) selects the FP8 dispatch quantizer and
+        ``combine_qdq`` the FP8 combine quantizer; ``dispatch_fp4`` /
+        ``combine_fp4`` ("nvfp4" or "mxfp4") the FP4 ones instead.  NVFP4
+        tensor scales live in ``dispatch_scale`` / ``combine_scale`` (device
+        scalars the caller fills, or ``calibrate_combine_scale``)."""
+        for fmt in (dispatch_fp4, combine_fp4):
+            if fmt not in (None, "nvfp4", "mxfp4"):
+                raise ValueError(f"unknown FP4 format {fmt!r}")
         self.T, self.H, self.E, self.K, self.I = T, H, E, K, I
+        self.dispatch_fp4, self.combine_fp4 = dispatch_fp4, combine_fp4
         self.shared_I = shared_I
         self.dispatch_block = dispatch_block
         self.combine_qdq = combine_qdq
@@ -46,7 +60,8 @@ class MoELayer:
 
         self.topk_idx = torch.empty(T, K, **i32)
         self.topk_w = torch.empty(T, K, **f32)
-        self.hidden_q = torch.empty(T, H, **bf) if dispatch_block else None
+        self.hidden_q = torch.empty(T, H, **bf) if (dispatch_block or dispatch_fp4) else None
+        self.dispatch_scale = torch.zeros(1, **f32) if dispatch_fp4 == "nvfp4" else None
         self.capacity = ops.moe_permute_capacity(T, K, self.El, pad_pow2)
         self.perm = ops.alloc_permuted(T, K, H, self.El, self.capacity, dev)
         self.perm_ws = torch.empty(max(ops.moe_permute_workspace_bytes(T, K, self.El, pad_pow2), 1),
@@ -56,7 +71,8 @@ class MoELayer:
         self.y_perm = torch.empty(self.capacity, H, **bf)
         self.out = torch.empty(T, H, **bf)
         self.dev_error = torch.zeros(1, **i32)
-        self.combine_scale = torch.zeros(1, **f32) if combine_qdq else None
+        self.combine_scale = (torch.zeros(1, **f32) if combine_qdq or combine_fp4 == "nvfp4"
+                              else None)
         self.amax = torch.zeros(1, **f32)
         if shared_I:
             # the shared expert depends only on `hidden`: forward() runs it on
@@ -106,10 +122,14 @@ class MoELayer:
         the two branches)."""
         p = self.perm
         layout = ops.MOE_FFN_PACKED_WEIGHTS if self.packed else 0
-        x = self.hidden_q if self.dispatch_block else hidden
+        x = self.hidden_q if self.hidden_q is not None else hidden
         st = [("route", lambda: ops.moe_route(logits, self.K, row_valid, self.renormalize,
                                                self.topk_idx, self.topk_w))]
-        if self.dispatch_block:
+        if self.dispatch_fp4:
+            mode, block = _FP4[self.dispatch_fp4]
+            st.append(("dispatch_qdq", lambda: ops.moe_fake_quant_rows(
+                hidden, self.hidden_q, None, mode, block, self.dispatch_scale)))
+        elif self.dispatch_block:
             st.append(("dispatch_qdq", lambda: ops.moe_fake_quant_rows(
                 hidden, self.hidden_q, None, ops.MOE_FQ_BLOCK, self.dispatch_block)))
         st.append(("permute", lambda: ops.moe_permute(
@@ -121,6 +141,12 @@ class MoELayer:
         st.append(("ffn_down", lambda: ops.moe_grouped_ffn(
             p.x_perm, p.cu_seqlens, p.counts, self.w13, self.w2, p.w_perm, self.y_perm,
             ops.MOE_FFN_DOWN | layout, self.ffn_ws, self.dev_error)))
+        if self.combine_fp4:
+            # FP4 combine rows: the routed rows quantized in place (padding
+            # rows skipped through src_of), then a plain combine
+            cmode, cblock = _FP4[self.combine_fp4]
+            st.append(("combine_qdq", lambda: ops.moe_fake_quant_rows(
+                self.y_perm, self.y_perm, p.src_of, cmode, cblock, self.combine_scale)))
         if self.shared_I:
             def shared(stream=None):
                 ops.moe_grouped_ffn(hidden, self.shared_cu, self.shared_counts, self.shared_w13,
@@ -137,9 +163,10 @@ class MoELayer:
                 st.append(("join_shared", lambda: torch.cuda.current_stream().wait_stream(self.side)))
             else:
                 st.append(("shared_ffn", shared))
+        fp8_scale = self.combine_scale if (self.combine_qdq and not self.combine_fp4) else None
         st.append(("combine", lambda: ops.moe_combine(
-            self.y_perm, p.row_of, self.T, self.K, self.shared_out,
-            self.combine_scale if self.combine_qdq else None, self.out, self.dev_error)))
+            self.y_perm, p.row_of, self.T, self.K, self.shared_out, fp8_scale, self.out,
+            self.dev_error)))
         return st
 
     def forward(self, logits: torch.Tensor, hidden: torch.Tensor,
@@ -153,17 +180,23 @@ class MoELayer:
     def calibrate_combine_scale(self, logits, hidden, row_valid=None) -> torch.Tensor:
         """One-time max calibration of the constant combine-row scale: run the
         layer without combine-row QDQ, take max|row| over the routed rows and
-        store amax/448 on the device."""
-        qdq = self.combine_qdq
-        self.combine_qdq = False
+        store amax/448 (FP8) or amax/(6*448) (NVFP4) on the device."""
+        qdq, fp4 = self.combine_qdq, self.combine_fp4
+        self.combine_qdq, self.combine_fp4 = False, None
         self.forward(logits, hidden, row_valid)
-        self.combine_qdq = qdq
+        self.combine_qdq, self.combine_fp4 = qdq, fp4
         self.amax.zero_()
         ops.moe_fake_quant_rows(self.y_perm, None, self.perm.src_of, ops.MOE_FQ_PER_TENSOR,
                                 128, None, None, self.amax)
         if self.combine_scale is None:
             self.combine_scale = torch.zeros(1, dtype=torch.float32, device=self.device)
-        ops.moe_scale_from_amax(self.amax, self.combine_scale)
+        if self.combine_fp4 == "nvfp4":
+            # one-time, outside the layer's hot path (a host sync is fine here):
+            # the IEEE float32 quotient amax / (6 * 448)
+            g = np.float32(np.float32(self.amax.item()) / np.float32(6.0 * 448.0))
+            self.combine_scale.fill_(float(g))
+        else:
+            ops.moe_scale_from_amax(self.amax, self.combine_scale)
         return self.combine_scale
 
     def stage_outputs(self) -> Dict[str, torch.Tensor]:

@@ -18,7 +18,7 @@ from ._lib import load, check
 MOE_ROUTE_RENORM = 1
 MOE_PERMUTE_PAD_POW2 = 1
 MOE_FFN_GATE_UP, MOE_FFN_DOWN, MOE_FFN_ALL, MOE_FFN_PACKED_WEIGHTS = 1, 2, 3, 4
-MOE_FQ_PER_TENSOR, MOE_FQ_BLOCK = 0, 1
+MOE_FQ_PER_TENSOR, MOE_FQ_BLOCK, MOE_FQ_NVFP4, MOE_FQ_MXFP4 = 0, 1, 2, 3
 MOE_DEVERR_ROW_RANGE, MOE_DEVERR_CAPACITY, MOE_DEVERR_LAYOUT = 1, 2, 3
 
 
@@ -184,7 +184,7 @@ def moe_fake_quant_rows(inp: torch.Tensor, out: Optional[torch.Tensor] = None,
                         amax_out: Optional[torch.Tensor] = None, stream=None):
     _want(inp, torch.bfloat16, "in")
     n_rows, H = inp.shape
-    if out is None and (mode == MOE_FQ_BLOCK or scale is not None):
+    if out is None and (mode in (MOE_FQ_BLOCK, MOE_FQ_MXFP4) or scale is not None):
         out = torch.empty_like(inp)
     if row_src is not None:
         _want(row_src, torch.int32, "row_src")

@@ -71,7 +71,9 @@ enum { MOE_FFN_GATE_UP = 1,           /* moe_grouped_ffn flags: stages ... */
        MOE_FFN_ALL = 3,
        MOE_FFN_PACKED_WEIGHTS = 4 };  /* ... and the weight layout          */
 enum { MOE_FQ_PER_TENSOR = 0,         /* moe_fake_quant_rows modes         */
-       MOE_FQ_BLOCK = 1 };
+       MOE_FQ_BLOCK = 1,
+       MOE_FQ_NVFP4 = 2,
+       MOE_FQ_MXFP4 = 3 };
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* moe_status_string(int status);
@@ -187,7 +189,7 @@ int moe_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32_t*
 int moe_pack_ffn_weights(const uint16_t* w13, const uint16_t* w2, int num_groups, int H, int I,
                          uint16_t* w13_packed, uint16_t* w2_packed, void* stream);
 
-/* ---- FP8 fake-quant of bf16 rows ---------------------------------------
+/* ---- FP8 and FP4 fake-quant of bf16 rows -------------------------------
  * QDQ to OCP E4M3FN and back ([P1] PR summary and "How it works": the
  * dispatch quantizer fake-quantizes the experts' input tokens, the combine
  * quantizer the router-weighted per-(token, slot) BF16 rows with a
@@ -211,6 +213,21 @@ int moe_pack_ffn_weights(const uint16_t* w13, const uint16_t* w2, int num_groups
 int moe_fake_quant_rows(const uint16_t* in, uint16_t* out, int64_t n_rows, int H,
                         const int32_t* row_src, int mode, int block, const float* scale,
                         float* block_scales, float* amax_out, void* stream);
+/* The FP4 modes ([P1] names NVFP4 dispatch and combine units, [P4]'s test
+ * plan an MXFP4 expert path; the pages do not define the formats, so these
+ * are the published definitions).  Elements are E2M1 (magnitudes 0, 0.5, 1,
+ * 1.5, 2, 3, 4, 6), round-to-nearest with ties to the even code, saturating
+ * at 6; the sign of a zero is kept.
+ *   MOE_FQ_MXFP4 (block must be 32): per row and 32 channels, the OCP MX
+ *     power-of-two scale X = 2^(floor(log2 amax) - 2), exponent clamped to
+ *     [-127, 127]; x' = bf16( e2m1(clamp(x / X, -6, 6)) * X ) (exact); an
+ *     all-zero block gives +0; block_scales [n_rows, H/32] receives X.
+ *     `scale` is ignored.
+ *   MOE_FQ_NVFP4 (block must be 16): g = *scale, the per-tensor scale
+ *     (calibrated, e.g. amax / (6 * 448), or constant; NULL = calibration
+ *     only); per row and 16 channels b = e4m3( min(fl32(amax / fl32(6 g)),
+ *     448) ), S = fl32(b * g), x' = bf16( fl32( e2m1(clamp(fl32(x / S), -6,
+ *     6)) * S ) ); S == 0 gives +0; block_scales [n_rows, H/16] receives b. */
 
 /* scale[0] = fl32(amax[0] / 448) (IEEE division) on the device: turns a
  * calibrated amax into the constant per-tensor E4M3FN scale ([P1] "How it

@@ -13,7 +13,7 @@ its Python binding) never calls into it.
 
 Precision: everything the pages fix exactly is emulated exactly (IEEE
 binary32 adds in the combine, one bfloat16 round-to-nearest-even, OCP
-E4M3FN round-to-nearest-even with saturation).  Everything else (softmax
+E4M3FN and E2M1 round-to-nearest-even with saturation).  Everything else (softmax
 weights, the expert FFN) is computed in float64.
 
 Pins (tests/test_oracle_*.py, run with ``-m "not gpu"``) tie every function
@@ -33,6 +33,7 @@ from .numerics import (
 )
 from .route import route
 from .quant import fake_quant_block, fake_quant_per_tensor, calibrate_amax
+from .fp4 import e2m1_round, fake_quant_mxfp4, fake_quant_nvfp4, nvfp4_tensor_scale
 from .permute import permute, next_pow2
 from .ffn import expert_ffn, grouped_ffn
 from .combine import combine

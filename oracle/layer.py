@@ -27,6 +27,7 @@ import numpy as np
 from .numerics import bf16_bits_to_f64, f32_to_bf16_bits
 from .route import route
 from .quant import fake_quant_block, fake_quant_per_tensor, calibrate_amax, scale_from_amax
+from .fp4 import fake_quant_mxfp4, fake_quant_nvfp4, nvfp4_tensor_scale
 from .permute import permute
 from .ffn import grouped_ffn, expert_ffn
 from .combine import combine
@@ -45,11 +46,16 @@ def _rows_to_bf16(y64):
 def moe_layer(logits, hidden_bits, weights, k: int, row_valid=None,
               renormalize: bool = True, dispatch_block=None, pad_pow2=False,
               shared_weights=None, combine_qdq: bool = False, combine_scale=None,
-              expert_begin: int = 0, num_local_experts=None):
+              expert_begin: int = 0, num_local_experts=None, dispatch_fp4=None,
+              dispatch_scale=None, combine_fp4=None):
     """Run the oracle layer and return every intermediate in a dict.
 
     ``weights(e)`` returns expert ``e``'s ``(w13, w2)`` as bfloat16 bits
     (global expert index).  ``shared_weights``: optional ``(w13, w2)``.
+    ``dispatch_fp4`` / ``combine_fp4`` ("nvfp4" or "mxfp4") select the FP4
+    quantizers instead of the FP8 ones; an NVFP4 tensor scale not given
+    (``dispatch_scale``, ``combine_scale``) is calibrated like the FP8
+    combine scale: ``amax / (6 * 448)`` over the rows the quantizer sees.
     """
     logits = np.asarray(logits, dtype=np.float32)
     hidden_bits = np.asarray(hidden_bits, dtype=np.uint16)
@@ -59,7 +65,14 @@ def moe_layer(logits, hidden_bits, weights, k: int, row_valid=None,
     topk_idx, topk_w = route(logits, row_valid, k, renormalize)
     valid_tok = (topk_idx >= 0).any(axis=1)
 
-    if dispatch_block:
+    dscale = None
+    if dispatch_fp4 == "mxfp4":
+        hidden_q, dscales = fake_quant_mxfp4(hidden_bits, row_mask=valid_tok)
+    elif dispatch_fp4 == "nvfp4":
+        dscale = (nvfp4_tensor_scale(calibrate_amax(hidden_bits, valid_tok))
+                  if dispatch_scale is None else np.float32(dispatch_scale))
+        hidden_q, dscales = fake_quant_nvfp4(hidden_bits, dscale, row_mask=valid_tok)
+    elif dispatch_block:
         hidden_q, dscales = fake_quant_block(hidden_bits, dispatch_block, row_mask=valid_tok)
     else:
         hidden_q, dscales = hidden_bits, None
@@ -72,7 +85,13 @@ def moe_layer(logits, hidden_bits, weights, k: int, row_valid=None,
 
     scale = None
     rows_q = rows
-    if combine_qdq:
+    if combine_fp4 == "mxfp4":
+        rows_q, _ = fake_quant_mxfp4(rows, row_mask=routed_rows)
+    elif combine_fp4 == "nvfp4":
+        scale = (nvfp4_tensor_scale(calibrate_amax(rows, routed_rows))
+                 if combine_scale is None else np.float32(combine_scale))
+        rows_q, _ = fake_quant_nvfp4(rows, scale, row_mask=routed_rows)
+    elif combine_qdq:
         if combine_scale is None:
             scale = scale_from_amax(calibrate_amax(rows, routed_rows))
         else:
@@ -87,7 +106,7 @@ def moe_layer(logits, hidden_bits, weights, k: int, row_valid=None,
     out = combine(rows_q, perm["row_of"], T, k, shared)
     return {
         "topk_idx": topk_idx, "topk_w": topk_w,
-        "hidden_q": hidden_q, "dispatch_scales": dscales,
+        "hidden_q": hidden_q, "dispatch_scales": dscales, "dispatch_scale": dscale,
         "perm": perm, "y": y, "rows": rows, "rows_q": rows_q,
         "combine_scale": scale, "shared": shared, "out": out,
     }

@@ -126,6 +126,64 @@ def test_layer_tiny_variants(variant):
         assert abs(s_gpu - float(ref["combine_scale"])) <= TOL * float(ref["combine_scale"])
 
 
+@pytest.mark.parametrize("dfmt,cfmt,shared_I", [("nvfp4", "nvfp4", 0), ("mxfp4", "mxfp4", 128),
+                                                 ("nvfp4", "mxfp4", 0), (None, "nvfp4", 256)])
+def test_layer_fp4_quantizers(dfmt, cfmt, shared_I):
+    """The FP4 dispatch and combine quantizers in the layer, stage by stage.
+    FP4 steps are coarse (25-50 % of a value), so a 1-ulp FFN difference can
+    flip a rounding: each quantizer is checked bit for bit on the rows it is
+    given, the FFN rows within the FFN tolerance.  The dispatch rows and the
+    NVFP4 tensor scales are the oracle's; the GPU's own NVFP4 combine
+    calibration must agree with the oracle's."""
+    cfg = workloads.CONFIGS["tiny"].with_(pad_rows=5, shared_I=shared_I)
+    W = Weights(cfg)
+    lg, hd, vd = workloads.logits(cfg), workloads.hidden(cfg), workloads.row_valid(cfg)
+    ref = oracle.moe_layer(lg, hd, lambda e: W.host[e], cfg.K, vd, shared_weights=W.shared_host,
+                           dispatch_fp4=dfmt, combine_fp4=cfmt)
+    layer = MoELayer(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, "cuda", shared_I=shared_I,
+                     dispatch_fp4=dfmt, combine_fp4=cfmt)
+    layer.set_weights(W.w13, W.w2, *(W.shared or (None, None)))
+    if dfmt == "nvfp4":
+        layer.dispatch_scale.fill_(float(ref["dispatch_scale"]))
+    if cfmt == "nvfp4":
+        layer.combine_scale.fill_(float(ref["combine_scale"]))
+    lgd, hdd, vdd = dev(lg), dev_bf16(hd), dev(vd)
+    y_unq = None
+    for name, enqueue in layer.stages(lgd, hdd, vdd):
+        if name == "combine_qdq":
+            torch.cuda.synchronize()
+            y_unq = host_bits(layer.y_perm).copy()
+        enqueue()
+    torch.cuda.synchronize()
+    assert layer.dev_error.item() == 0
+    valid_tok = (ref["topk_idx"] >= 0).any(axis=1)
+    np.testing.assert_array_equal(host(layer.topk_idx), ref["topk_idx"])
+    if dfmt:
+        np.testing.assert_array_equal(host_bits(layer.hidden_q)[valid_tok], ref["hidden_q"][valid_tok])
+    src = host(layer.perm.src_of)
+    routed = src >= 0
+    used = int(ref["perm"]["cu_seqlens"][-1])
+    # FFN rows within tolerance of the oracle's
+    np.testing.assert_array_equal(host(layer.perm.row_of), ref["perm"]["row_of"])
+    err = rel_err(bf16_bits_to_f64(y_unq[:used][routed[:used]]),
+                  bf16_bits_to_f64(ref["rows"][:used][routed[:used]]))
+    assert err <= TOL, err
+    # the combine quantizer, bit for bit on the GPU's own rows
+    if cfmt == "nvfp4":
+        want_q, _ = oracle.fake_quant_nvfp4(y_unq, ref["combine_scale"], row_mask=routed)
+    else:
+        want_q, _ = oracle.fake_quant_mxfp4(y_unq, row_mask=routed)
+    got_q = host_bits(layer.y_perm)
+    np.testing.assert_array_equal(got_q[routed], want_q[routed])
+    # the combine, bit for bit on those rows
+    shared = host_bits(layer.shared_out) if shared_I else None
+    np.testing.assert_array_equal(host_bits(layer.out),
+                                  oracle.combine(got_q, ref["perm"]["row_of"], cfg.T, cfg.K, shared))
+    if cfmt == "nvfp4":
+        g = float(host(layer.calibrate_combine_scale(lgd, hdd, vdd))[0])
+        assert abs(g - float(ref["combine_scale"])) <= TOL * float(ref["combine_scale"])
+
+
 def test_layer_expert_parallel_share():
     """One rank's share of experts [3, 7) of 8: only its slots are combined."""
     cfg = workloads.CONFIGS["tiny"]

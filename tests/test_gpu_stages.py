@@ -126,6 +126,68 @@ def test_fake_quant_near_rounding_midpoints():
         np.testing.assert_array_equal(host_bits(out), oracle.fake_quant_per_tensor(rows, s), err_msg=str(s))
 
 
+def _fp4_rows(arrange, seed=11):
+    """Every finite bfloat16 value once, as rows of 128: shuffled (blocks of
+    mixed magnitude) or sorted by magnitude (blocks of similar magnitude,
+    every scale exponent in reach)."""
+    flat = _all_finite_bf16_rows(128).reshape(-1)
+    if arrange == "shuffled":
+        flat = np.random.default_rng(seed).permutation(flat)
+    else:
+        flat = flat[np.argsort(np.abs(bf16_bits_to_f32(flat)), kind="stable")]
+    return flat.reshape(-1, 128)
+
+
+@pytest.mark.parametrize("arrange", ["shuffled", "sorted"])
+def test_fake_quant_mxfp4_exhaustive(arrange):
+    rows = _fp4_rows(arrange)
+    ref, X = oracle.fake_quant_mxfp4(rows)
+    scales = torch.empty(rows.shape[0], 4, dtype=torch.float32, device="cuda")
+    out = ops.moe_fake_quant_rows(dev_bf16(rows), mode=ops.MOE_FQ_MXFP4, block=32,
+                                  block_scales=scales)
+    np.testing.assert_array_equal(host_bits(out), ref)
+    np.testing.assert_array_equal(host(scales), X.astype(np.float32))
+
+
+@pytest.mark.parametrize("g", [1.0, 0.0123, 2.0 ** -20, 1e-30, "calibrated"])
+@pytest.mark.parametrize("arrange", ["shuffled", "sorted"])
+def test_fake_quant_nvfp4_exhaustive(g, arrange):
+    rows = _fp4_rows(arrange)
+    if g == "calibrated":
+        g = oracle.nvfp4_tensor_scale(oracle.calibrate_amax(rows))
+    g = np.float32(g)
+    ref, b = oracle.fake_quant_nvfp4(rows, g)
+    scales = torch.empty(rows.shape[0], 8, dtype=torch.float32, device="cuda")
+    out = ops.moe_fake_quant_rows(dev_bf16(rows), mode=ops.MOE_FQ_NVFP4, block=16,
+                                  scale=torch.tensor([g], device="cuda"), block_scales=scales)
+    np.testing.assert_array_equal(host_bits(out), ref)
+    np.testing.assert_array_equal(host(scales), b.astype(np.float32))
+
+
+def test_fake_quant_fp4_row_skip_and_calibration():
+    rng = np.random.default_rng(12)
+    x = f32_to_bf16_bits((rng.standard_normal((21, 256)) * 3).astype(np.float32))
+    src = np.where(rng.random(21) < 0.3, -1, np.arange(21)).astype(np.int32)
+    mask = src >= 0
+    ref, X = oracle.fake_quant_mxfp4(x, mask)
+    sc = torch.full((21, 8), 99.0, device="cuda")
+    out = ops.moe_fake_quant_rows(dev_bf16(x), row_src=dev(src), mode=ops.MOE_FQ_MXFP4, block=32,
+                                  block_scales=sc)
+    np.testing.assert_array_equal(host_bits(out), ref)
+    np.testing.assert_array_equal(host(sc), X.astype(np.float32))
+    g = np.float32(0.004)
+    ref, b = oracle.fake_quant_nvfp4(x, g, mask)
+    xd = dev_bf16(x)                                  # in place: skipped rows untouched
+    ops.moe_fake_quant_rows(xd, xd, dev(src), ops.MOE_FQ_NVFP4, 16, torch.tensor([g], device="cuda"))
+    np.testing.assert_array_equal(host_bits(xd), ref)
+    # NVFP4 without a tensor scale: calibration only
+    amax = torch.zeros(1, device="cuda")
+    keep = dev_bf16(x)
+    ops.moe_fake_quant_rows(keep, keep, dev(src), ops.MOE_FQ_NVFP4, 16, None, None, amax)
+    np.testing.assert_array_equal(host_bits(keep), x)
+    assert host(amax)[0] == oracle.calibrate_amax(x, mask)
+
+
 def test_fake_quant_row_skip_inplace_and_amax():
     rng = np.random.default_rng(1)
     x = f32_to_bf16_bits((rng.standard_normal((37, 256)) * 5).astype(np.float32))

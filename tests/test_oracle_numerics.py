@@ -10,6 +10,7 @@
 import numpy as np
 import pytest
 import torch
+import oracle
 
 from oracle.numerics import (
     bf16_bits_to_f32, f32_to_bf16_bits, e4m3fn_table, e4m3fn_round, qdq_e4m3fn,
@@ -127,3 +128,93 @@ def test_qdq_invariants():
     assert rel.max() <= 2.0 ** -4 + 2.0 ** -8
     # zero scale: all zero output
     assert np.all(qdq_e4m3fn(np.zeros(8, np.float32), np.float32(0)) == 0)
+
+
+# ---------------------------------------------------------------- FP4 (E2M1)
+# Hand-worked values; E2M1 magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6 and a
+# tie goes to the code whose mantissa bit is 0.
+
+def test_e2m1_grid_and_ties():
+    from oracle.fp4 import e2m1_table
+    np.testing.assert_array_equal(e2m1_table(), [0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    cases = {0.0: 0, 0.2: 0, 0.25: 0, 0.3: 0.5, 0.5: 0.5, 0.75: 1, 1.0: 1, 1.25: 1, 1.3: 1.5,
+             1.75: 2, 2.4: 2, 2.5: 2, 2.6: 3, 3.5: 4, 4.9: 4, 5.0: 4, 5.1: 6, 6.0: 6}
+    for v, want in cases.items():
+        assert oracle.e2m1_round(v) == want, v
+        assert oracle.e2m1_round(-v) == -want, -v
+    assert np.signbit(oracle.e2m1_round(-0.1))             # the sign survives a zero
+
+
+def _bf(vals):
+    return f32_to_bf16_bits(np.asarray(vals, np.float32))
+
+
+def test_mxfp4_hand_examples():
+    # block 0: amax 1 -> scale 2^(0-2) = 0.25; block 1: amax 7.875 -> scale 1,
+    # 7.875 saturates to 6; block 2: amax 3.984375 -> floor(log2) = 1 -> scale
+    # 0.5, 7.97 saturates to 6 -> 3; block 3: all zero
+    b0 = [1.0, 0.3, -0.6, 0.1, 0.0625] + [0.0] * 27
+    b1 = [7.875, -2.5, 0.75] + [0.0] * 29
+    b2 = [3.984375, 1.25] + [0.0] * 30
+    b3 = [0.0] * 32
+    x = _bf([b0 + b1 + b2 + b3])
+    out, X = oracle.fake_quant_mxfp4(x)
+    np.testing.assert_array_equal(X, [[0.25, 1.0, 0.5, 0.0]])
+    got = bf16_bits_to_f32(out)[0]
+    # 0.3/0.25 = 1.2 -> 1; -0.6/0.25 = -2.4 -> -2; 0.1/0.25 -> 0.5 (bf16 0.1 is
+    # 0.10009765625, 0.4004 -> 0.5); 0.0625/0.25 = 0.25 -> tie -> 0
+    np.testing.assert_array_equal(got[:5], [1.0, 0.25, -0.5, 0.125, 0.0])
+    np.testing.assert_array_equal(got[32:35], [6.0, -2.0, 1.0])     # -2.5 tie -> -2
+    np.testing.assert_array_equal(got[64:66], [3.0, 1.0])           # 1.25/0.5 = 2.5 -> 2
+    assert np.all(out[0, 96:] == 0)
+
+
+def test_mxfp4_scale_exponent_clamp():
+    # amax 2^-130 (a bfloat16 subnormal): floor(log2) - 2 = -132 clamps to
+    # -127, so x / 2^-127 = 2^-3 rounds to +0
+    tiny = np.uint16(0x0008)                                # 2^-130 in bfloat16
+    assert bf16_bits_to_f32(np.array([tiny]))[0] == np.float32(2.0 ** -130)
+    x = np.zeros((1, 32), np.uint16)
+    x[0, 0] = tiny
+    out, X = oracle.fake_quant_mxfp4(x)
+    assert X[0, 0] == 2.0 ** -127 and np.all(out == 0)
+    # a huge block: amax 2^127 -> scale 2^125; 2^127 / 2^125 = 4 exactly
+    x[0, 0] = np.uint16(0x7F00)                             # 2^127
+    out, X = oracle.fake_quant_mxfp4(x)
+    assert X[0, 0] == 2.0 ** 125 and out[0, 0] == np.uint16(0x7F00)
+
+
+def test_nvfp4_hand_examples():
+    # tensor scale 1: block scale = e4m3(amax / 6)
+    x = _bf([[6.0, 2.703125] + [0.0] * 14 +            # b = 1: 2.703 -> 3
+             [12.0, 5.0, -3.0] + [0.0] * 13 +          # b = 2: 2.5 -> 2 -> 4; -1.5 -> -3
+             [6.5, 1.0] + [0.0] * 14 +                 # b = e4m3(1.0833) = 1.125: 5.78 -> 6
+             [0.0] * 16])
+    out, b = oracle.fake_quant_nvfp4(x, 1.0)
+    np.testing.assert_array_equal(b, [[1.0, 2.0, 1.125, 0.0]])
+    got = bf16_bits_to_f32(out)[0]
+    np.testing.assert_array_equal(got[:2], [6.0, 3.0])
+    np.testing.assert_array_equal(got[16:19], [12.0, 4.0, -3.0])
+    # 6.5 / 1.125 = 5.78 -> 6 -> 6.75; 1 / 1.125 = 0.889 -> 1 -> 1.125
+    np.testing.assert_array_equal(got[32:34], [6.75, 1.125])
+    assert np.all(out[0, 48:] == 0)
+    # a zero tensor scale zeroes everything
+    out0, _ = oracle.fake_quant_nvfp4(x, 0.0)
+    assert np.all(out0 == 0)
+
+
+def test_nvfp4_tensor_scale_closed_form():
+    assert oracle.nvfp4_tensor_scale(6 * 448) == np.float32(1.0)
+    assert oracle.nvfp4_tensor_scale(0) == np.float32(0.0)
+
+
+def test_fp4_row_mask_leaves_rows():
+    rng = np.random.default_rng(3)
+    x = _bf(rng.standard_normal((4, 64)))
+    mask = np.array([True, False, True, False])
+    for fn in (lambda a, m: oracle.fake_quant_mxfp4(a, m),
+               lambda a, m: oracle.fake_quant_nvfp4(a, 0.01, m)):
+        out, sc = fn(x, mask)
+        np.testing.assert_array_equal(out[~mask], x[~mask])
+        assert np.all(sc[~mask] == 0)
+        assert not np.array_equal(out[mask], x[mask])

@@ -32,7 +32,7 @@ from .numerics import (
     qdq_e4m3fn,
 )
 from .route import route
-from .quant import fake_quant_block, fake_quant_per_tensor, calibrate_amax
+from .quant import fake_quant_block, fake_quant_per_tensor, calibrate_amax, quantize_weight_blocks
 from .fp4 import e2m1_round, fake_quant_mxfp4, fake_quant_nvfp4, nvfp4_tensor_scale
 from .permute import permute, next_pow2
 from .ffn import expert_ffn, grouped_ffn

@@ -24,7 +24,7 @@ Formula (for one block, or one tensor with a given scale):
 
 import numpy as np
 
-from .numerics import bf16_bits_to_f32, qdq_e4m3fn, E4M3FN_MAX
+from .numerics import bf16_bits_to_f32, qdq_e4m3fn, e4m3fn_round, E4M3FN_MAX
 
 
 def fake_quant_block(x_bits, block: int = 128, row_mask=None):
@@ -78,3 +78,31 @@ def fake_quant_per_tensor(x_bits, scale, row_mask=None):
         keep = ~np.asarray(row_mask, dtype=bool)
         out[keep] = x_bits[keep]
     return out
+
+
+def quantize_weight_blocks(w_bits, block: int = 128):
+    """FP8 weights with one scale per ``block x block`` tile of a bfloat16
+    matrix ``[N, K]`` (both multiples of ``block``): the weight half of the
+    real FP8 grouped GEMM ("next" after the fake-quant units: weights in
+    E4M3 with 128x128 block scales).
+
+    ``s = fl32(amax / 448)`` per tile (``amax == 0`` gives ``s = 0``), element
+    ``q = e4m3(clamp(fl32(w / s), +-448))``.  Returns ``(q float64 [N, K]`` —
+    the E4M3 values themselves — ``, s float32 [N/block, K/block],
+    dequantized bf16 bits [N, K])`` where the dequantized weight is
+    ``bf16(fl32(q * s))``: the FP8 fake-quant of ``w`` with the tile's scale,
+    which is exactly what a GEMM on the FP8 weights multiplies.
+    """
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    N, K = w_bits.shape
+    if N % block or K % block:
+        raise ValueError("both dimensions must be multiples of the block size")
+    w = bf16_bits_to_f32(w_bits).reshape(N // block, block, K // block, block)
+    amax = np.abs(w).max(axis=(1, 3))                                  # exact, float32
+    s = (amax / np.float32(E4M3FN_MAX)).astype(np.float32)             # IEEE division
+    sb = s[:, None, :, None]
+    safe = np.where(sb > 0, sb, np.float32(1))
+    r = np.clip((w / safe).astype(np.float32), -E4M3FN_MAX, E4M3FN_MAX)
+    q = np.where(sb > 0, e4m3fn_round(r), 0.0)
+    deq = qdq_e4m3fn(w, sb).reshape(N, K)
+    return q.reshape(N, K), s, deq

@@ -218,3 +218,24 @@ def test_fp4_row_mask_leaves_rows():
         np.testing.assert_array_equal(out[~mask], x[~mask])
         assert np.all(sc[~mask] == 0)
         assert not np.array_equal(out[mask], x[mask])
+
+
+def test_fp8_weight_blocks_hand_examples():
+    """Weights in E4M3 with one scale per 128x128 tile: tile (0, 1) has amax
+    448 (scale 1, E4M3 step 0.25 in [2, 4): 3.09375 -> 3), tile (1, 0) amax
+    4.48 -> bf16 4.46875, scale fl32(4.46875/448); tile (1, 1) is all zero."""
+    w = np.zeros((256, 256), np.float32)
+    w[5, 130] = 448.0
+    w[7, 200] = 3.09375
+    w[7, 201] = -3.15625                       # nearer to -3.25 than to -3
+    w[140, 3] = 4.46875
+    w[141, 4] = -4.46875
+    q, s, deq = oracle.quantize_weight_blocks(f32_to_bf16_bits(w))
+    s_10 = np.float32(np.float32(4.46875) / np.float32(448))
+    np.testing.assert_array_equal(s, np.array([[0, 1], [s_10, 0]], np.float32))
+    assert q[7, 200] == 3.0 and q[7, 201] == -3.25 and q[5, 130] == 448.0
+    assert abs(q[140, 3]) == 448.0 and q[141, 4] == -q[140, 3]
+    d = bf16_bits_to_f32(deq)
+    assert d[7, 200] == 3.0 and d[7, 201] == -3.25 and d[5, 130] == 448.0
+    assert d[140, 3] == np.float32(4.46875)    # 448 * s rounds back to the bf16 amax
+    assert np.count_nonzero(d) == 5

@@ -21,10 +21,12 @@ int launch_permute(const int32_t*, const float*, const uint16_t*, int, int, int,
                    int32_t*, hipStream_t);
 size_t grouped_ffn_workspace_bytes(int64_t, int, int);
 int launch_grouped_ffn(const uint16_t*, const int32_t*, const int32_t*, int, int, int,
-                       const uint16_t*, const uint16_t*, const float*, uint16_t*, int64_t, int,
-                       void*, int32_t*, hipStream_t);
+                       const void*, const float*, const void*, const float*, const float*,
+                       uint16_t*, int64_t, int, void*, int32_t*, hipStream_t);
 int launch_pack_weights(const uint16_t*, const uint16_t*, int, int, int, uint16_t*, uint16_t*,
                         hipStream_t);
+int launch_pack_weights_fp8(const uint16_t*, const uint16_t*, int, int, int, uint8_t*, float*,
+                            uint8_t*, float*, hipStream_t);
 
 __global__ void __launch_bounds__(256) copy_kernel(const uint4* __restrict__ src,
                                                    uint4* __restrict__ dst, int64_t n) {
@@ -136,8 +138,37 @@ int moe_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32_t*
   const size_t need = grouped_ffn_workspace_bytes(capacity, num_groups, I);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return MOE_ERR_WORKSPACE;
-  return launch_grouped_ffn(x, cu_seqlens, counts, num_groups, H, I, w13, w2, row_scale, y,
-                            capacity, flags, workspace, dev_error, as_stream(stream));
+  return launch_grouped_ffn(x, cu_seqlens, counts, num_groups, H, I, w13, nullptr, w2, nullptr,
+                            row_scale, y, capacity, flags, workspace, dev_error,
+                            as_stream(stream));
+}
+
+int moe_grouped_ffn_fp8(const uint16_t* x, const int32_t* cu_seqlens, const int32_t* counts,
+                        int num_groups, int H, int I, const uint8_t* w13q, const float* w13_scales,
+                        const uint8_t* w2q, const float* w2_scales, const float* row_scale,
+                        uint16_t* y, int64_t capacity, int flags, void* workspace,
+                        size_t workspace_bytes, int32_t* dev_error, void* stream) {
+  if (num_groups < 1 || H < 1 || I < 1 || capacity < 0) return MOE_ERR_INVALID_ARG;
+  if ((flags & ~MOE_FFN_ALL) || !(flags & MOE_FFN_ALL)) return MOE_ERR_INVALID_ARG;
+  if (H % 128 || I % 128 || num_groups > 1024) return MOE_ERR_UNSUPPORTED;
+  if (capacity > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  if (!cu_seqlens || !counts) return MOE_ERR_INVALID_ARG;
+  if ((flags & MOE_FFN_GATE_UP) && (!x || !w13q || !w13_scales)) return MOE_ERR_INVALID_ARG;
+  if ((flags & MOE_FFN_DOWN) && (!y || !w2q || !w2_scales)) return MOE_ERR_INVALID_ARG;
+  if ((x && !aligned16(x)) || (y && !aligned16(y)) || (w13q && !aligned16(w13q)) ||
+      (w2q && !aligned16(w2q)) || (w13_scales && !aligned16(w13_scales)) ||
+      (w2_scales && !aligned16(w2_scales)))
+    return MOE_ERR_INVALID_ARG;
+  const size_t need = grouped_ffn_workspace_bytes(capacity, num_groups, I);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return MOE_ERR_WORKSPACE;
+  // the FP8 kernels take the scale pointers as their mark: pass both (only
+  // the selected stage reads its own)
+  const float* s13 = w13_scales ? w13_scales : w2_scales;
+  const float* s2 = w2_scales ? w2_scales : w13_scales;
+  return launch_grouped_ffn(x, cu_seqlens, counts, num_groups, H, I, w13q, s13, w2q, s2,
+                            row_scale, y, capacity, flags | MOE_FFN_PACKED_WEIGHTS, workspace,
+                            dev_error, as_stream(stream));
 }
 
 int moe_pack_ffn_weights(const uint16_t* w13, const uint16_t* w2, int num_groups, int H, int I,
@@ -150,6 +181,20 @@ int moe_pack_ffn_weights(const uint16_t* w13, const uint16_t* w2, int num_groups
     return MOE_ERR_INVALID_ARG;
   if ((w13 && w13 == w13_packed) || (w2 && w2 == w2_packed)) return MOE_ERR_INVALID_ARG;
   return launch_pack_weights(w13, w2, num_groups, H, I, w13_packed, w2_packed, as_stream(stream));
+}
+
+int moe_pack_ffn_weights_fp8(const uint16_t* w13, const uint16_t* w2, int num_groups, int H,
+                             int I, uint8_t* w13q, float* w13_scales, uint8_t* w2q,
+                             float* w2_scales, void* stream) {
+  if (num_groups < 1 || H < 1 || I < 1) return MOE_ERR_INVALID_ARG;
+  if (H % 128 || I % 128) return MOE_ERR_UNSUPPORTED;
+  if (!w13 != !w13q || !w13 != !w13_scales || !w2 != !w2q || !w2 != !w2_scales)
+    return MOE_ERR_INVALID_ARG;
+  if ((w13 && (!aligned16(w13) || !aligned16(w13q) || !aligned16(w13_scales))) ||
+      (w2 && (!aligned16(w2) || !aligned16(w2q) || !aligned16(w2_scales))))
+    return MOE_ERR_INVALID_ARG;
+  return launch_pack_weights_fp8(w13, w2, num_groups, H, I, w13q, w13_scales, w2q, w2_scales,
+                                 as_stream(stream));
 }
 
 int moe_fake_quant_rows(const uint16_t* in, uint16_t* out, int64_t n_rows, int H,

@@ -38,6 +38,7 @@
 // Workgroups past the last tile exit at once.  MFMA sub-tiles lying wholly
 // past the segment's last row are skipped.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -46,6 +47,9 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 16-byte staging
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));  // 8 FP8 codes
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 128;
 constexpr int kBN = 128;
@@ -327,9 +331,29 @@ __device__ __forceinline__ void dma16(const uint16_t* sbase, uint32_t voff, cons
                : "m0");
 }
 
-template <bool GATE_UP, bool NT, int NW>
+// FP8 weights: a lane's 8 E4M3 codes (a B-fragment row piece) to the bf16
+// fragment the MFMA reads, bf16(fl32(code * s)) with the tile's scale s —
+// the FP8 fake-quant of the original weight, exactly.
+__device__ __forceinline__ bf16x8_t dequant8(u32x2_t c, float s) {
+  const f32x2_t v0 = __builtin_amdgcn_cvt_pk_f32_fp8(c.x, false) * s;
+  const f32x2_t v1 = __builtin_amdgcn_cvt_pk_f32_fp8(c.x, true) * s;
+  const f32x2_t v2 = __builtin_amdgcn_cvt_pk_f32_fp8(c.y, false) * s;
+  const f32x2_t v3 = __builtin_amdgcn_cvt_pk_f32_fp8(c.y, true) * s;
+  const u32x4_t w = {__builtin_bit_cast(uint32_t, __builtin_convertvector(v0, bf16x2_t)),
+                     __builtin_bit_cast(uint32_t, __builtin_convertvector(v1, bf16x2_t)),
+                     __builtin_bit_cast(uint32_t, __builtin_convertvector(v2, bf16x2_t)),
+                     __builtin_bit_cast(uint32_t, __builtin_convertvector(v3, bf16x2_t))};
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
+// The weight element of a B-fragment lane: 16 bytes of bf16, or 8 FP8 codes.
+template <bool F8>
+using WFrag = typename std::conditional<F8, u32x2_t, u32x4_t>::type;
+
+template <bool GATE_UP, bool NT, int NW, bool F8>
 __device__ __forceinline__ void frag_gemm_body(
-    u32x4_t (*As)[kStageBlocks][kWave], const u32x4_t* __restrict__ wp, int kstride,
+    u32x4_t (*As)[kStageBlocks][kWave], const WFrag<F8>* __restrict__ wp, int kstride,
+    const float* __restrict__ sc_g, const float* __restrict__ sc_u,
     const uint16_t* a_base, const int64_t* a_uoff, const uint32_t* a_voff, int a_chunk_stride,
     int w, int lane, int nks, int nlive,
     int valid, int ct, bool ct_ok, int64_t row_base, int64_t mt_glob, int Nout,
@@ -353,10 +377,26 @@ __device__ __forceinline__ void frag_gemm_body(
     }
     asm volatile("" ::: "memory");
   };
+  WFrag<F8> bq[kPrefetch][kFrags];
   // weights read exactly once stream past the caches (non-temporal)
-  auto load_w = [&](int idx) -> u32x4_t {
+  auto load_w = [&](int idx) -> WFrag<F8> {
     if (NT) return __builtin_nontemporal_load(&wp[idx]);
     return wp[idx];
+  };
+  // FP8: the tile scales of K-step kidx (128 K-columns = 4 steps per tile);
+  // for w13 fragments 0, 1 are gate rows (sc_g), 2, 3 up rows (sc_u)
+  float bsg[kPrefetch], bsu[kPrefetch];
+  auto load_scales = [&](int s, int kidx) {
+    if (F8) {
+      bsg[s] = sc_g[kidx >> 2];
+      bsu[s] = sc_u[kidx >> 2];
+    }
+  };
+  auto bfrag = [&](int s, int f) -> bf16x8_t {
+    if constexpr (F8)
+      return dequant8(bq[s][f], f >= 2 ? bsu[s] : bsg[s]);
+    else
+      return __builtin_bit_cast(bf16x8_t, bq[s][f]);
   };
 
   f32x4_t acc[kMsub][kFrags];
@@ -368,11 +408,12 @@ __device__ __forceinline__ void frag_gemm_body(
   const int nchunks = nks / kChunkSteps;
 #pragma unroll
   for (int c = 0; c < kStages - 1; ++c) issue_chunk(min(c, nchunks - 1), c);
-  u32x4_t bq[kPrefetch][kFrags];
 #pragma unroll
-  for (int s = 0; s < kPrefetch; ++s)
+  for (int s = 0; s < kPrefetch; ++s) {
 #pragma unroll
     for (int f = 0; f < kFrags; ++f) bq[s][f] = load_w(wrap(s + krot, nks) * kstride + f * kWave);
+    load_scales(s, wrap(s + krot, nks));
+  }
   asm volatile("" ::: "memory");
 
   // Loads complete in issue order, so waiting until at most n are
@@ -402,6 +443,9 @@ __device__ __forceinline__ void frag_gemm_body(
         issue_chunk(min(chunk + kStages - 1, nchunks - 1), ahead);
       }
       const int sub = ks % kChunkSteps;
+      bf16x8_t bfr[kFrags];
+#pragma unroll
+      for (int f = 0; f < kFrags; ++f) bfr[f] = bfrag(s, f);
       // all of the step's activation fragments are read before the MFMAs
       // (in two halves, so a segment of at most 64 rows reads only the
       // first): one LDS latency per step instead of one per m-subtile
@@ -418,8 +462,7 @@ __device__ __forceinline__ void frag_gemm_body(
         const bf16x8_t af = __builtin_bit_cast(bf16x8_t, a[i]);
 #pragma unroll
         for (int f = 0; f < kFrags; ++f)
-          acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              af, __builtin_bit_cast(bf16x8_t, bq[s][f]), acc[i][f], 0, 0, 0);
+          acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[f], acc[i][f], 0, 0, 0);
       }
       // refill this slot kPrefetch steps ahead (past the end: the last step
       // again, which keeps the outstanding-load count constant)
@@ -427,6 +470,7 @@ __device__ __forceinline__ void frag_gemm_body(
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int f = 0; f < kFrags; ++f) bq[s][f] = load_w(wrap(nxt + krot, nks) * kstride + f * kWave);
+      load_scales(s, wrap(nxt + krot, nks));
       asm volatile("" ::: "memory");
     }
   }
@@ -469,9 +513,9 @@ __device__ __forceinline__ void frag_gemm_body(
 
 // Two waves per SIMD: an 8-wave workgroup needs them, a 4-wave one gets two
 // workgroups per CU; the register budget is 256 per lane either way.
-template <bool GATE_UP, int NW>
+template <bool GATE_UP, int NW, bool F8>
 __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Wf,
+    const uint16_t* __restrict__ A, const void* __restrict__ Wf, const float* __restrict__ Wsc,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ counts, int G,
     int Kdim, int Nw /* weight rows per group */, int Nout, const float* __restrict__ row_scale,
     uint16_t* __restrict__ Out, int64_t capacity, int32_t* __restrict__ dev_error) {
@@ -508,10 +552,21 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
   const int nks = Kdim / 32;
 
   // this wave's weight stream: step ks, fragment f at wp[ks * kstride + f * 64]
-  // (16-byte units)
+  // (in fragment-lane units: 16 bytes of bf16 or 8 FP8 codes)
   const int kstride = n_ct * kFrags * kWave;
-  const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(Wf) +
-                      ((int64_t)g * nks * n_ct + ct) * (kFrags * kWave) + lane;
+  const WFrag<F8>* wp = reinterpret_cast<const WFrag<F8>*>(Wf) +
+                        ((int64_t)g * nks * n_ct + ct) * (kFrags * kWave) + lane;
+  // FP8: the scale rows ([G][Nw/128][Kdim/128]) of this tile's gate and up
+  // rows (w13: gate rows 32 ct.., up rows Nw/2 + 32 ct..; w2: rows 64 ct..)
+  const int nkb = Kdim / 128, nrb = Nw / 128;
+  const float* sc_g = nullptr;
+  const float* sc_u = nullptr;
+  if (F8) {
+    const int rb_g = GATE_UP ? (32 * ct) / 128 : (64 * ct) / 128;
+    const int rb_u = GATE_UP ? (Nw / 2 + 32 * ct) / 128 : rb_g;
+    sc_g = Wsc + ((int64_t)g * nrb + rb_g) * nkb;
+    sc_u = Wsc + ((int64_t)g * nrb + rb_u) * nkb;
+  }
   // the activation DMA: this wave fills LDS blocks kDmaPerWave*w .. of a
   // stage; block b is m-subtile b / kChunkSteps, K-step b % kChunkSteps
   constexpr int kDmaPerWave = kStageBlocks / NW;
@@ -560,10 +615,10 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
   const uint32_t rkey = NW == 8 ? (uint32_t)g * 977u : (uint32_t)g * 977u + (uint32_t)cb;
   const int crot = once ? (int)((rkey * 2654435761u) >> 8) % (nks / kChunkSteps) : 0;
   if (once)
-    frag_gemm_body<GATE_UP, true, NW>(As, wp, kstride, a_base, a_uoff, a_voff, a_chunk_stride, w, lane, nks, nlive, valid,
+    frag_gemm_body<GATE_UP, true, NW, F8>(As, wp, kstride, sc_g, sc_u, a_base, a_uoff, a_voff, a_chunk_stride, w, lane, nks, nlive, valid,
                                       ct, ct_ok, row_base, mt_glob, Nout, tile_scale, Out, crot);
   else
-    frag_gemm_body<GATE_UP, false, NW>(As, wp, kstride, a_base, a_uoff, a_voff, a_chunk_stride, w, lane, nks, nlive, valid,
+    frag_gemm_body<GATE_UP, false, NW, F8>(As, wp, kstride, sc_g, sc_u, a_base, a_uoff, a_voff, a_chunk_stride, w, lane, nks, nlive, valid,
                                        ct, ct_ok, row_base, mt_glob, Nout, tile_scale, Out, crot);
 }
 
@@ -599,6 +654,96 @@ __global__ void __launch_bounds__(256) pack_weights_kernel(const uint16_t* __res
   }
 }
 
+// FP8 weights: one workgroup per 128 x 128 tile of one group's [N, Kdim]
+// matrix.  The tile's amax gives its scale s = amax / 448 (IEEE division;
+// an all-zero tile gets s = 0 and codes 0); every element becomes the E4M3
+// code of clamp(w / s, +-448) (round to nearest even), written in the same
+// fragment order as the bf16 packing with 8 codes (8 bytes) per lane.
+__global__ void __launch_bounds__(256) pack_weights_fp8_kernel(const uint16_t* __restrict__ W,
+                                                               uint8_t* __restrict__ Q,
+                                                               float* __restrict__ S, int N,
+                                                               int Kdim, int gate_up) {
+  const int nrb = N / 128, nkb = Kdim / 128;
+  const int64_t tile = blockIdx.x;
+  const int kb = (int)(tile % nkb);
+  const int rb = (int)((tile / nkb) % nrb);
+  const int64_t g = tile / ((int64_t)nkb * nrb);
+  const int c = threadIdx.x & 15;  // 16-byte vector of the tile row
+  const int r0 = threadIdx.x >> 4;  // rows r0, r0 + 16, ...
+  const int kvec = Kdim / 8;
+  uint4 raw[8];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = (int64_t)g * N + rb * 128 + r0 + 16 * i;
+    raw[i] = reinterpret_cast<const uint4*>(W)[row * kvec + kb * 16 + c];
+    float f[8];
+    unpack8(raw[i], f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(f[j]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float s = amax / 448.0f;
+  if (threadIdx.x == 0) S[((int64_t)g * nrb + rb) * nkb + kb] = s;
+  const int nks = Kdim / 32, n_ct = N / 64;
+  const int k8 = kb * 16 + c;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float f[8];
+    unpack8(raw[i], f);
+    uint32_t code[2] = {0u, 0u};
+    if (s > 0.0f) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float q[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q[j] = fminf(fmaxf(f[4 * h + j] / s, -448.0f), 448.0f);
+        int p = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+        p = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], p, true);
+        code[h] = (uint32_t)p;
+      }
+    }
+    const int row = rb * 128 + r0 + 16 * i;
+    int ct, f_;
+    if (gate_up) {
+      const int half = N / 2;
+      const int r = row < half ? row : row - half;
+      ct = r / 32;
+      f_ = (row < half ? 0 : 2) + (r % 32) / 16;
+    } else {
+      ct = row / 64;
+      f_ = (row % 64) / 16;
+    }
+    const int ks = k8 / 4;
+    const int lane = (row & 15) + 16 * (k8 & 3);
+    const int64_t dst = (((g * nks + ks) * n_ct + ct) * kFrags + f_) * kWave + lane;
+    reinterpret_cast<uint2*>(Q)[dst] = make_uint2(code[0], code[1]);
+  }
+}
+
+int launch_pack_weights_fp8(const uint16_t* w13, const uint16_t* w2, int G, int H, int I,
+                            uint8_t* w13q, float* w13s, uint8_t* w2q, float* w2s,
+                            hipStream_t stream) {
+  if (w13) {
+    const int64_t tiles = (int64_t)G * (2 * I / 128) * (H / 128);
+    if (tiles > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(pack_weights_fp8_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, w13,
+                       w13q, w13s, 2 * I, H, 1);
+  }
+  if (w2) {
+    const int64_t tiles = (int64_t)G * (H / 128) * (I / 128);
+    if (tiles > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(pack_weights_fp8_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, w2,
+                       w2q, w2s, H, I, 0);
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 int launch_pack_weights(const uint16_t* w13, const uint16_t* w2, int G, int H, int I,
                         uint16_t* w13p, uint16_t* w2p, hipStream_t stream) {
   if (w13 && w13p) {
@@ -624,11 +769,12 @@ size_t grouped_ffn_workspace_bytes(int64_t capacity, int G, int I) {
 }
 
 int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32_t* counts, int G,
-                       int H, int I, const uint16_t* w13, const uint16_t* w2,
-                       const float* row_scale, uint16_t* y, int64_t capacity, int flags,
-                       void* workspace, int32_t* dev_error, hipStream_t stream) {
+                       int H, int I, const void* w13, const float* w13s, const void* w2,
+                       const float* w2s, const float* row_scale, uint16_t* y, int64_t capacity,
+                       int flags, void* workspace, int32_t* dev_error, hipStream_t stream) {
   uint16_t* act = static_cast<uint16_t*>(workspace);
-  const bool packed = (flags & MOE_FFN_PACKED_WEIGHTS) != 0;
+  const bool f8 = w13s != nullptr || w2s != nullptr;  // FP8 weights are always packed
+  const bool packed = f8 || (flags & MOE_FFN_PACKED_WEIGHTS) != 0;
   const int64_t m_tiles = (capacity + kBM - 1) / kBM + G;
   const int64_t grid_unit = (int64_t)kNumXcd * kXcdChunk;
   auto grid_for = [&](int64_t n_tiles) {
@@ -648,19 +794,21 @@ int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32
       const int nw = wide ? 8 : 4;
       const int64_t blocks = grid_for((2 * I / 64 + nw - 1) / nw);
       if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-      if (wide)
-        hipLaunchKernelGGL((frag_gemm_kernel<true, 8>), dim3((unsigned)blocks), dim3(8 * kWave), 0,
-                           stream, x, w13, cu_seqlens, counts, G, H, 2 * I, I, nullptr, act,
-                           capacity, dev_error);
-      else
-        hipLaunchKernelGGL((frag_gemm_kernel<true, 4>), dim3((unsigned)blocks), dim3(4 * kWave), 0,
-                           stream, x, w13, cu_seqlens, counts, G, H, 2 * I, I, nullptr, act,
-                           capacity, dev_error);
+#define MOE_FRAG_GU(NW, F8)                                                                  \
+  hipLaunchKernelGGL((frag_gemm_kernel<true, NW, F8>), dim3((unsigned)blocks), dim3(NW * kWave), \
+                     0, stream, x, w13, w13s, cu_seqlens, counts, G, H, 2 * I, I, nullptr, act,  \
+                     capacity, dev_error)
+      if (f8) {
+        if (wide) MOE_FRAG_GU(8, true); else MOE_FRAG_GU(4, true);
+      } else {
+        if (wide) MOE_FRAG_GU(8, false); else MOE_FRAG_GU(4, false);
+      }
+#undef MOE_FRAG_GU
     } else {
       const int64_t blocks = grid_for(I / (kBN / 2));
       if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
       hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                         stream, x, w13, cu_seqlens, counts, G, H, 2 * I, I, nullptr, act,
+                         stream, x, static_cast<const uint16_t*>(w13), cu_seqlens, counts, G, H, 2 * I, I, nullptr, act,
                          capacity, dev_error);
     }
   }
@@ -669,19 +817,22 @@ int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32
       const int nw = wide_down ? 8 : 4;
       const int64_t blocks = grid_for((H / 64 + nw - 1) / nw);
       if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-      if (wide_down)
-        hipLaunchKernelGGL((frag_gemm_kernel<false, 8>), dim3((unsigned)blocks), dim3(8 * kWave),
-                           0, stream, act, w2, cu_seqlens, counts, G, I, H, H, row_scale, y,
-                           capacity, dev_error);
-      else
-        hipLaunchKernelGGL((frag_gemm_kernel<false, 4>), dim3((unsigned)blocks), dim3(4 * kWave),
-                           0, stream, act, w2, cu_seqlens, counts, G, I, H, H, row_scale, y,
-                           capacity, dev_error);
+#define MOE_FRAG_DN(NW, F8)                                                                   \
+  hipLaunchKernelGGL((frag_gemm_kernel<false, NW, F8>), dim3((unsigned)blocks), dim3(NW * kWave), \
+                     0, stream, act, w2, w2s, cu_seqlens, counts, G, I, H, H, row_scale, y,       \
+                     capacity, dev_error)
+      if (f8) {
+        if (wide_down) MOE_FRAG_DN(8, true); else MOE_FRAG_DN(4, true);
+      } else {
+        if (wide_down) MOE_FRAG_DN(8, false); else MOE_FRAG_DN(4, false);
+      }
+#undef MOE_FRAG_DN
     } else {
       const int64_t blocks = grid_for(H / kBN);
       if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
       hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                         stream, act, w2, cu_seqlens, counts, G, I, H, H, row_scale, y, capacity,
+                         stream, act, static_cast<const uint16_t*>(w2), cu_seqlens, counts, G, I,
+                         H, H, row_scale, y, capacity,
                          dev_error);
     }
   }

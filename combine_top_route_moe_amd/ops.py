@@ -177,6 +177,71 @@ def moe_pack_ffn_weights(w13: Optional[torch.Tensor], w2: Optional[torch.Tensor]
     return w13_packed, w2_packed
 
 
+def moe_grouped_ffn_fp8(x: torch.Tensor, cu_seqlens: torch.Tensor, counts: torch.Tensor,
+                        w13q: torch.Tensor, w13_scales: torch.Tensor, w2q: torch.Tensor,
+                        w2_scales: torch.Tensor, row_scale: Optional[torch.Tensor] = None,
+                        y: Optional[torch.Tensor] = None, flags: int = MOE_FFN_ALL,
+                        workspace: Optional[torch.Tensor] = None,
+                        dev_error: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The grouped FFN with FP8 weights from moe_pack_ffn_weights_fp8 (codes
+    uint8 [G,2I,H] / [G,H,I] in packed order, tile scales float32)."""
+    _want(x, torch.bfloat16, "x")
+    _want(w13q, torch.uint8, "w13q")
+    _want(w2q, torch.uint8, "w2q")
+    _want(w13_scales, torch.float32, "w13_scales")
+    _want(w2_scales, torch.float32, "w2_scales")
+    _want(cu_seqlens, torch.int32, "cu_seqlens")
+    _want(counts, torch.int32, "counts")
+    if row_scale is not None:
+        _want(row_scale, torch.float32, "row_scale")
+    capacity, H = x.shape
+    G, two_i, H2 = w13q.shape
+    I = two_i // 2
+    if H2 != H or tuple(w2q.shape) != (G, H, I):
+        raise ValueError("weight shapes do not match x")
+    if (tuple(w13_scales.shape) != (G, two_i // 128, H // 128)
+            or tuple(w2_scales.shape) != (G, H // 128, I // 128)):
+        raise ValueError("scale shapes do not match the weights")
+    if counts.numel() != G or cu_seqlens.numel() != G + 1:
+        raise ValueError("counts / cu_seqlens do not match the number of groups")
+    lib = load()
+    y = torch.empty(capacity, H, dtype=torch.bfloat16, device=x.device) if y is None else y
+    need = lib.moe_grouped_ffn_workspace_bytes(capacity, G, H, I)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    check("moe_grouped_ffn_fp8", lib.moe_grouped_ffn_fp8(
+        _ptr(x), _ptr(cu_seqlens), _ptr(counts), G, H, I, _ptr(w13q), _ptr(w13_scales),
+        _ptr(w2q), _ptr(w2_scales), _ptr(row_scale), _ptr(y), capacity, flags, _ptr(workspace),
+        workspace.numel(), _ptr(dev_error), _stream(stream)))
+    return y
+
+
+def moe_pack_ffn_weights_fp8(w13: Optional[torch.Tensor], w2: Optional[torch.Tensor],
+                             stream=None):
+    """Quantize w13 [G,2I,H] / w2 [G,H,I] to E4M3 with one float32 scale per
+    128 x 128 tile, codes in the grouped GEMM's packed order.  Returns
+    ``(w13q, w13_scales, w2q, w2_scales)`` (None for an absent input)."""
+    if w13 is not None:
+        _want(w13, torch.bfloat16, "w13")
+        G, two_i, H = w13.shape
+        I = two_i // 2
+    else:
+        _want(w2, torch.bfloat16, "w2")
+        G, H, I = w2.shape
+    dev = (w13 if w13 is not None else w2).device
+    w13q = w13s = w2q = w2s = None
+    if w13 is not None:
+        w13q = torch.empty(G, 2 * I, H, dtype=torch.uint8, device=dev)
+        w13s = torch.empty(G, 2 * I // 128, H // 128, dtype=torch.float32, device=dev)
+    if w2 is not None:
+        w2q = torch.empty(G, H, I, dtype=torch.uint8, device=dev)
+        w2s = torch.empty(G, H // 128, I // 128, dtype=torch.float32, device=dev)
+    check("moe_pack_ffn_weights_fp8", load().moe_pack_ffn_weights_fp8(
+        _ptr(w13), _ptr(w2), G, H, I, _ptr(w13q), _ptr(w13s), _ptr(w2q), _ptr(w2s),
+        _stream(stream)))
+    return w13q, w13s, w2q, w2s
+
+
 def moe_fake_quant_rows(inp: torch.Tensor, out: Optional[torch.Tensor] = None,
                         row_src: Optional[torch.Tensor] = None, mode: int = MOE_FQ_BLOCK,
                         block: int = 128, scale: Optional[torch.Tensor] = None,

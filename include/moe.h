@@ -189,6 +189,39 @@ int moe_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32_t*
 int moe_pack_ffn_weights(const uint16_t* w13, const uint16_t* w2, int num_groups, int H, int I,
                          uint16_t* w13_packed, uint16_t* w2_packed, void* stream);
 
+/* ---- FP8 expert weights (the weight half of the FP8 grouped GEMM) -------
+ * [P2] review thread on the DeepEP + DeepGEMM test (FP8 expert weights with
+ * one scale per block_n x block_k tile; here 128 x 128, the size of the
+ * activation blocks): each 128 x 128 tile of w13[g] [2I, H]
+ * and w2[g] [H, I] gets s = fl32(amax / 448) (0 for an all-zero tile) and
+ * every element the OCP E4M3FN code of clamp(fl32(w / s), +-448), rounded to
+ * nearest even (code 0 where s = 0).
+ *   w13q [G, 2I, H] / w2q [G, H, I] uint8 (out): one code per weight, in the
+ *     packed order of moe_pack_ffn_weights with 8 codes (8 bytes) per lane
+ *     where the bf16 packing holds 8 values (16 bytes): unit index
+ *     ((g * (Kdim/32) + ks) * n_ct + ct) * 256 + f * 64 + l, 8 bytes each.
+ *   w13_scales [G, 2I/128, H/128], w2_scales [G, H/128, I/128] float32 (out),
+ *     tile (row block, column block) row-major per group.
+ * Either group of three (w13, w13q, w13_scales) / (w2, ...) may be all NULL.
+ * Pointers 16-byte aligned.  Runs once at load time.
+ * Requires H % 128 == 0, I % 128 == 0. */
+int moe_pack_ffn_weights_fp8(const uint16_t* w13, const uint16_t* w2, int num_groups, int H,
+                             int I, uint8_t* w13q, float* w13_scales, uint8_t* w2q,
+                             float* w2_scales, void* stream);
+
+/* moe_grouped_ffn with the FP8 weights above: the same operation, segments,
+ * flags (stage bits only; the weights are always the packed FP8 ones),
+ * workspace and errors, where every weight the matmuls read is the
+ * dequantized bf16( fl32(code * s) ) of its tile — exactly
+ * moe_grouped_ffn on the FP8 fake-quantized bf16 weights.  Activations stay
+ * bf16; half the weight bytes are read.  The stage(s) selected need their
+ * codes and scales (others may be NULL). */
+int moe_grouped_ffn_fp8(const uint16_t* x, const int32_t* cu_seqlens, const int32_t* counts,
+                        int num_groups, int H, int I, const uint8_t* w13q, const float* w13_scales,
+                        const uint8_t* w2q, const float* w2_scales, const float* row_scale,
+                        uint16_t* y, int64_t capacity, int flags, void* workspace,
+                        size_t workspace_bytes, int32_t* dev_error, void* stream);
+
 /* ---- FP8 and FP4 fake-quant of bf16 rows -------------------------------
  * QDQ to OCP E4M3FN and back ([P1] PR summary and "How it works": the
  * dispatch quantizer fake-quantizes the experts' input tokens, the combine

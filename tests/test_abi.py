@@ -49,5 +49,12 @@ def test_host_only_entry_points():
     assert lib.moe_route(None, None, 4, 2048, 2, 1, None, None, None) == -2     # E > 1024
     assert lib.moe_grouped_ffn(None, None, None, 4, 100, 128, None, None, None, None, 16, 3,
                                None, 0, None, None) == -2                       # H % 128
+    # FP8 weights: a selected stage needs its codes and its scales
+    assert lib.moe_grouped_ffn_fp8(None, None, None, 4, 256, 128, None, None, None, None, None,
+                                   None, 16, 3, None, 0, None, None) == -1
+    assert lib.moe_grouped_ffn_fp8(None, None, None, 4, 256, 128, None, None, None, None, None,
+                                   None, 16, 3 | 4, None, 0, None, None) == -1   # stage bits only
+    assert lib.moe_pack_ffn_weights_fp8(None, None, 4, 256, 100, None, None, None, None,
+                                        None) == -2                              # I % 128
     assert lib.moe_combine(None, 0, None, None, 0, 1, 128, None, None, None, None) == 0  # T = 0
     assert lib.moe_copy_bytes(None, None, 15, None) == -1

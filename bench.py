@@ -31,10 +31,11 @@ PEAK_BF16_TFLOPS = 2500.0       # MI355X dense BF16 MFMA, published
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def algorithmic(cfg, counts: np.ndarray) -> dict:
+def algorithmic(cfg, counts: np.ndarray, fp8_weights: bool = False) -> dict:
     """Bytes (and FLOPs) each stage must move (compute) at minimum: every
     input read once, every output written once, padding rows and re-reads
-    not counted."""
+    not counted.  FP8 weights: one byte per weight plus a float32 scale per
+    128 x 128 tile."""
     T, H, E, K, I = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I
     Tv = cfg.T_valid
     N = int(counts.sum())
@@ -44,13 +45,15 @@ def algorithmic(cfg, counts: np.ndarray) -> dict:
     if cfg.dispatch_block:
         st["dispatch_qdq"] = dict(bytes=4 * Tv * H)
     st["permute"] = dict(bytes=8 * T * K + 2 * Tv * H + 2 * N * H + 4 * T * K + 8 * N + 8 * E)
-    st["ffn_gate_up"] = dict(bytes=2 * 2 * E_act * I * H + 2 * N * H + 2 * N * I,
+    wb = 1 + 4 / (128 * 128) if fp8_weights else 2      # bytes per weight
+    st["ffn_gate_up"] = dict(bytes=int(wb * 2 * E_act * I * H) + 2 * N * H + 2 * N * I,
                              flops=4 * N * I * H)
-    st["ffn_down"] = dict(bytes=2 * E_act * I * H + 2 * N * I + 2 * N * H + 4 * N,
+    st["ffn_down"] = dict(bytes=int(wb * E_act * I * H) + 2 * N * I + 2 * N * H + 4 * N,
                           flops=2 * N * I * H)
     if cfg.shared_I:
         Is = cfg.shared_I
-        st["shared_ffn"] = dict(bytes=6 * Is * H + 2 * T * H + 2 * T * H, flops=6 * T * Is * H)
+        st["shared_ffn"] = dict(bytes=int(wb * 3 * Is * H) + 2 * T * H + 2 * T * H,
+                                flops=6 * T * Is * H)
     st["combine"] = dict(bytes=2 * N * H + 4 * T * K + 2 * T * H + (2 * T * H if cfg.shared_I else 0))
     return st
 
@@ -73,7 +76,9 @@ def kernel_source_hash(stage: str) -> str:
 
 def committed_traffic(stage: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
-    taken on the kernel as it is now (same source hash); else None."""
+    taken on the kernel as it is now (same source hash); else None.
+    ``workload`` names the summary (the workload, plus "_fp8w" for FP8
+    weights)."""
     path = os.path.join(PROFILES, f"hbm_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -84,8 +89,11 @@ def committed_traffic(stage: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, logits, hidden, row_valid, budget_s: float):
-    """Time the oracle layer (as it stands) on a bounded sample of tokens."""
+def cpu_baseline(cfg, logits, hidden, row_valid, budget_s: float, fp8_weights: bool = False):
+    """Time the oracle layer (as it stands) on a bounded sample of tokens.
+    With FP8 weights the oracle's weight quantization runs once per expert
+    before timing (like weight generation): the timed layer is the oracle
+    on the dequantized weights, which is what its FP8-weight mode computes."""
     import oracle
     import workloads
 
@@ -101,12 +109,19 @@ def cpu_baseline(cfg, logits, hidden, row_valid, budget_s: float):
     # probe with a small sample, then scale
     weights_cache = {}
 
+    def prep(ws):
+        if not fp8_weights:
+            return ws
+        return tuple(oracle.quantize_weight_blocks(w)[2] for w in ws)
+
     def weights(e):
         if e not in weights_cache:
-            weights_cache[e] = workloads.expert_weights(cfg, e)
+            weights_cache[e] = prep(workloads.expert_weights(cfg, e))
         return weights_cache[e]
 
     shared = workloads.shared_weights(cfg)
+    if shared is not None:
+        shared = prep(shared)
 
     def run(n):
         rv = None if row_valid is None else row_valid[:n]
@@ -133,7 +148,8 @@ def cpu_baseline(cfg, logits, hidden, row_valid, budget_s: float):
     tv = n if row_valid is None else int(row_valid[:n].sum())
     return {"value": tv / dt, "unit": "routed tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {n} of {cfg.T} tokens of the {cfg.name} batch ({tv} routed), "
-                      f"whole layer, float64 numpy, median of {len(times)} runs: {dt:.2f} s"}
+                      f"whole layer, float64 numpy, median of {len(times)} runs: {dt:.2f} s"
+                      + ("; FP8 weights dequantized once before timing" if fp8_weights else "")}
 
 
 def calibrate_spin(stream, target_ms: float = 1.0) -> int:
@@ -186,6 +202,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true",
                     help="time the steps as eager launches instead of HIP-graph replays")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
+    ap.add_argument("--fp8-weights", action="store_true",
+                    help="expert weights as E4M3 codes with 128x128 tile scales, dequantized "
+                         "in registers before the BF16 MFMAs (activations stay bf16)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the reference copy kernel (1 GiB -> 1 GiB) and report its "
                          "bandwidth; its byte counters scale the PMC traffic figures")
@@ -231,7 +250,10 @@ def main():
 
     workloads.for_each_expert(cfg, put)
     sw = workloads.shared_weights(cfg)
-    layer.set_weights(w13, w2, *(bf16(x) for x in sw) if sw else (None, None))
+    layer.set_weights(w13, w2, *(bf16(x) for x in sw) if sw else (None, None),
+                      fp8=args.fp8_weights)
+    if args.fp8_weights:
+        del w13, w2                   # only the packed FP8 codes stay resident
     if cfg.combine_qdq:
         layer.calibrate_combine_scale(logits, hidden, row_valid)
     torch.cuda.synchronize()
@@ -291,7 +313,7 @@ def main():
     assert layer.dev_error.item() == 0, "device error word set during the stage timing"
 
     counts = layer.perm.counts.cpu().numpy()
-    alg = algorithmic(cfg, counts)
+    alg = algorithmic(cfg, counts, args.fp8_weights)
     stages = {}
     for name, ms in stage_ms.items():
         a = alg.get(name, {})
@@ -319,7 +341,7 @@ def main():
     roof["kernel"] = {"ffn_gate_up": "frag_gemm_kernel<true>",
                       "ffn_down": "frag_gemm_kernel<false>"}.get(dom, dom)
     roof["alg_bytes_per_launch"] = a["bytes"]
-    roof["traffic"] = committed_traffic(dom, cfg.name)
+    roof["traffic"] = committed_traffic(dom, cfg.name + ("_fp8w" if args.fp8_weights else ""))
 
     ms_step = elapsed / args.steps * 1e3
     gemm_flops = alg["ffn_gate_up"]["flops"] + alg["ffn_down"]["flops"]
@@ -341,6 +363,8 @@ def main():
                    "E": cfg.E, "K": cfg.K, "I": cfg.I, "shared_I": cfg.shared_I,
                    "routed_rows": int(counts.sum()), "dispatch_fp8_block": cfg.dispatch_block,
                    "combine_fp8": cfg.combine_qdq, "pad_pow2": cfg.pad_pow2,
+                   "expert_weights": ("fp8 e4m3, 128x128 tile scales" if args.fp8_weights
+                                      else "bf16"),
                    "parallelism": "single GPU (all experts local)"},
         "grouped_gemm_mfma_util": round(gemm_flops / (gemm_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
         "permute_GBps": stages["permute"]["GBps"],
@@ -356,7 +380,8 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, logits_h, hidden_h, valid_h, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(cfg, logits_h, hidden_h, valid_h, args.cpu_budget,
+                                              args.fp8_weights)
     print(json.dumps(result), flush=True)
 
 

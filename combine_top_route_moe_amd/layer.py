@@ -88,19 +88,34 @@ class MoELayer:
             self.shared_out = None
         self.w13 = self.w2 = self.shared_w13 = self.shared_w2 = None
         self.packed = False
+        self.fp8_weights = False
 
     # ------------------------------------------------------------------ weights
     def set_weights(self, w13: torch.Tensor, w2: torch.Tensor,
                     shared_w13: Optional[torch.Tensor] = None,
-                    shared_w2: Optional[torch.Tensor] = None, pack: bool = True) -> None:
+                    shared_w2: Optional[torch.Tensor] = None, pack: bool = True,
+                    fp8: bool = False) -> None:
         """Device bf16 weights: w13 [E_l, 2I, H], w2 [E_l, H, I] (local experts);
         the shared expert's [2Is, H] and [H, Is] (run as a single group).
 
         With ``pack`` (the default) the weights are copied once into the
         grouped GEMM's packed layout (``moe_pack_ffn_weights``) and the
-        row-major tensors are not referenced afterwards."""
+        row-major tensors are not referenced afterwards.  With ``fp8`` they
+        are quantized once instead to E4M3 codes with 128 x 128 tile scales
+        (``moe_pack_ffn_weights_fp8``), routed and shared experts alike, and
+        the FFN stages read those (``moe_grouped_ffn_fp8``)."""
         if shared_w13 is not None and shared_w13.dim() == 2:
             shared_w13, shared_w2 = shared_w13.unsqueeze(0), shared_w2.unsqueeze(0)
+        self.fp8_weights = fp8
+        if fp8:
+            self.packed = True
+            q13, s13, q2, s2 = ops.moe_pack_ffn_weights_fp8(w13, w2)
+            self.w13, self.w2 = (q13, s13), (q2, s2)
+            self.shared_w13 = self.shared_w2 = None
+            if shared_w13 is not None:
+                q13, s13, q2, s2 = ops.moe_pack_ffn_weights_fp8(shared_w13, shared_w2)
+                self.shared_w13, self.shared_w2 = (q13, s13), (q2, s2)
+            return
         self.packed = pack
         if pack:
             w13, w2 = ops.moe_pack_ffn_weights(w13, w2)
@@ -108,6 +123,16 @@ class MoELayer:
                 shared_w13, shared_w2 = ops.moe_pack_ffn_weights(shared_w13, shared_w2)
         self.w13, self.w2 = w13, w2
         self.shared_w13, self.shared_w2 = shared_w13, shared_w2
+
+    def _ffn(self, x, cu, counts, w13, w2, row_scale, y, stage, ws, stream=None) -> None:
+        """One grouped-FFN call on the weights ``set_weights`` prepared."""
+        if self.fp8_weights:
+            ops.moe_grouped_ffn_fp8(x, cu, counts, w13[0], w13[1], w2[0], w2[1], row_scale, y,
+                                    stage, ws, self.dev_error, stream=stream)
+        else:
+            layout = ops.MOE_FFN_PACKED_WEIGHTS if self.packed else 0
+            ops.moe_grouped_ffn(x, cu, counts, w13, w2, row_scale, y, stage | layout, ws,
+                                self.dev_error, stream=stream)
 
     # ------------------------------------------------------------------ stages
     def stages(self, logits: torch.Tensor, hidden: torch.Tensor,
@@ -121,7 +146,6 @@ class MoELayer:
         the combine (the form ``forward`` uses; a graph capture of it holds
         the two branches)."""
         p = self.perm
-        layout = ops.MOE_FFN_PACKED_WEIGHTS if self.packed else 0
         x = self.hidden_q if self.hidden_q is not None else hidden
         st = [("route", lambda: ops.moe_route(logits, self.K, row_valid, self.renormalize,
                                                self.topk_idx, self.topk_w))]
@@ -135,12 +159,12 @@ class MoELayer:
         st.append(("permute", lambda: ops.moe_permute(
             self.topk_idx, self.topk_w, x, self.El, self.expert_begin, self.pad_pow2,
             self.capacity, p, self.perm_ws, self.dev_error)))
-        st.append(("ffn_gate_up", lambda: ops.moe_grouped_ffn(
+        st.append(("ffn_gate_up", lambda: self._ffn(
             p.x_perm, p.cu_seqlens, p.counts, self.w13, self.w2, p.w_perm, self.y_perm,
-            ops.MOE_FFN_GATE_UP | layout, self.ffn_ws, self.dev_error)))
-        st.append(("ffn_down", lambda: ops.moe_grouped_ffn(
+            ops.MOE_FFN_GATE_UP, self.ffn_ws)))
+        st.append(("ffn_down", lambda: self._ffn(
             p.x_perm, p.cu_seqlens, p.counts, self.w13, self.w2, p.w_perm, self.y_perm,
-            ops.MOE_FFN_DOWN | layout, self.ffn_ws, self.dev_error)))
+            ops.MOE_FFN_DOWN, self.ffn_ws)))
         if self.combine_fp4:
             # FP4 combine rows: the routed rows quantized in place (padding
             # rows skipped through src_of), then a plain combine
@@ -149,10 +173,9 @@ class MoELayer:
                 self.y_perm, self.y_perm, p.src_of, cmode, cblock, self.combine_scale)))
         if self.shared_I:
             def shared(stream=None):
-                ops.moe_grouped_ffn(hidden, self.shared_cu, self.shared_counts, self.shared_w13,
-                                    self.shared_w2, None, self.shared_out,
-                                    ops.MOE_FFN_ALL | layout, self.shared_ws, self.dev_error,
-                                    stream=stream)
+                self._ffn(hidden, self.shared_cu, self.shared_counts, self.shared_w13,
+                          self.shared_w2, None, self.shared_out, ops.MOE_FFN_ALL,
+                          self.shared_ws, stream=stream)
 
             if overlap_shared:
                 def fork():

@@ -19,14 +19,18 @@ Readings where the pages are silent:
   dispatch quantization and a fused shared expert apart, so no config has
   both) and its output is a BF16 row with weight 1, added for every token;
 * combine-row quantization covers routed rows only; with no scale given it
-  is calibrated from this batch's own rows (max calibration).
+  is calibrated from this batch's own rows (max calibration);
+* FP8 expert weights (128 x 128 tile scales, the "DeepEP + DeepGEMM" review
+  thread) enter the FFN as their dequantized values, for the routed and the
+  shared experts alike.
 """
 
 import numpy as np
 
 from .numerics import bf16_bits_to_f64, f32_to_bf16_bits
 from .route import route
-from .quant import fake_quant_block, fake_quant_per_tensor, calibrate_amax, scale_from_amax
+from .quant import (fake_quant_block, fake_quant_per_tensor, calibrate_amax, scale_from_amax,
+                    quantize_weight_blocks)
 from .fp4 import fake_quant_mxfp4, fake_quant_nvfp4, nvfp4_tensor_scale
 from .permute import permute
 from .ffn import grouped_ffn, expert_ffn
@@ -47,7 +51,7 @@ def moe_layer(logits, hidden_bits, weights, k: int, row_valid=None,
               renormalize: bool = True, dispatch_block=None, pad_pow2=False,
               shared_weights=None, combine_qdq: bool = False, combine_scale=None,
               expert_begin: int = 0, num_local_experts=None, dispatch_fp4=None,
-              dispatch_scale=None, combine_fp4=None):
+              dispatch_scale=None, combine_fp4=None, fp8_weights: bool = False):
     """Run the oracle layer and return every intermediate in a dict.
 
     ``weights(e)`` returns expert ``e``'s ``(w13, w2)`` as bfloat16 bits
@@ -56,7 +60,17 @@ def moe_layer(logits, hidden_bits, weights, k: int, row_valid=None,
     quantizers instead of the FP8 ones; an NVFP4 tensor scale not given
     (``dispatch_scale``, ``combine_scale``) is calibrated like the FP8
     combine scale: ``amax / (6 * 448)`` over the rows the quantizer sees.
+    ``fp8_weights``: every expert weight matrix is replaced by its FP8
+    fake-quant with one scale per 128 x 128 tile.
     """
+    if fp8_weights:
+        def deq(w):
+            return quantize_weight_blocks(w)[2]
+
+        raw_weights = weights
+        weights = lambda e: tuple(deq(w) for w in raw_weights(e))  # noqa: E731
+        if shared_weights is not None:
+            shared_weights = tuple(deq(w) for w in shared_weights)
     logits = np.asarray(logits, dtype=np.float32)
     hidden_bits = np.asarray(hidden_bits, dtype=np.uint16)
     T, E = logits.shape

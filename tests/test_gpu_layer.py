@@ -195,6 +195,50 @@ def test_layer_expert_parallel_share():
     _check_layer(cfg, layer, ref, None)
 
 
+@pytest.mark.parametrize("variant", ["tiny_everything", "mid_skewed_shared"])
+def test_layer_fp8_weights(variant):
+    """FP8 expert weights (routed and shared): the layer against the oracle
+    layer on the FP8 fake-quantized weights, and bit for bit against the bf16
+    layer given the oracle's dequantized weights."""
+    base = workloads.CONFIGS["tiny"]
+    cfg = {
+        "tiny_everything": base.with_(pad_rows=5, dispatch_block=128, pad_pow2=True,
+                                      shared_I=256, combine_qdq=True),
+        "mid_skewed_shared": workloads.MoEConfig("mid", 31, T=300, H=512, E=16, K=4, I=256,
+                                                 hot_experts=4, shared_I=128),
+    }[variant]
+    W = Weights(cfg)
+    lg, hd, vd = workloads.logits(cfg), workloads.hidden(cfg), workloads.row_valid(cfg)
+    kw = dict(dispatch_block=cfg.dispatch_block or None, pad_pow2=cfg.pad_pow2,
+              shared_weights=W.shared_host, combine_qdq=cfg.combine_qdq)
+    ref = oracle.moe_layer(lg, hd, lambda e: W.host[e], cfg.K, vd, fp8_weights=True, **kw)
+
+    def make():
+        return MoELayer(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, "cuda", shared_I=cfg.shared_I,
+                        dispatch_block=cfg.dispatch_block, combine_qdq=cfg.combine_qdq,
+                        pad_pow2=cfg.pad_pow2)
+
+    lgd, hdd = dev(lg), dev_bf16(hd)
+    vdd = None if vd is None else dev(vd)
+    f8 = make()
+    f8.set_weights(W.w13, W.w2, *(W.shared or (None, None)), fp8=True)
+    deq = lambda w: oracle.quantize_weight_blocks(w)[2]  # noqa: E731
+    bf = make()
+    d13 = torch.stack([dev_bf16(deq(W.host[e][0])) for e in range(cfg.E)])
+    d2 = torch.stack([dev_bf16(deq(W.host[e][1])) for e in range(cfg.E)])
+    sh = (None, None) if W.shared_host is None else tuple(dev_bf16(deq(w)) for w in W.shared_host)
+    bf.set_weights(d13, d2, *sh)
+    for layer in (f8, bf):
+        if cfg.combine_qdq:
+            layer.combine_scale.fill_(float(ref["combine_scale"]))
+        layer.forward(lgd, hdd, vdd)
+    torch.cuda.synchronize()
+    assert f8.dev_error.item() == 0 and bf.dev_error.item() == 0
+    assert torch.equal(f8.out.view(torch.int16), bf.out.view(torch.int16))
+    err = _check_layer(cfg, f8, ref, vd)
+    print(f"{variant}: FP8-weight layer rel err {err:.3e}")
+
+
 def _sampled(cfg, n_tok, scale=None, seed=0):
     rng = np.random.default_rng(seed)
     lg, hd, vd = workloads.logits(cfg), workloads.hidden(cfg), workloads.row_valid(cfg)

@@ -26,7 +26,14 @@ int launch_grouped_ffn(const uint16_t*, const int32_t*, const int32_t*, int, int
 int launch_pack_weights(const uint16_t*, const uint16_t*, int, int, int, uint16_t*, uint16_t*,
                         hipStream_t);
 int launch_pack_weights_fp8(const uint16_t*, const uint16_t*, int, int, int, uint8_t*, float*,
-                            uint8_t*, float*, hipStream_t);
+                            uint8_t*, float*, int, hipStream_t);
+int launch_quant_rows_fp8(const uint16_t*, int64_t, int, const int32_t*, uint8_t*, float*, int64_t,
+                          hipStream_t);
+size_t w8a8_workspace_bytes(int64_t, int, int);
+int launch_grouped_ffn_w8a8(const uint8_t*, const float*, int64_t, const int32_t*, const int32_t*,
+                            int, int, int, const uint8_t*, const float*, const uint8_t*,
+                            const float*, const float*, uint16_t*, int64_t, int, void*, int32_t*,
+                            hipStream_t);
 
 __global__ void __launch_bounds__(256) copy_kernel(const uint4* __restrict__ src,
                                                    uint4* __restrict__ dst, int64_t n) {
@@ -183,10 +190,53 @@ int moe_pack_ffn_weights(const uint16_t* w13, const uint16_t* w2, int num_groups
   return launch_pack_weights(w13, w2, num_groups, H, I, w13_packed, w2_packed, as_stream(stream));
 }
 
+int moe_quant_rows_fp8(const uint16_t* in, int64_t n_rows, int H, const int32_t* row_src,
+                       uint8_t* codes, float* scales, int64_t scale_stride, void* stream) {
+  if (n_rows < 0 || H < 1 || scale_stride < n_rows) return MOE_ERR_INVALID_ARG;
+  if (H % 128) return MOE_ERR_UNSUPPORTED;
+  if (n_rows == 0) return MOE_OK;
+  if (!in || !codes || !scales || !aligned16(in) || !aligned16(codes)) return MOE_ERR_INVALID_ARG;
+  return launch_quant_rows_fp8(in, n_rows, H, row_src, codes, scales, scale_stride,
+                               as_stream(stream));
+}
+
+size_t moe_grouped_ffn_w8a8_workspace_bytes(int64_t capacity, int num_groups, int H, int I) {
+  (void)H;
+  if (capacity < 0 || num_groups < 1 || I < 1) return 0;
+  return w8a8_workspace_bytes(capacity, num_groups, I);
+}
+
+int moe_grouped_ffn_w8a8(const uint8_t* xq, const float* x_scales, int64_t scale_stride,
+                         const int32_t* cu_seqlens, const int32_t* counts, int num_groups, int H,
+                         int I, const uint8_t* w13q, const float* w13_scales, const uint8_t* w2q,
+                         const float* w2_scales, const float* row_scale, uint16_t* y,
+                         int64_t capacity, int flags, void* workspace, size_t workspace_bytes,
+                         int32_t* dev_error, void* stream) {
+  if (num_groups < 1 || H < 1 || I < 1 || capacity < 0) return MOE_ERR_INVALID_ARG;
+  if ((flags & ~MOE_FFN_ALL) || !(flags & MOE_FFN_ALL)) return MOE_ERR_INVALID_ARG;
+  if (H % 128 || I % 128 || num_groups > 1024) return MOE_ERR_UNSUPPORTED;
+  if (capacity > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  if (!cu_seqlens || !counts) return MOE_ERR_INVALID_ARG;
+  if ((flags & MOE_FFN_GATE_UP) &&
+      (!xq || !x_scales || !w13q || !w13_scales || scale_stride < capacity))
+    return MOE_ERR_INVALID_ARG;
+  if ((flags & MOE_FFN_DOWN) && (!y || !w2q || !w2_scales)) return MOE_ERR_INVALID_ARG;
+  if ((xq && !aligned16(xq)) || (y && !aligned16(y)) || (w13q && !aligned16(w13q)) ||
+      (w2q && !aligned16(w2q)))
+    return MOE_ERR_INVALID_ARG;
+  const size_t need = w8a8_workspace_bytes(capacity, num_groups, I);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return MOE_ERR_WORKSPACE;
+  return launch_grouped_ffn_w8a8(xq, x_scales, scale_stride, cu_seqlens, counts, num_groups, H, I,
+                                 w13q, w13_scales, w2q, w2_scales, row_scale, y, capacity, flags,
+                                 workspace, dev_error, as_stream(stream));
+}
+
 int moe_pack_ffn_weights_fp8(const uint16_t* w13, const uint16_t* w2, int num_groups, int H,
                              int I, uint8_t* w13q, float* w13_scales, uint8_t* w2q,
-                             float* w2_scales, void* stream) {
+                             float* w2_scales, int flags, void* stream) {
   if (num_groups < 1 || H < 1 || I < 1) return MOE_ERR_INVALID_ARG;
+  if (flags & ~MOE_FP8_LAYOUT_K128) return MOE_ERR_INVALID_ARG;
   if (H % 128 || I % 128) return MOE_ERR_UNSUPPORTED;
   if (!w13 != !w13q || !w13 != !w13_scales || !w2 != !w2q || !w2 != !w2_scales)
     return MOE_ERR_INVALID_ARG;
@@ -194,7 +244,7 @@ int moe_pack_ffn_weights_fp8(const uint16_t* w13, const uint16_t* w2, int num_gr
       (w2 && (!aligned16(w2) || !aligned16(w2q) || !aligned16(w2_scales))))
     return MOE_ERR_INVALID_ARG;
   return launch_pack_weights_fp8(w13, w2, num_groups, H, I, w13q, w13_scales, w2q, w2_scales,
-                                 as_stream(stream));
+                                 (flags & MOE_FP8_LAYOUT_K128) ? 1 : 0, as_stream(stream));
 }
 
 int moe_fake_quant_rows(const uint16_t* in, uint16_t* out, int64_t n_rows, int H,

@@ -40,73 +40,15 @@
 #include <algorithm>
 #include <type_traits>
 
-#include "common.h"
+#include "gemm_common.h"
 
 namespace moe {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 16-byte staging
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));  // 8 FP8 codes
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-constexpr int kBM = 128;
+// the row-major-weight kernel's block tile
 constexpr int kBN = 128;
 constexpr int kBK = 64;
 constexpr int kLdsStride = kBK + 8;  // bf16 elements per LDS row
 constexpr int kThreads = 256;
-constexpr int kNumXcd = 8;
-
-// Workgroup ids are dealt round-robin over the 8 XCDs.  Remap them so that
-// runs of kXcdChunk consecutive tile numbers land on one XCD (they share
-// weight and activation panels through its L2) while successive runs go to
-// successive XCDs (the work, including the empty tail, stays balanced).
-// The grid is a multiple of 8 * kXcdChunk, which makes this a bijection.
-constexpr int kXcdChunk = 16;
-__device__ __forceinline__ int xcd_remap(int bid) {
-  const int xcd = bid % kNumXcd, local = bid / kNumXcd;
-  const int chunk = local / kXcdChunk, off = local % kXcdChunk;
-  return (chunk * kNumXcd + xcd) * kXcdChunk + off;
-}
-
-// Decode tile number `pid` into (group, m-tile, n-tile).  Every lane of the
-// calling wave returns the same answer; returns false past the last tile.
-__device__ __forceinline__ bool decode_tile(int pid, const int32_t* __restrict__ counts, int G,
-                                            int n_tiles, int& g, int& mt, int& nt,
-                                            int* mt_base = nullptr) {
-  const int lane = threadIdx.x & 63;
-  int carry = 0;
-  for (int base = 0; base < G; base += kWave) {
-    const int e = base + lane;
-    const int c = e < G ? max(counts[e], 0) : 0;
-    const int tiles = ((c + kBM - 1) / kBM) * n_tiles;
-    int incl = tiles;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += y;
-    }
-    incl += carry;
-    const int excl = incl - tiles;
-    const uint64_t hit = __ballot(e < G && pid >= excl && pid < incl);
-    if (hit) {
-      const int src = __ffsll((unsigned long long)hit) - 1;
-      g = base + src;
-      const int ex = __shfl(excl, src, kWave);
-      const int local = pid - ex;
-      const int mtiles = (__shfl(c, src, kWave) + kBM - 1) / kBM;
-      nt = local / mtiles;
-      mt = local - nt * mtiles;
-      if (mt_base) *mt_base = ex / n_tiles;  // m-tiles of the groups before g
-      return true;
-    }
-    carry = __shfl(incl, 63, kWave);
-  }
-  return false;
-}
-
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
 template <bool GATE_UP>
 __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
@@ -286,50 +228,6 @@ constexpr int kStageBlocks = kMsub * kChunkSteps;  // 1 KB blocks per LDS stage
 // activation tile is then shared by more columns), 4 when they are short (more,
 // smaller workgroups balance skewed segment sizes better).
 
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wave are outstanding (and for nothing else)
-__device__ __forceinline__ constexpr int vmcnt_imm(int n) {
-  return (n & 0xf) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xf << 8);
-}
-
-// Workgroup barrier for the activation ring, without the memory fence that
-// __syncthreads() carries: with direct-to-LDS loads in flight that fence
-// becomes a wait for every outstanding load, weight prefetches included, and
-// drains the weight pipeline at every chunk.  The ordering it would give is
-// established explicitly instead: each wave first waits (vmcnt) until its own
-// DMA for the chunk has landed in LDS, so after the barrier the whole chunk
-// is there; and the slot the next DMA overwrites was last read for MFMAs the
-// waves had already issued, so those LDS reads were complete.  The empty asm
-// statements keep the compiler from moving LDS accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// The activation DMA (global_load_lds_dwordx4: 64 lanes x 16 bytes from
-// global memory to LDS at M0), issued as inline assembly.  When the
-// compiler's wait-count insertion sees a direct-to-LDS load, it cannot tell
-// which ring slot it writes, so it makes the next LDS read (and any reuse of
-// the load's address registers) wait until no vector-memory operation is
-// outstanding, weight prefetches included, which drains the weight pipeline
-// at every chunk.  It does not model this statement; the DMA of a chunk is
-// waited for explicitly (vmcnt at the chunk barrier), and the compiler's own
-// waits for the weight loads, which do not count these DMAs, are only
-// stricter than needed, never looser.  The LDS reads stay ordinary loads, so
-// their waits and register hazards remain the compiler's; they cannot move
-// across lds_barrier(), whose empty asm statements clobber memory.
-// The source address is a wave-uniform base (SGPRs) plus a 32-bit per-lane
-// byte offset, which keeps the per-lane state of the DMA small.
-__device__ __forceinline__ void dma16(const uint16_t* sbase, uint32_t voff, const u32x4_t* l) {
-  const uint32_t lds =
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) u32x4_t*)l;
-  // one wait state between the SALU write of M0 and the DMA that reads it
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "m0");
-}
 
 // FP8 weights: a lane's 8 E4M3 codes (a B-fragment row piece) to the bf16
 // fragment the MFMA reads, bf16(fl32(code * s)) with the tile's scale s —
@@ -420,10 +318,13 @@ __device__ __forceinline__ void frag_gemm_body(
   // outstanding, with n no larger than the number issued after the chunk's
   // DMA, guarantees that DMA has landed.  After the DMA of chunk c (issued
   // at the start of chunk c - (kStages-1)) come at least the weight loads of
-  // kStages-1 chunks (the later DMAs may be empty for this wave); the
-  // prologue issues at least as many.
+  // kStages-1 chunks (the later DMAs may be empty for this wave).  The
+  // prologue's DMAs are followed by its kPrologue weight loads and the
+  // refills of the chunks before c: fewer than that only for chunk 0, which
+  // then waits for kPrologue.
   constexpr int kAfterDma = (kStages - 1) * kChunkSteps * kFrags;
-  static_assert(kAfterDma <= kPrefetch * kFrags, "prologue count");
+  constexpr int kPrologue = kPrefetch * kFrags;
+  static_assert(kAfterDma <= kPrologue + kChunkSteps * kFrags, "prologue count");
   static_assert(kPrefetch % kChunkSteps == 0, "chunk boundaries fall on prefetch slots");
   // nks is a multiple of kPrefetch = 4 (K is a multiple of 128)
   int stage = 0;  // ring slot of the current chunk
@@ -434,7 +335,10 @@ __device__ __forceinline__ void frag_gemm_body(
       if (s % kChunkSteps == 0) {
         const int chunk = ks / kChunkSteps;
         if (chunk > 0) stage = (stage + 1 == kStages) ? 0 : stage + 1;
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAfterDma));
+        if (kAfterDma > kPrologue && chunk == 0)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAfterDma > kPrologue ? kPrologue : kAfterDma));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAfterDma));
         lds_barrier();
         // the slot kStages-1 ahead was last read in the previous chunk, which
         // every wave has finished; past the end this reloads a valid chunk so
@@ -657,12 +561,17 @@ __global__ void __launch_bounds__(256) pack_weights_kernel(const uint16_t* __res
 // FP8 weights: one workgroup per 128 x 128 tile of one group's [N, Kdim]
 // matrix.  The tile's amax gives its scale s = amax / 448 (IEEE division;
 // an all-zero tile gets s = 0 and codes 0); every element becomes the E4M3
-// code of clamp(w / s, +-448) (round to nearest even), written in the same
-// fragment order as the bf16 packing with 8 codes (8 bytes) per lane.
+// code of clamp(w / s, +-448) (round to nearest even), written in one of
+// two fragment orders: k128 = 0, the order of the bf16 packing with 8 codes
+// (8 bytes) per lane per 32-wide K-step (for the GEMM that dequantizes to
+// bf16); k128 = 1, the order of the FP8 matrix-core GEMM, whose B fragment
+// covers a whole 128-wide K-block: per K-block, column tile, fragment and
+// half h, 64 lanes x 16 bytes, lane l holding row l%16, columns
+// 64 h + 16 (l/16) .. +16 of the block.
 __global__ void __launch_bounds__(256) pack_weights_fp8_kernel(const uint16_t* __restrict__ W,
                                                                uint8_t* __restrict__ Q,
                                                                float* __restrict__ S, int N,
-                                                               int Kdim, int gate_up) {
+                                                               int Kdim, int gate_up, int k128) {
   const int nrb = N / 128, nkb = Kdim / 128;
   const int64_t tile = blockIdx.x;
   const int kb = (int)(tile % nkb);
@@ -719,27 +628,35 @@ __global__ void __launch_bounds__(256) pack_weights_fp8_kernel(const uint16_t* _
       ct = row / 64;
       f_ = (row % 64) / 16;
     }
-    const int ks = k8 / 4;
-    const int lane = (row & 15) + 16 * (k8 & 3);
-    const int64_t dst = (((g * nks + ks) * n_ct + ct) * kFrags + f_) * kWave + lane;
+    int64_t dst;  // in 8-byte units
+    if (k128) {
+      const int kk = (k8 % 16) * 8;  // column within the K-block
+      const int lane = (row & 15) + 16 * ((kk % 64) / 16);
+      const int64_t unit = ((((g * nkb + kb) * n_ct + ct) * kFrags + f_) * 2 + kk / 64) * kWave + lane;
+      dst = unit * 2 + (kk % 16) / 8;
+    } else {
+      const int ks = k8 / 4;
+      const int lane = (row & 15) + 16 * (k8 & 3);
+      dst = (((g * nks + ks) * n_ct + ct) * kFrags + f_) * kWave + lane;
+    }
     reinterpret_cast<uint2*>(Q)[dst] = make_uint2(code[0], code[1]);
   }
 }
 
 int launch_pack_weights_fp8(const uint16_t* w13, const uint16_t* w2, int G, int H, int I,
-                            uint8_t* w13q, float* w13s, uint8_t* w2q, float* w2s,
+                            uint8_t* w13q, float* w13s, uint8_t* w2q, float* w2s, int k128,
                             hipStream_t stream) {
   if (w13) {
     const int64_t tiles = (int64_t)G * (2 * I / 128) * (H / 128);
     if (tiles > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(pack_weights_fp8_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, w13,
-                       w13q, w13s, 2 * I, H, 1);
+                       w13q, w13s, 2 * I, H, 1, k128);
   }
   if (w2) {
     const int64_t tiles = (int64_t)G * (H / 128) * (I / 128);
     if (tiles > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(pack_weights_fp8_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, w2,
-                       w2q, w2s, H, I, 0);
+                       w2q, w2s, H, I, 0, k128);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

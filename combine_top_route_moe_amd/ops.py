@@ -20,6 +20,7 @@ MOE_PERMUTE_PAD_POW2 = 1
 MOE_FFN_GATE_UP, MOE_FFN_DOWN, MOE_FFN_ALL, MOE_FFN_PACKED_WEIGHTS = 1, 2, 3, 4
 MOE_FQ_PER_TENSOR, MOE_FQ_BLOCK, MOE_FQ_NVFP4, MOE_FQ_MXFP4 = 0, 1, 2, 3
 MOE_DEVERR_ROW_RANGE, MOE_DEVERR_CAPACITY, MOE_DEVERR_LAYOUT = 1, 2, 3
+MOE_FP8_LAYOUT_K128 = 1
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -217,9 +218,10 @@ def moe_grouped_ffn_fp8(x: torch.Tensor, cu_seqlens: torch.Tensor, counts: torch
 
 
 def moe_pack_ffn_weights_fp8(w13: Optional[torch.Tensor], w2: Optional[torch.Tensor],
-                             stream=None):
+                             k128: bool = False, stream=None):
     """Quantize w13 [G,2I,H] / w2 [G,H,I] to E4M3 with one float32 scale per
-    128 x 128 tile, codes in the grouped GEMM's packed order.  Returns
+    128 x 128 tile, codes in the packed order of moe_grouped_ffn_fp8 (or,
+    with ``k128``, of moe_grouped_ffn_w8a8).  Returns
     ``(w13q, w13_scales, w2q, w2_scales)`` (None for an absent input)."""
     if w13 is not None:
         _want(w13, torch.bfloat16, "w13")
@@ -238,8 +240,73 @@ def moe_pack_ffn_weights_fp8(w13: Optional[torch.Tensor], w2: Optional[torch.Ten
         w2s = torch.empty(G, H // 128, I // 128, dtype=torch.float32, device=dev)
     check("moe_pack_ffn_weights_fp8", load().moe_pack_ffn_weights_fp8(
         _ptr(w13), _ptr(w2), G, H, I, _ptr(w13q), _ptr(w13s), _ptr(w2q), _ptr(w2s),
-        _stream(stream)))
+        MOE_FP8_LAYOUT_K128 if k128 else 0, _stream(stream)))
     return w13q, w13s, w2q, w2s
+
+
+def moe_quant_rows_fp8(inp: torch.Tensor, row_src: Optional[torch.Tensor] = None,
+                       codes: Optional[torch.Tensor] = None,
+                       scales: Optional[torch.Tensor] = None, stream=None):
+    """bf16 rows [R, H] -> E4M3 codes uint8 [R, H] and float32 scales
+    [H/128, stride] (K-block-major, stride = scales.shape[1] >= R)."""
+    _want(inp, torch.bfloat16, "inp")
+    R, H = inp.shape
+    if codes is None:
+        codes = torch.empty(R, H, dtype=torch.uint8, device=inp.device)
+    if scales is None:
+        scales = torch.empty(H // 128, max(R, 1), dtype=torch.float32, device=inp.device)
+    _want(codes, torch.uint8, "codes")
+    _want(scales, torch.float32, "scales")
+    if row_src is not None:
+        _want(row_src, torch.int32, "row_src")
+    check("moe_quant_rows_fp8", load().moe_quant_rows_fp8(
+        _ptr(inp), R, H, _ptr(row_src), _ptr(codes), _ptr(scales), scales.shape[1],
+        _stream(stream)))
+    return codes, scales
+
+
+def moe_grouped_ffn_w8a8_workspace_bytes(capacity: int, num_groups: int, H: int, I: int) -> int:
+    return load().moe_grouped_ffn_w8a8_workspace_bytes(capacity, num_groups, H, I)
+
+
+def moe_grouped_ffn_w8a8(xq: torch.Tensor, x_scales: torch.Tensor, cu_seqlens: torch.Tensor,
+                         counts: torch.Tensor, w13q: torch.Tensor, w13_scales: torch.Tensor,
+                         w2q: torch.Tensor, w2_scales: torch.Tensor,
+                         row_scale: Optional[torch.Tensor] = None,
+                         y: Optional[torch.Tensor] = None, flags: int = MOE_FFN_ALL,
+                         workspace: Optional[torch.Tensor] = None,
+                         dev_error: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The grouped FFN on FP8 rows (moe_quant_rows_fp8) and FP8 weights
+    (moe_pack_ffn_weights_fp8 with ``k128=True``) on the FP8 matrix cores."""
+    _want(xq, torch.uint8, "xq")
+    _want(x_scales, torch.float32, "x_scales")
+    _want(w13q, torch.uint8, "w13q")
+    _want(w2q, torch.uint8, "w2q")
+    _want(w13_scales, torch.float32, "w13_scales")
+    _want(w2_scales, torch.float32, "w2_scales")
+    _want(cu_seqlens, torch.int32, "cu_seqlens")
+    _want(counts, torch.int32, "counts")
+    if row_scale is not None:
+        _want(row_scale, torch.float32, "row_scale")
+    capacity, H = xq.shape
+    G, two_i, H2 = w13q.shape
+    I = two_i // 2
+    if H2 != H or tuple(w2q.shape) != (G, H, I):
+        raise ValueError("weight shapes do not match xq")
+    if x_scales.shape[0] != H // 128 or x_scales.shape[1] < capacity:
+        raise ValueError("x_scales must be [H/128, >= capacity]")
+    if counts.numel() != G or cu_seqlens.numel() != G + 1:
+        raise ValueError("counts / cu_seqlens do not match the number of groups")
+    lib = load()
+    y = torch.empty(capacity, H, dtype=torch.bfloat16, device=xq.device) if y is None else y
+    need = lib.moe_grouped_ffn_w8a8_workspace_bytes(capacity, G, H, I)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=xq.device)
+    check("moe_grouped_ffn_w8a8", lib.moe_grouped_ffn_w8a8(
+        _ptr(xq), _ptr(x_scales), x_scales.shape[1], _ptr(cu_seqlens), _ptr(counts), G, H, I,
+        _ptr(w13q), _ptr(w13_scales), _ptr(w2q), _ptr(w2_scales), _ptr(row_scale), _ptr(y),
+        capacity, flags, _ptr(workspace), workspace.numel(), _ptr(dev_error), _stream(stream)))
+    return y
 
 
 def moe_fake_quant_rows(inp: torch.Tensor, out: Optional[torch.Tensor] = None,

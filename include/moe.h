@@ -74,6 +74,8 @@ enum { MOE_FQ_PER_TENSOR = 0,         /* moe_fake_quant_rows modes         */
        MOE_FQ_BLOCK = 1,
        MOE_FQ_NVFP4 = 2,
        MOE_FQ_MXFP4 = 3 };
+enum { MOE_FP8_LAYOUT_K128 = 1 };     /* moe_pack_ffn_weights_fp8: the FP8
+                                         matrix-core GEMM's weight order     */
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* moe_status_string(int status);
@@ -202,12 +204,17 @@ int moe_pack_ffn_weights(const uint16_t* w13, const uint16_t* w2, int num_groups
  *     ((g * (Kdim/32) + ks) * n_ct + ct) * 256 + f * 64 + l, 8 bytes each.
  *   w13_scales [G, 2I/128, H/128], w2_scales [G, H/128, I/128] float32 (out),
  *     tile (row block, column block) row-major per group.
+ * With flags = MOE_FP8_LAYOUT_K128 the codes are instead in the order
+ * moe_grouped_ffn_w8a8 streams: 16-byte unit
+ * ((((g * (Kdim/128) + kb) * n_ct + ct) * 4 + f) * 2 + h) * 64 + l holds weight
+ * row row0(ct, f) + l % 16 (rows as above), columns
+ * 128 kb + 64 h + 16 (l / 16) .. +16.
  * Either group of three (w13, w13q, w13_scales) / (w2, ...) may be all NULL.
- * Pointers 16-byte aligned.  Runs once at load time.
- * Requires H % 128 == 0, I % 128 == 0. */
+ * Pointers 16-byte aligned.  Runs once at load time.  Unknown flag bits:
+ * MOE_ERR_INVALID_ARG.  Requires H % 128 == 0, I % 128 == 0. */
 int moe_pack_ffn_weights_fp8(const uint16_t* w13, const uint16_t* w2, int num_groups, int H,
                              int I, uint8_t* w13q, float* w13_scales, uint8_t* w2q,
-                             float* w2_scales, void* stream);
+                             float* w2_scales, int flags, void* stream);
 
 /* moe_grouped_ffn with the FP8 weights above: the same operation, segments,
  * flags (stage bits only; the weights are always the packed FP8 ones),
@@ -221,6 +228,50 @@ int moe_grouped_ffn_fp8(const uint16_t* x, const int32_t* cu_seqlens, const int3
                         const uint8_t* w2q, const float* w2_scales, const float* row_scale,
                         uint16_t* y, int64_t capacity, int flags, void* workspace,
                         size_t workspace_bytes, int32_t* dev_error, void* stream);
+
+/* ---- FP8 activations and weights on the FP8 matrix cores -----------------
+ * The dispatch quantizer for real ([P2] review thread on the low-latency
+ * dispatch: tokens handed over as FP8 codes with their block scales): for
+ * every row r and 128-channel block kb of bf16 rows in [n_rows, H],
+ * s = fl32(amax / 448) and codes e4m3(clamp(fl32(x / s), +-448)) (IEEE
+ * quotient, round to nearest even) — the codes and scales whose dequant
+ * bf16(q * s) is moe_fake_quant_rows(MOE_FQ_BLOCK).  Rows with
+ * row_src[r] < 0 (row_src may be NULL) and all-zero blocks get codes 0 and
+ * scale 0.
+ *   codes [n_rows, H] uint8 (out), 16-byte aligned;
+ *   scales (out) K-block-major: scales[kb * scale_stride + r], float32,
+ *     scale_stride >= n_rows.
+ * Requires H % 128 == 0. */
+int moe_quant_rows_fp8(const uint16_t* in, int64_t n_rows, int H, const int32_t* row_src,
+                       uint8_t* codes, float* scales, int64_t scale_stride, void* stream);
+
+/* The grouped SwiGLU FFN on FP8 rows and FP8 weights ([P2] review threads on
+ * the low-latency dispatch and on the DeepEP + DeepGEMM test: FP8 tokens
+ * with block scales times FP8 weights with tile scales in the grouped GEMMs;
+ * [P3] commit message adding the modular experts): per segment g (rows as in
+ * moe_grouped_ffn),
+ *   h[r, n] = sum_kb sx[r, kb] * sw13[g][n/128, kb] * sum_{k in kb} qx[r, k] qw13[g][n, k]
+ *   a = bf16(silu(h[:, :I]) * h[:, I:]), quantized per 1 x 128 block like
+ *       moe_quant_rows_fp8 (codes qa, scales sa; kept in the workspace)
+ *   y[r] = bf16(row_scale[r] * sum_kb sa[r, kb] * sw2[g][n/128, kb] * (qa . qw2))
+ * with every K-block's code products summed by the matrix cores in float32
+ * and scaled into a float32 accumulator.
+ *   xq [capacity, H] uint8 and x_scales (K-block-major, stride
+ *     scale_stride >= capacity) from moe_quant_rows_fp8;
+ *   w13q / w2q and their tile scales from moe_pack_ffn_weights_fp8 with
+ *     MOE_FP8_LAYOUT_K128; row_scale, y, cu_seqlens, counts, capacity as in
+ *     moe_grouped_ffn.
+ * flags: MOE_FFN_GATE_UP (writes qa, sa into the workspace), MOE_FFN_DOWN
+ * (reads them; needs the workspace of a GATE_UP call on the same segments)
+ * or MOE_FFN_ALL.  Segments past capacity are skipped with
+ * MOE_DEVERR_ROW_RANGE.  Requires H % 128 == 0, I % 128 == 0, G <= 1024. */
+size_t moe_grouped_ffn_w8a8_workspace_bytes(int64_t capacity, int num_groups, int H, int I);
+int moe_grouped_ffn_w8a8(const uint8_t* xq, const float* x_scales, int64_t scale_stride,
+                         const int32_t* cu_seqlens, const int32_t* counts, int num_groups, int H,
+                         int I, const uint8_t* w13q, const float* w13_scales, const uint8_t* w2q,
+                         const float* w2_scales, const float* row_scale, uint16_t* y,
+                         int64_t capacity, int flags, void* workspace, size_t workspace_bytes,
+                         int32_t* dev_error, void* stream);
 
 /* ---- FP8 and FP4 fake-quant of bf16 rows -------------------------------
  * QDQ to OCP E4M3FN and back ([P1] PR summary and "How it works": the

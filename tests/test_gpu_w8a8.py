@@ -1,0 +1,146 @@
+"""The FP8 matrix-core path: FP8 rows, FP8 weights, block scales per K-block.
+
+* moe_quant_rows_fp8 against oracle.quantize_rows_fp8: codes (decoded from
+  their E4M3 bit fields, sign of zero included) and scales bit-exact, padding
+  rows skipped, scales in the documented K-block-major layout.
+* moe_pack_ffn_weights_fp8 with the K=128 layout: codes and scales
+  bit-exact against oracle.quantize_weight_blocks through the documented
+  order.
+* moe_grouped_ffn_w8a8 against oracle.grouped_ffn_w8a8 (float64, the same
+  quantization of rows, weights and intermediate): Frobenius relative error
+  <= 2e-2 per expert; pow2 padding rows never written; GATE_UP then DOWN
+  gives the same bits as ALL.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from combine_top_route_moe_amd import ops
+from oracle.numerics import bf16_bits_to_f32
+from tests.gpu_util import need_gpu, dev_bf16, host_bits, dev, host, rel_err, stacked_weights
+
+pytestmark = pytest.mark.gpu
+
+FFN_TOL = 2e-2
+
+
+def setup_module(module):
+    need_gpu()
+    assert ops.moe_device_check(0) == 0, "not a gfx950 device"
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """OCP E4M3FN bytes to values (sign, 4 exponent bits with bias 7, 3
+    mantissa bits; exponent 0 subnormal).  NaN codes must not appear."""
+    c = codes.astype(np.int64)
+    assert not np.any((c & 0x7F) == 0x7F), "NaN code"
+    e, m = (c >> 3) & 0xF, c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.where(c & 0x80, -mag, mag)
+
+
+def test_quant_rows_fp8_matches_oracle():
+    rng = np.random.default_rng(5)
+    R, H = 77, 384
+    x = (rng.standard_normal((R, H)) * np.exp2(rng.integers(-8, 8, (R, 1)))).astype(np.float32)
+    x[3, 128:256] = 0.0                     # an all-zero block
+    x[4, :] = -0.0                          # negative zeros
+    x[5, 7] = 3e-38                         # far below the block's E4M3 range
+    xb = oracle.f32_to_bf16_bits(x)
+    src = np.arange(R, dtype=np.int32)
+    src[[10, 40, 76]] = -1                  # padding rows
+    stride = R + 13
+    codes, scales = ops.moe_quant_rows_fp8(dev_bf16(xb), dev(src),
+                                           scales=torch.full((H // 128, stride), 7.0, device="cuda"))
+    torch.cuda.synchronize()
+    q_want, s_want = oracle.quantize_rows_fp8(xb, row_mask=src >= 0)
+    got_s = host(scales)
+    np.testing.assert_array_equal(got_s[:, :R].T.view(np.uint32), s_want.view(np.uint32))
+    assert np.all(got_s[:, R:] == 7.0)      # nothing past n_rows is written
+    vals = e4m3_decode(host(codes))
+    np.testing.assert_array_equal(vals, q_want)
+    np.testing.assert_array_equal(np.signbit(vals), np.signbit(q_want))
+
+
+def unpack_k128(q: np.ndarray, gate_up: bool, G: int, N: int, Kdim: int) -> np.ndarray:
+    """K=128-layout codes back to row-major [G, N, Kdim]: 16-byte unit
+    ((((g * Kdim/128 + kb) * n_ct + ct) * 4 + f) * 2 + h) * 64 + l holds row
+    row0(ct, f) + l % 16, columns 128 kb + 64 h + 16 (l / 16) .. +16."""
+    def order(p):          # g kb ct f h l4 l16 c -> g ct f l16 kb h l4 c
+        return p.transpose(0, 2, 3, 6, 1, 4, 5, 7)
+    if not gate_up:
+        p = q.reshape(G, Kdim // 128, N // 64, 4, 2, 4, 16, 16)
+        return order(p).reshape(G, N, Kdim)
+    I = N // 2
+    p = q.reshape(G, Kdim // 128, I // 32, 4, 2, 4, 16, 16)
+    gate = order(p[:, :, :, :2]).reshape(G, I, Kdim)
+    up = order(p[:, :, :, 2:]).reshape(G, I, Kdim)
+    return np.concatenate([gate, up], axis=1)
+
+
+def test_pack_k128_layout_matches_oracle():
+    G, H, I = 2, 384, 256
+    cfg = workloads.MoEConfig("t", 23, T=8, H=H, E=G, K=1, I=I)
+    w13, w2, host_w = stacked_weights(cfg)
+    w13q, w13s, w2q, w2s = ops.moe_pack_ffn_weights_fp8(w13, w2, k128=True)
+    torch.cuda.synchronize()
+    for q, s, gate_up, N, Kd, idx in ((w13q, w13s, True, 2 * I, H, 0), (w2q, w2s, False, H, I, 1)):
+        codes = unpack_k128(host(q), gate_up, G, N, Kd)
+        for g in range(G):
+            want_q, want_s, _ = oracle.quantize_weight_blocks(host_w[g][idx])
+            np.testing.assert_array_equal(host(s)[g].view(np.uint32), want_s.view(np.uint32))
+            vals = e4m3_decode(codes[g])
+            np.testing.assert_array_equal(vals, want_q)
+            np.testing.assert_array_equal(np.signbit(vals), np.signbit(want_q))
+
+
+@pytest.mark.parametrize("H,I,T,hot,pow2", [
+    (256, 128, 40, 0, False),      # short segments (one live row half)
+    (384, 256, 300, 2, True),      # partial column block in the down GEMM, pow2 padding
+    (256, 256, 2000, 2, False),    # several m-tiles per expert
+    (512, 384, 500, 0, False),     # an odd number of K-blocks in the down GEMM
+])
+def test_w8a8_ffn_matches_oracle(H, I, T, hot, pow2):
+    G = 6
+    cfg = workloads.MoEConfig("t", 24, T=T, H=H, E=G, K=2, I=I, hot_experts=hot)
+    idx, w = oracle.route(workloads.logits(cfg), None, 2)
+    hid = workloads.hidden(cfg)
+    w13, w2, host_w = stacked_weights(cfg)
+    w13q, w13s, w2q, w2s = ops.moe_pack_ffn_weights_fp8(w13, w2, k128=True)
+    p = ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), G, 0, pow2)
+    cap = p.x_perm.shape[0]
+    xq, xs = ops.moe_quant_rows_fp8(p.x_perm, p.src_of)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y = torch.zeros(cap, H, dtype=torch.bfloat16, device="cuda")
+    ops.moe_grouped_ffn_w8a8(xq, xs, p.cu_seqlens, p.counts, w13q, w13s, w2q, w2s, p.w_perm, y,
+                             dev_error=err)
+    ws = torch.empty(ops.moe_grouped_ffn_w8a8_workspace_bytes(cap, G, H, I), dtype=torch.uint8,
+                     device="cuda")
+    y2 = torch.zeros_like(y)
+    ops.moe_grouped_ffn_w8a8(xq, xs, p.cu_seqlens, p.counts, w13q, w13s, w2q, w2s, p.w_perm, y2,
+                             ops.MOE_FFN_GATE_UP, ws)
+    ops.moe_grouped_ffn_w8a8(xq, xs, p.cu_seqlens, p.counts, w13q, w13s, w2q, w2s, p.w_perm, y2,
+                             ops.MOE_FFN_DOWN, ws)
+    torch.cuda.synchronize()
+    assert host(err)[0] == 0
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    ref = oracle.permute(idx, w, hid, G, 0, pow2)
+    qx, sx = oracle.quantize_rows_fp8(ref["x_perm"], row_mask=ref["src_of"] >= 0)
+    want = oracle.grouped_ffn_w8a8(qx, sx, ref["cu_seqlens"], ref["counts"],
+                                   lambda e: host_w[e], ref["w_perm"])
+    got = bf16_bits_to_f32(host_bits(y))
+    worst = 0.0
+    for e in range(G):
+        n, r0 = int(ref["counts"][e]), int(ref["cu_seqlens"][e])
+        if n == 0:
+            continue
+        err_e = rel_err(got[r0:r0 + n], want[r0:r0 + n])
+        worst = max(worst, err_e)
+        assert err_e <= FFN_TOL, (e, n, err_e)
+        seg_end = int(ref["cu_seqlens"][e + 1])
+        if seg_end > r0 + n:
+            assert np.all(host_bits(y[r0 + n:seg_end]) == 0)
+    print(f"H={H} I={I} T={T}: worst per-expert rel err vs the FP8 oracle {worst:.3e}")

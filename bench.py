@@ -28,31 +28,44 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense BF16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense FP8 MFMA, published
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def algorithmic(cfg, counts: np.ndarray, fp8_weights: bool = False) -> dict:
+def algorithmic(cfg, counts: np.ndarray, fp8=None) -> dict:
     """Bytes (and FLOPs) each stage must move (compute) at minimum: every
     input read once, every output written once, padding rows and re-reads
-    not counted.  FP8 weights: one byte per weight plus a float32 scale per
-    128 x 128 tile."""
+    not counted.  FP8 weights (``fp8`` = "weights" or "w8a8"): one byte per
+    weight plus a float32 scale per 128 x 128 tile; the FP8 path ("w8a8")
+    also moves the rows and the intermediate as one-byte codes plus a float32
+    scale per 1 x 128 block."""
     T, H, E, K, I = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I
     Tv = cfg.T_valid
     N = int(counts.sum())
     E_act = int((counts > 0).sum())
+    w8a8 = fp8 == "w8a8"
     st = {}
     st["route"] = dict(bytes=4 * T * E + 8 * T * K + (T if cfg.pad_rows else 0))
-    if cfg.dispatch_block:
+    if w8a8:
+        st["dispatch_quant"] = dict(bytes=2 * T * H + T * H + T * H // 32)
+    elif cfg.dispatch_block:
         st["dispatch_qdq"] = dict(bytes=4 * Tv * H)
-    st["permute"] = dict(bytes=8 * T * K + 2 * Tv * H + 2 * N * H + 4 * T * K + 8 * N + 8 * E)
-    wb = 1 + 4 / (128 * 128) if fp8_weights else 2      # bytes per weight
-    st["ffn_gate_up"] = dict(bytes=int(wb * 2 * E_act * I * H) + 2 * N * H + 2 * N * I,
-                             flops=4 * N * I * H)
-    st["ffn_down"] = dict(bytes=int(wb * E_act * I * H) + 2 * N * I + 2 * N * H + 4 * N,
-                          flops=2 * N * I * H)
+    xb = 1 if w8a8 else 2                                  # bytes per row element
+    st["permute"] = dict(bytes=8 * T * K + xb * Tv * H + xb * N * H + 4 * T * K + 8 * N + 8 * E)
+    wb = 1 + 4 / (128 * 128) if fp8 else 2                 # bytes per weight
+    if w8a8:
+        st["ffn_gate_up"] = dict(bytes=int(wb * 2 * E_act * I * H) + N * H + N * H // 32 + 4 * N
+                                 + N * I + N * I // 32, flops=4 * N * I * H)
+        st["ffn_down"] = dict(bytes=int(wb * E_act * I * H) + N * I + N * I // 32 + 2 * N * H
+                              + 4 * N, flops=2 * N * I * H)
+    else:
+        st["ffn_gate_up"] = dict(bytes=int(wb * 2 * E_act * I * H) + 2 * N * H + 2 * N * I,
+                                 flops=4 * N * I * H)
+        st["ffn_down"] = dict(bytes=int(wb * E_act * I * H) + 2 * N * I + 2 * N * H + 4 * N,
+                              flops=2 * N * I * H)
     if cfg.shared_I:
         Is = cfg.shared_I
-        st["shared_ffn"] = dict(bytes=int(wb * 3 * Is * H) + 2 * T * H + 2 * T * H,
+        st["shared_ffn"] = dict(bytes=int(wb * 3 * Is * H) + xb * T * H + 2 * T * H,
                                 flops=6 * T * Is * H)
     st["combine"] = dict(bytes=2 * N * H + 4 * T * K + 2 * T * H + (2 * T * H if cfg.shared_I else 0))
     return st
@@ -60,8 +73,10 @@ def algorithmic(cfg, counts: np.ndarray, fp8_weights: bool = False) -> dict:
 
 STAGE_SOURCES = {
     "route": ["route.hip"], "dispatch_qdq": ["fake_quant.hip"], "permute": ["permute.hip"],
-    "ffn_gate_up": ["grouped_ffn.hip"], "ffn_down": ["grouped_ffn.hip"],
-    "shared_ffn": ["grouped_ffn.hip"], "combine": ["combine.hip"],
+    "dispatch_quant": ["fp8_ffn.hip"],
+    "ffn_gate_up": ["grouped_ffn.hip", "fp8_ffn.hip", "gemm_common.h"],
+    "ffn_down": ["grouped_ffn.hip", "fp8_ffn.hip", "gemm_common.h"],
+    "shared_ffn": ["grouped_ffn.hip", "fp8_ffn.hip", "gemm_common.h"], "combine": ["combine.hip"],
 }
 
 
@@ -89,7 +104,7 @@ def committed_traffic(stage: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, logits, hidden, row_valid, budget_s: float, fp8_weights: bool = False):
+def cpu_baseline(cfg, logits, hidden, row_valid, budget_s: float, fp8=None):
     """Time the oracle layer (as it stands) on a bounded sample of tokens.
     With FP8 weights the oracle's weight quantization runs once per expert
     before timing (like weight generation): the timed layer is the oracle
@@ -110,7 +125,7 @@ def cpu_baseline(cfg, logits, hidden, row_valid, budget_s: float, fp8_weights: b
     weights_cache = {}
 
     def prep(ws):
-        if not fp8_weights:
+        if fp8 != "weights":
             return ws
         return tuple(oracle.quantize_weight_blocks(w)[2] for w in ws)
 
@@ -128,7 +143,8 @@ def cpu_baseline(cfg, logits, hidden, row_valid, budget_s: float, fp8_weights: b
         t0 = time.perf_counter()
         oracle.moe_layer(logits[:n], hidden[:n], weights, cfg.K, rv,
                          dispatch_block=cfg.dispatch_block or None, pad_pow2=cfg.pad_pow2,
-                         shared_weights=shared, combine_qdq=cfg.combine_qdq)
+                         shared_weights=shared, combine_qdq=cfg.combine_qdq,
+                         fp8_gemm=fp8 == "w8a8")
         return time.perf_counter() - t0
 
     n = min(cfg.T, 64)
@@ -149,7 +165,8 @@ def cpu_baseline(cfg, logits, hidden, row_valid, budget_s: float, fp8_weights: b
     return {"value": tv / dt, "unit": "routed tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {n} of {cfg.T} tokens of the {cfg.name} batch ({tv} routed), "
                       f"whole layer, float64 numpy, median of {len(times)} runs: {dt:.2f} s"
-                      + ("; FP8 weights dequantized once before timing" if fp8_weights else "")}
+                      + ("; FP8 weights dequantized once before timing" if fp8 == "weights"
+                         else "; the oracle's FP8 path" if fp8 == "w8a8" else "")}
 
 
 def calibrate_spin(stream, target_ms: float = 1.0) -> int:
@@ -202,9 +219,12 @@ def main():
     ap.add_argument("--no-graph", action="store_true",
                     help="time the steps as eager launches instead of HIP-graph replays")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
-    ap.add_argument("--fp8-weights", action="store_true",
-                    help="expert weights as E4M3 codes with 128x128 tile scales, dequantized "
-                         "in registers before the BF16 MFMAs (activations stay bf16)")
+    ap.add_argument("--fp8", choices=["weights", "w8a8"], default=None,
+                    help="weights: expert weights as E4M3 codes with 128x128 tile scales, "
+                         "dequantized in registers before the BF16 MFMAs; w8a8: rows and weights "
+                         "as E4M3 codes on the FP8 matrix cores")
+    ap.add_argument("--fp8-weights", action="store_const", const="weights", dest="fp8",
+                    help="same as --fp8 weights")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the reference copy kernel (1 GiB -> 1 GiB) and report its "
                          "bandwidth; its byte counters scale the PMC traffic figures")
@@ -251,8 +271,8 @@ def main():
     workloads.for_each_expert(cfg, put)
     sw = workloads.shared_weights(cfg)
     layer.set_weights(w13, w2, *(bf16(x) for x in sw) if sw else (None, None),
-                      fp8=args.fp8_weights)
-    if args.fp8_weights:
+                      fp8={None: False, "weights": True, "w8a8": "w8a8"}[args.fp8])
+    if args.fp8:
         del w13, w2                   # only the packed FP8 codes stay resident
     if cfg.combine_qdq:
         layer.calibrate_combine_scale(logits, hidden, row_valid)
@@ -313,7 +333,8 @@ def main():
     assert layer.dev_error.item() == 0, "device error word set during the stage timing"
 
     counts = layer.perm.counts.cpu().numpy()
-    alg = algorithmic(cfg, counts, args.fp8_weights)
+    alg = algorithmic(cfg, counts, args.fp8)
+    peak_mfma = PEAK_FP8_TFLOPS if args.fp8 == "w8a8" else PEAK_BF16_TFLOPS
     stages = {}
     for name, ms in stage_ms.items():
         a = alg.get(name, {})
@@ -324,24 +345,25 @@ def main():
             d["hbm_frac"] = round(d["GBps"] / PEAK_HBM_GBPS, 4)
         if "flops" in a:
             d["TFLOPs"] = round(a["flops"] / (ms * 1e-3) / 1e12, 2)
-            d["mfma_util"] = round(d["TFLOPs"] / PEAK_BF16_TFLOPS, 4)
+            d["mfma_util"] = round(d["TFLOPs"] / peak_mfma, 4)
         stages[name] = d
 
     dom = max(stage_ms, key=stage_ms.get)
     a = alg[dom]
     intensity = a.get("flops", 0) / a["bytes"]
-    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    ridge = peak_mfma * 1e12 / (PEAK_HBM_GBPS * 1e9)
     if intensity >= ridge:
-        roof = {"bound": "mfma", "achieved": stages[dom]["TFLOPs"], "peak": PEAK_BF16_TFLOPS,
+        roof = {"bound": "mfma", "achieved": stages[dom]["TFLOPs"], "peak": peak_mfma,
                 "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": stages[dom]["GBps"], "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["kernel"] = {"ffn_gate_up": "frag_gemm_kernel<true>",
-                      "ffn_down": "frag_gemm_kernel<false>"}.get(dom, dom)
+    gemm = "w8a8_gemm_kernel" if args.fp8 == "w8a8" else "frag_gemm_kernel"
+    roof["kernel"] = {"ffn_gate_up": f"{gemm}<true>", "ffn_down": f"{gemm}<false>"}.get(dom, dom)
     roof["alg_bytes_per_launch"] = a["bytes"]
-    roof["traffic"] = committed_traffic(dom, cfg.name + ("_fp8w" if args.fp8_weights else ""))
+    roof["traffic"] = committed_traffic(
+        dom, cfg.name + {None: "", "weights": "_fp8w", "w8a8": "_w8a8"}[args.fp8])
 
     ms_step = elapsed / args.steps * 1e3
     gemm_flops = alg["ffn_gate_up"]["flops"] + alg["ffn_down"]["flops"]
@@ -357,16 +379,18 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3" if args.fp8 == "w8a8" else "bf16",
         "data": "synthetic (seeded N(0,1) logits and hidden, N(0,0.02) weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "T_valid": cfg.T_valid, "H": cfg.H,
                    "E": cfg.E, "K": cfg.K, "I": cfg.I, "shared_I": cfg.shared_I,
                    "routed_rows": int(counts.sum()), "dispatch_fp8_block": cfg.dispatch_block,
                    "combine_fp8": cfg.combine_qdq, "pad_pow2": cfg.pad_pow2,
-                   "expert_weights": ("fp8 e4m3, 128x128 tile scales" if args.fp8_weights
+                   "expert_weights": ("fp8 e4m3, 128x128 tile scales" if args.fp8
                                       else "bf16"),
+                   "activations": ("fp8 e4m3, 1x128 block scales" if args.fp8 == "w8a8"
+                                   else "bf16"),
                    "parallelism": "single GPU (all experts local)"},
-        "grouped_gemm_mfma_util": round(gemm_flops / (gemm_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+        "grouped_gemm_mfma_util": round(gemm_flops / (gemm_ms * 1e-3) / (peak_mfma * 1e12), 4),
         "permute_GBps": stages["permute"]["GBps"],
         "combine_GBps": stages["combine"]["GBps"],
         "stages": stages,
@@ -381,7 +405,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, logits_h, hidden_h, valid_h, args.cpu_budget,
-                                              args.fp8_weights)
+                                              args.fp8)
     print(json.dumps(result), flush=True)
 
 

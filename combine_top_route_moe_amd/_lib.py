@@ -32,9 +32,9 @@ SIGNATURES = {
                                           _c_int, _vp]),
     "moe_quant_rows_fp8": (_c_int, [_vp, _c_i64, _c_int, _vp, _vp, _vp, _c_i64, _vp]),
     "moe_grouped_ffn_w8a8_workspace_bytes": (_c_size, [_c_i64, _c_int, _c_int, _c_int]),
-    "moe_grouped_ffn_w8a8": (_c_int, [_vp, _vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp,
-                                      _vp, _vp, _vp, _vp, _c_i64, _c_int, _vp, _c_size, _vp,
-                                      _vp]),
+    "moe_grouped_ffn_w8a8": (_c_int, [_vp, _vp, _c_i64, _vp, _c_int, _vp, _vp, _c_int, _c_int,
+                                      _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_int, _vp,
+                                      _c_size, _vp, _vp]),
     "moe_fake_quant_rows": (_c_int, [_vp, _vp, _c_i64, _c_int, _vp, _c_int, _c_int, _vp, _vp,
                                      _vp, _vp]),
     "moe_scale_from_amax": (_c_int, [_vp, _vp, _vp]),

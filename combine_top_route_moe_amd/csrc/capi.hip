@@ -30,8 +30,8 @@ int launch_pack_weights_fp8(const uint16_t*, const uint16_t*, int, int, int, uin
 int launch_quant_rows_fp8(const uint16_t*, int64_t, int, const int32_t*, uint8_t*, float*, int64_t,
                           hipStream_t);
 size_t w8a8_workspace_bytes(int64_t, int, int);
-int launch_grouped_ffn_w8a8(const uint8_t*, const float*, int64_t, const int32_t*, const int32_t*,
-                            int, int, int, const uint8_t*, const float*, const uint8_t*,
+int launch_grouped_ffn_w8a8(const uint8_t*, const float*, int64_t, const int32_t*, int,
+                            const int32_t*, const int32_t*, int, int, int, const uint8_t*, const float*, const uint8_t*,
                             const float*, const float*, uint16_t*, int64_t, int, void*, int32_t*,
                             hipStream_t);
 
@@ -207,7 +207,7 @@ size_t moe_grouped_ffn_w8a8_workspace_bytes(int64_t capacity, int num_groups, in
 }
 
 int moe_grouped_ffn_w8a8(const uint8_t* xq, const float* x_scales, int64_t scale_stride,
-                         const int32_t* cu_seqlens, const int32_t* counts, int num_groups, int H,
+                         const int32_t* scale_src, int scale_div, const int32_t* cu_seqlens, const int32_t* counts, int num_groups, int H,
                          int I, const uint8_t* w13q, const float* w13_scales, const uint8_t* w2q,
                          const float* w2_scales, const float* row_scale, uint16_t* y,
                          int64_t capacity, int flags, void* workspace, size_t workspace_bytes,
@@ -218,8 +218,10 @@ int moe_grouped_ffn_w8a8(const uint8_t* xq, const float* x_scales, int64_t scale
   if (capacity > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
   if (!cu_seqlens || !counts) return MOE_ERR_INVALID_ARG;
   if ((flags & MOE_FFN_GATE_UP) &&
-      (!xq || !x_scales || !w13q || !w13_scales || scale_stride < capacity))
+      (!xq || !x_scales || !w13q || !w13_scales || scale_stride < 1 ||
+       (!scale_src && scale_stride < capacity) || (scale_src && scale_div < 1)))
     return MOE_ERR_INVALID_ARG;
+  if (scale_stride > 0x3fffffffLL) return MOE_ERR_UNSUPPORTED;
   if ((flags & MOE_FFN_DOWN) && (!y || !w2q || !w2_scales)) return MOE_ERR_INVALID_ARG;
   if ((xq && !aligned16(xq)) || (y && !aligned16(y)) || (w13q && !aligned16(w13q)) ||
       (w2q && !aligned16(w2q)))
@@ -227,7 +229,8 @@ int moe_grouped_ffn_w8a8(const uint8_t* xq, const float* x_scales, int64_t scale
   const size_t need = w8a8_workspace_bytes(capacity, num_groups, I);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return MOE_ERR_WORKSPACE;
-  return launch_grouped_ffn_w8a8(xq, x_scales, scale_stride, cu_seqlens, counts, num_groups, H, I,
+  return launch_grouped_ffn_w8a8(xq, x_scales, scale_stride, scale_src, scale_div, cu_seqlens,
+                                 counts, num_groups, H, I,
                                  w13q, w13_scales, w2q, w2_scales, row_scale, y, capacity, flags,
                                  workspace, dev_error, as_stream(stream));
 }

@@ -118,7 +118,8 @@ int launch_quant_rows_fp8(const uint16_t* in, int64_t n_rows, int H, const int32
 // block's row maxima stay inside the workgroup.
 //
 // GATE_UP: A = the permuted rows' codes [cap, Kdim] row-major with scales
-// [Kdim/128][sstride]; writes a's codes in the down GEMM's activation order
+// [Kdim/128][sstride], row r's scales in row smap[r] / sdiv of the scale
+// table (smap NULL: row r itself); writes a's codes in the down GEMM's activation order
 // (per m-tile, m-subtile, K-block and half: 64 lanes x 16 bytes) and a's
 // scales [m-tile][Nout/128][128].  DOWN: A = those; Out = y [cap, Nout]
 // bf16 with the router weight.
@@ -129,6 +130,7 @@ constexpr int kQSub = kQMsub / 2;       // m-subtiles per wave
 template <bool GATE_UP>
 __global__ void __launch_bounds__(kQNW * kWave, 2) w8a8_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ Ascale, int64_t sstride,
+    const int32_t* __restrict__ smap, int sdiv,
     const uint8_t* __restrict__ Wq, const float* __restrict__ Wsc,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ counts, int G, int Kdim,
     int Nw, int Nout, const float* __restrict__ row_scale, uint8_t* __restrict__ OutQ,
@@ -197,11 +199,17 @@ __global__ void __launch_bounds__(kQNW * kWave, 2) w8a8_gemm_kernel(
     }
   }
   const int a_kstride = GATE_UP ? 128 : 2 * kWave * 16;
-  // the K-block's 128 row scales: two 4-byte DMAs by wave 0
-  const float* s_base = GATE_UP ? Ascale + row_base : Ascale + mt_glob * nkb * kBM;
+  // the K-block's 128 row scales: two 4-byte DMAs (rows lane, 64 + lane)
+  // by wave 0, gathered through smap for gate/up
+  const float* s_base = GATE_UP ? Ascale : Ascale + mt_glob * nkb * kBM;
   const int64_t s_kstride = GATE_UP ? sstride : kBM;
-  const uint32_t s_voff0 = (uint32_t)(GATE_UP ? min(lane, valid - 1) : lane) * 4u;
-  const uint32_t s_voff1 = (uint32_t)(GATE_UP ? min(64 + lane, valid - 1) : 64 + lane) * 4u;
+  auto scale_row = [&](int r) -> uint32_t {
+    if (!GATE_UP) return (uint32_t)r;
+    const int64_t pr = row_base + min(r, valid - 1);
+    return (uint32_t)(smap ? smap[pr] / sdiv : pr);
+  };
+  const uint32_t s_voff0 = scale_row(lane) * 4u;
+  const uint32_t s_voff1 = scale_row(64 + lane) * 4u;
 
   const float* tile_scale = nullptr;
   if (!GATE_UP && row_scale) {
@@ -267,19 +275,17 @@ __global__ void __launch_bounds__(kQNW * kWave, 2) w8a8_gemm_kernel(
 #pragma unroll
     for (int s = 0; s < kQPrefetch; ++s) {
       const int kb = kb0 + s;
-      if (kb >= nkb) continue;
+      // past the last K-block (odd counts) only the refill below runs: every
+      // path issues the same loads, so the compiler's waits for the weight
+      // slots stay as loose as the prefetch allows (a path without them
+      // would make it wait for every load at each step)
+      if (kb < nkb) {
       if (kb > 0) stage = (stage + 1 == kQStages) ? 0 : stage + 1;
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAfterDma));
       lds_barrier();
       issue_chunk(min(kb + kQStages - 1, nkb - 1), (stage + kQStages - 1) % kQStages);
-#pragma unroll
-      for (int ii = 0; ii < kQSub; ++ii) {
-        if (ii >= my_live) break;
-        const int i = i0 + ii;
-        const i32x8_t af = __builtin_bit_cast(
-            i32x8_t, __builtin_shufflevector(Aq[stage][2 * i][lane], Aq[stage][2 * i + 1][lane], 0,
-                                             1, 2, 3, 4, 5, 6, 7));
-        const f32x4_t sa = *reinterpret_cast<const f32x4_t*>(&Sa[stage][i * 16 + 4 * (lane >> 4)]);
+      // one m-subtile: its K-block's code products, scaled into acc
+      auto subtile = [&](int ii, const i32x8_t& af, const f32x4_t& sa) {
         f32x4_t t[kQFrags];
 #pragma unroll
         for (int f = 0; f < kQFrags; ++f)
@@ -293,6 +299,35 @@ __global__ void __launch_bounds__(kQNW * kWave, 2) w8a8_gemm_kernel(
 #pragma unroll
           for (int q = 0; q < 4; ++q) acc[ii][f][q] = __builtin_fmaf(t[f][q], c[q], acc[ii][f][q]);
         }
+      };
+      auto a_frag = [&](int i) {
+        return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(Aq[stage][2 * i][lane],
+                                                                   Aq[stage][2 * i + 1][lane], 0,
+                                                                   1, 2, 3, 4, 5, 6, 7));
+      };
+      auto s_frag = [&](int i) {
+        return *reinterpret_cast<const f32x4_t*>(&Sa[stage][i * 16 + 4 * (lane >> 4)]);
+      };
+      if (my_live == kQSub) {
+        // all subtiles live (the common case): straight-line code, every
+        // LDS read first, so the scheduler can overlap one subtile's
+        // scaling with the next subtile's MFMAs
+        i32x8_t af[kQSub];
+        f32x4_t sa[kQSub];
+#pragma unroll
+        for (int ii = 0; ii < kQSub; ++ii) {
+          af[ii] = a_frag(i0 + ii);
+          sa[ii] = s_frag(i0 + ii);
+        }
+#pragma unroll
+        for (int ii = 0; ii < kQSub; ++ii) subtile(ii, af[ii], sa[ii]);
+      } else {
+#pragma unroll
+        for (int ii = 0; ii < kQSub; ++ii) {
+          if (ii >= my_live) break;
+          subtile(ii, a_frag(i0 + ii), s_frag(i0 + ii));
+        }
+      }
       }
       // refill this slot kQPrefetch blocks ahead (past the end: the last again)
       asm volatile("" ::: "memory");
@@ -384,7 +419,7 @@ size_t w8a8_workspace_bytes(int64_t capacity, int G, int I) {
 }
 
 int launch_grouped_ffn_w8a8(const uint8_t* xq, const float* xs, int64_t sstride,
-                            const int32_t* cu_seqlens, const int32_t* counts, int G, int H, int I,
+                            const int32_t* smap, int sdiv, const int32_t* cu_seqlens, const int32_t* counts, int G, int H, int I,
                             const uint8_t* w13q, const float* w13s, const uint8_t* w2q,
                             const float* w2s, const float* row_scale, uint16_t* y,
                             int64_t capacity, int flags, void* workspace, int32_t* dev_error,
@@ -401,14 +436,16 @@ int launch_grouped_ffn_w8a8(const uint8_t* xq, const float* xs, int64_t sstride,
     const int64_t blocks = grid_for((2 * I / 64 + kQTiles - 1) / kQTiles);
     if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(w8a8_gemm_kernel<true>, dim3((unsigned)blocks), dim3(kQNW * kWave), 0,
-                       stream, xq, xs, sstride, w13q, w13s, cu_seqlens, counts, G, H, 2 * I, I,
+                       stream, xq, xs, sstride, smap, sdiv, w13q, w13s, cu_seqlens, counts, G, H,
+                       2 * I, I,
                        nullptr, aq, as, nullptr, capacity, dev_error);
   }
   if (flags & MOE_FFN_DOWN) {
     const int64_t blocks = grid_for((H / 64 + kQTiles - 1) / kQTiles);
     if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(w8a8_gemm_kernel<false>, dim3((unsigned)blocks), dim3(kQNW * kWave), 0,
-                       stream, aq, as, (int64_t)0, w2q, w2s, cu_seqlens, counts, G, I, H, H,
+                       stream, aq, as, (int64_t)0, (const int32_t*)nullptr, 1, w2q, w2s,
+                       cu_seqlens, counts, G, I, H, H,
                        row_scale, nullptr, nullptr, y, capacity, dev_error);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;

@@ -89,12 +89,13 @@ class MoELayer:
         self.w13 = self.w2 = self.shared_w13 = self.shared_w2 = None
         self.packed = False
         self.fp8_weights = False
+        self.w8a8 = False
 
     # ------------------------------------------------------------------ weights
     def set_weights(self, w13: torch.Tensor, w2: torch.Tensor,
                     shared_w13: Optional[torch.Tensor] = None,
                     shared_w2: Optional[torch.Tensor] = None, pack: bool = True,
-                    fp8: bool = False) -> None:
+                    fp8=False) -> None:
         """Device bf16 weights: w13 [E_l, 2I, H], w2 [E_l, H, I] (local experts);
         the shared expert's [2Is, H] and [H, Is] (run as a single group).
 
@@ -103,10 +104,28 @@ class MoELayer:
         row-major tensors are not referenced afterwards.  With ``fp8`` they
         are quantized once instead to E4M3 codes with 128 x 128 tile scales
         (``moe_pack_ffn_weights_fp8``), routed and shared experts alike, and
-        the FFN stages read those (``moe_grouped_ffn_fp8``)."""
+        the FFN stages read those (``moe_grouped_ffn_fp8``).  With
+        ``fp8="w8a8"`` the activations are FP8 too: the dispatch rows are
+        quantized for real (``moe_quant_rows_fp8``, 1 x 128 blocks) before the
+        permute, which moves their codes, and both GEMMs run on the FP8
+        matrix cores (``moe_grouped_ffn_w8a8``); this replaces the dispatch
+        fake-quant.  Requires H % 256 == 0."""
         if shared_w13 is not None and shared_w13.dim() == 2:
             shared_w13, shared_w2 = shared_w13.unsqueeze(0), shared_w2.unsqueeze(0)
-        self.fp8_weights = fp8
+        if fp8 not in (False, True, "w8a8"):
+            raise ValueError(f"unknown fp8 mode {fp8!r}")
+        self.w8a8 = fp8 == "w8a8"
+        self.fp8_weights = bool(fp8)
+        if self.w8a8:
+            self._setup_w8a8()
+            q13, s13, q2, s2 = ops.moe_pack_ffn_weights_fp8(w13, w2, k128=True)
+            self.w13, self.w2 = (q13, s13), (q2, s2)
+            self.shared_w13 = self.shared_w2 = None
+            if shared_w13 is not None:
+                q13, s13, q2, s2 = ops.moe_pack_ffn_weights_fp8(shared_w13, shared_w2, k128=True)
+                self.shared_w13, self.shared_w2 = (q13, s13), (q2, s2)
+            self.packed = True
+            return
         if fp8:
             self.packed = True
             q13, s13, q2, s2 = ops.moe_pack_ffn_weights_fp8(w13, w2)
@@ -124,9 +143,36 @@ class MoELayer:
         self.w13, self.w2 = w13, w2
         self.shared_w13, self.shared_w2 = shared_w13, shared_w2
 
+    def _setup_w8a8(self) -> None:
+        """Buffers of the FP8 path: the [T, H] rows' codes and scales, the
+        permuted codes (moved by the permute as 2-byte units), workspaces."""
+        T, H, K, dev = self.T, self.H, self.K, self.device
+        if H % 256:
+            raise ValueError("the FP8 path needs H % 256 == 0 (codes move as 2-byte units)")
+        if self.dispatch_fp4:
+            raise ValueError("the FP8 path quantizes the dispatch rows itself (no FP4 dispatch)")
+        self.hq = torch.empty(T, H, dtype=torch.uint8, device=dev)
+        self.hs = torch.empty(H // 128, max(T, 1), dtype=torch.float32, device=dev)
+        # the permutation moves the codes: x_perm holds [cap, H] bytes as
+        # [cap, H/2] 2-byte units (the maps are those of any permute)
+        self.perm = ops.alloc_permuted(T, K, H // 2, self.El, self.capacity, dev)
+        self.ffn_ws = torch.empty(
+            max(ops.moe_grouped_ffn_w8a8_workspace_bytes(self.capacity, self.El, H, self.I), 1),
+            dtype=torch.uint8, device=dev)
+        if self.shared_I:
+            self.shared_ws = torch.empty(
+                max(ops.moe_grouped_ffn_w8a8_workspace_bytes(T, 1, H, self.shared_I), 1),
+                dtype=torch.uint8, device=dev)
+
     def _ffn(self, x, cu, counts, w13, w2, row_scale, y, stage, ws, stream=None) -> None:
         """One grouped-FFN call on the weights ``set_weights`` prepared."""
-        if self.fp8_weights:
+        if self.w8a8:
+            # x = (codes [rows, H], scales [H/128, stride], scale_src or None)
+            xq, xs, src = x
+            ops.moe_grouped_ffn_w8a8(xq, xs, cu, counts, w13[0], w13[1], w2[0], w2[1], row_scale,
+                                     y, stage, ws, self.dev_error, stream=stream, scale_src=src,
+                                     scale_div=self.K)
+        elif self.fp8_weights:
             ops.moe_grouped_ffn_fp8(x, cu, counts, w13[0], w13[1], w2[0], w2[1], row_scale, y,
                                     stage, ws, self.dev_error, stream=stream)
         else:
@@ -149,7 +195,21 @@ class MoELayer:
         x = self.hidden_q if self.hidden_q is not None else hidden
         st = [("route", lambda: ops.moe_route(logits, self.K, row_valid, self.renormalize,
                                                self.topk_idx, self.topk_w))]
-        if self.dispatch_fp4:
+        if self.w8a8:
+            # the dispatch quantizer for real: codes + scales of the [T, H]
+            # rows; the permute moves the codes, the GEMM finds each permuted
+            # row's scales through src_of
+            x = self.hq.view(torch.bfloat16)
+            x_ffn = (p.x_perm.view(torch.uint8), self.hs, p.src_of)
+            x_shared = (self.hq, self.hs, None)
+            st.append(("dispatch_quant", lambda: ops.moe_quant_rows_fp8(
+                hidden, None, self.hq, self.hs)))
+        else:
+            x_ffn = p.x_perm
+            x_shared = hidden
+        if self.w8a8:
+            pass                          # replaced by the real quantizer above
+        elif self.dispatch_fp4:
             mode, block = _FP4[self.dispatch_fp4]
             st.append(("dispatch_qdq", lambda: ops.moe_fake_quant_rows(
                 hidden, self.hidden_q, None, mode, block, self.dispatch_scale)))
@@ -160,10 +220,10 @@ class MoELayer:
             self.topk_idx, self.topk_w, x, self.El, self.expert_begin, self.pad_pow2,
             self.capacity, p, self.perm_ws, self.dev_error)))
         st.append(("ffn_gate_up", lambda: self._ffn(
-            p.x_perm, p.cu_seqlens, p.counts, self.w13, self.w2, p.w_perm, self.y_perm,
+            x_ffn, p.cu_seqlens, p.counts, self.w13, self.w2, p.w_perm, self.y_perm,
             ops.MOE_FFN_GATE_UP, self.ffn_ws)))
         st.append(("ffn_down", lambda: self._ffn(
-            p.x_perm, p.cu_seqlens, p.counts, self.w13, self.w2, p.w_perm, self.y_perm,
+            x_ffn, p.cu_seqlens, p.counts, self.w13, self.w2, p.w_perm, self.y_perm,
             ops.MOE_FFN_DOWN, self.ffn_ws)))
         if self.combine_fp4:
             # FP4 combine rows: the routed rows quantized in place (padding
@@ -173,7 +233,7 @@ class MoELayer:
                 self.y_perm, self.y_perm, p.src_of, cmode, cblock, self.combine_scale)))
         if self.shared_I:
             def shared(stream=None):
-                self._ffn(hidden, self.shared_cu, self.shared_counts, self.shared_w13,
+                self._ffn(x_shared, self.shared_cu, self.shared_counts, self.shared_w13,
                           self.shared_w2, None, self.shared_out, ops.MOE_FFN_ALL,
                           self.shared_ws, stream=stream)
 
@@ -182,7 +242,10 @@ class MoELayer:
                     self.side.wait_stream(torch.cuda.current_stream())
                     shared(self.side)
 
-                st.insert(0, ("shared_ffn", fork))
+                # it forks at the start, or (FP8 path) once its input rows
+                # are quantized; the side stream waits for what precedes it
+                at = [n for n, _ in st].index("dispatch_quant") + 1 if self.w8a8 else 0
+                st.insert(at, ("shared_ffn", fork))
                 st.append(("join_shared", lambda: torch.cuda.current_stream().wait_stream(self.side)))
             else:
                 st.append(("shared_ffn", shared))
@@ -229,6 +292,8 @@ class MoELayer:
                  w_perm=p.w_perm, y_perm=self.y_perm, out=self.out)
         if self.hidden_q is not None:
             d["hidden_q"] = self.hidden_q
+        if self.w8a8:
+            d["hidden_codes"], d["hidden_scales"] = self.hq, self.hs
         if self.shared_out is not None:
             d["shared"] = self.shared_out
         return d

@@ -275,9 +275,12 @@ def moe_grouped_ffn_w8a8(xq: torch.Tensor, x_scales: torch.Tensor, cu_seqlens: t
                          row_scale: Optional[torch.Tensor] = None,
                          y: Optional[torch.Tensor] = None, flags: int = MOE_FFN_ALL,
                          workspace: Optional[torch.Tensor] = None,
-                         dev_error: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                         dev_error: Optional[torch.Tensor] = None, stream=None,
+                         scale_src: Optional[torch.Tensor] = None, scale_div: int = 1) -> torch.Tensor:
     """The grouped FFN on FP8 rows (moe_quant_rows_fp8) and FP8 weights
-    (moe_pack_ffn_weights_fp8 with ``k128=True``) on the FP8 matrix cores."""
+    (moe_pack_ffn_weights_fp8 with ``k128=True``) on the FP8 matrix cores.
+    ``scale_src`` / ``scale_div``: row r's scales are those of row
+    ``scale_src[r] // scale_div`` of ``x_scales`` (the permute's src_of and K)."""
     _want(xq, torch.uint8, "xq")
     _want(x_scales, torch.float32, "x_scales")
     _want(w13q, torch.uint8, "w13q")
@@ -293,8 +296,10 @@ def moe_grouped_ffn_w8a8(xq: torch.Tensor, x_scales: torch.Tensor, cu_seqlens: t
     I = two_i // 2
     if H2 != H or tuple(w2q.shape) != (G, H, I):
         raise ValueError("weight shapes do not match xq")
-    if x_scales.shape[0] != H // 128 or x_scales.shape[1] < capacity:
-        raise ValueError("x_scales must be [H/128, >= capacity]")
+    if x_scales.shape[0] != H // 128 or (scale_src is None and x_scales.shape[1] < capacity):
+        raise ValueError("x_scales must be [H/128, >= capacity] (or >= T with scale_src)")
+    if scale_src is not None:
+        _want(scale_src, torch.int32, "scale_src")
     if counts.numel() != G or cu_seqlens.numel() != G + 1:
         raise ValueError("counts / cu_seqlens do not match the number of groups")
     lib = load()
@@ -303,7 +308,8 @@ def moe_grouped_ffn_w8a8(xq: torch.Tensor, x_scales: torch.Tensor, cu_seqlens: t
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=xq.device)
     check("moe_grouped_ffn_w8a8", lib.moe_grouped_ffn_w8a8(
-        _ptr(xq), _ptr(x_scales), x_scales.shape[1], _ptr(cu_seqlens), _ptr(counts), G, H, I,
+        _ptr(xq), _ptr(x_scales), x_scales.shape[1], _ptr(scale_src), scale_div, _ptr(cu_seqlens),
+        _ptr(counts), G, H, I,
         _ptr(w13q), _ptr(w13_scales), _ptr(w2q), _ptr(w2_scales), _ptr(row_scale), _ptr(y),
         capacity, flags, _ptr(workspace), workspace.numel(), _ptr(dev_error), _stream(stream)))
     return y

@@ -130,6 +130,8 @@ int moe_route(const float* logits, const uint8_t* row_valid, int T, int E, int K
  *                  written
  *
  *   topk_idx [T, K] int32   topk_w [T, K] float32   hidden [T, H] bf16
+ *   (rows are copied as opaque 2-byte units, so any 2H-byte row payload can
+ *   be permuted this way — FP8 codes of 2H channels, for instance)
  *   counts [E_l] int32, cu_seqlens [E_l + 1] int32, row_of [T*K] int32,
  *   src_of [capacity] int32, w_perm [capacity] float32,
  *   x_perm [capacity, H] bf16 — all outputs.
@@ -257,7 +259,13 @@ int moe_quant_rows_fp8(const uint16_t* in, int64_t n_rows, int H, const int32_t*
  * with every K-block's code products summed by the matrix cores in float32
  * and scaled into a float32 accumulator.
  *   xq [capacity, H] uint8 and x_scales (K-block-major, stride
- *     scale_stride >= capacity) from moe_quant_rows_fp8;
+ *     scale_stride) from moe_quant_rows_fp8.  With scale_src NULL, row r's
+ *     scales are x_scales[kb * scale_stride + r] (scale_stride >= capacity);
+ *     otherwise row r's are those of row scale_src[r] / scale_div
+ *     (scale_div >= 1) — moe_permute's src_of and K, so that the scales of
+ *     the unpermuted [T, H] rows serve the permuted codes, which moe_permute
+ *     moves like any other row payload; scale_stride must then exceed every
+ *     such row (>= T);
  *   w13q / w2q and their tile scales from moe_pack_ffn_weights_fp8 with
  *     MOE_FP8_LAYOUT_K128; row_scale, y, cu_seqlens, counts, capacity as in
  *     moe_grouped_ffn.
@@ -267,7 +275,7 @@ int moe_quant_rows_fp8(const uint16_t* in, int64_t n_rows, int H, const int32_t*
  * MOE_DEVERR_ROW_RANGE.  Requires H % 128 == 0, I % 128 == 0, G <= 1024. */
 size_t moe_grouped_ffn_w8a8_workspace_bytes(int64_t capacity, int num_groups, int H, int I);
 int moe_grouped_ffn_w8a8(const uint8_t* xq, const float* x_scales, int64_t scale_stride,
-                         const int32_t* cu_seqlens, const int32_t* counts, int num_groups, int H,
+                         const int32_t* scale_src, int scale_div, const int32_t* cu_seqlens, const int32_t* counts, int num_groups, int H,
                          int I, const uint8_t* w13q, const float* w13_scales, const uint8_t* w2q,
                          const float* w2_scales, const float* row_scale, uint16_t* y,
                          int64_t capacity, int flags, void* workspace, size_t workspace_bytes,

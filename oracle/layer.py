@@ -22,7 +22,12 @@ Readings where the pages are silent:
   is calibrated from this batch's own rows (max calibration);
 * FP8 expert weights (128 x 128 tile scales, the "DeepEP + DeepGEMM" review
   thread) enter the FFN as their dequantized values, for the routed and the
-  shared experts alike.
+  shared experts alike;
+* the real FP8 path (``fp8_gemm``) quantizes every row of the layer input
+  per 1 x 128 block (the dispatch quantizer of the low-latency dispatch
+  thread, handing over codes and scales), which replaces the dispatch
+  fake-quant; routed and shared experts run the FP8 FFN of ``fp8_gemm.py``
+  on those codes.
 """
 
 import numpy as np
@@ -34,6 +39,7 @@ from .quant import (fake_quant_block, fake_quant_per_tensor, calibrate_amax, sca
 from .fp4 import fake_quant_mxfp4, fake_quant_nvfp4, nvfp4_tensor_scale
 from .permute import permute
 from .ffn import grouped_ffn, expert_ffn
+from .fp8_gemm import quantize_rows_fp8, grouped_ffn_w8a8, expert_ffn_w8a8
 from .combine import combine
 
 
@@ -51,7 +57,8 @@ def moe_layer(logits, hidden_bits, weights, k: int, row_valid=None,
               renormalize: bool = True, dispatch_block=None, pad_pow2=False,
               shared_weights=None, combine_qdq: bool = False, combine_scale=None,
               expert_begin: int = 0, num_local_experts=None, dispatch_fp4=None,
-              dispatch_scale=None, combine_fp4=None, fp8_weights: bool = False):
+              dispatch_scale=None, combine_fp4=None, fp8_weights: bool = False,
+              fp8_gemm: bool = False):
     """Run the oracle layer and return every intermediate in a dict.
 
     ``weights(e)`` returns expert ``e``'s ``(w13, w2)`` as bfloat16 bits
@@ -61,7 +68,9 @@ def moe_layer(logits, hidden_bits, weights, k: int, row_valid=None,
     (``dispatch_scale``, ``combine_scale``) is calibrated like the FP8
     combine scale: ``amax / (6 * 448)`` over the rows the quantizer sees.
     ``fp8_weights``: every expert weight matrix is replaced by its FP8
-    fake-quant with one scale per 128 x 128 tile.
+    fake-quant with one scale per 128 x 128 tile.  ``fp8_gemm``: the real FP8
+    path (rows and weights as codes with block scales; see the module
+    readings).
     """
     if fp8_weights:
         def deq(w):
@@ -80,7 +89,13 @@ def moe_layer(logits, hidden_bits, weights, k: int, row_valid=None,
     valid_tok = (topk_idx >= 0).any(axis=1)
 
     dscale = None
-    if dispatch_fp4 == "mxfp4":
+    hq = hs = None
+    if fp8_gemm:
+        if dispatch_fp4:
+            raise ValueError("the FP8 path has its own dispatch quantizer")
+        hq, hs = quantize_rows_fp8(hidden_bits)
+        hidden_q, dscales = hidden_bits, hs
+    elif dispatch_fp4 == "mxfp4":
         hidden_q, dscales = fake_quant_mxfp4(hidden_bits, row_mask=valid_tok)
     elif dispatch_fp4 == "nvfp4":
         dscale = (nvfp4_tensor_scale(calibrate_amax(hidden_bits, valid_tok))
@@ -92,8 +107,16 @@ def moe_layer(logits, hidden_bits, weights, k: int, row_valid=None,
         hidden_q, dscales = hidden_bits, None
 
     perm = permute(topk_idx, topk_w, hidden_q, El, expert_begin, pad_pow2)
-    y = grouped_ffn(perm["x_perm"], perm["cu_seqlens"], perm["counts"],
-                    lambda e: weights(e + expert_begin), row_scale=perm["w_perm"])
+    if fp8_gemm:
+        src = perm["src_of"]
+        tok = np.where(src >= 0, src // k, 0)
+        qx = np.where((src >= 0)[:, None], hq[tok], 0.0)
+        sx = np.where((src >= 0)[:, None], hs[tok], np.float32(0))
+        y = grouped_ffn_w8a8(qx, sx, perm["cu_seqlens"], perm["counts"],
+                             lambda e: weights(e + expert_begin), row_scale=perm["w_perm"])
+    else:
+        y = grouped_ffn(perm["x_perm"], perm["cu_seqlens"], perm["counts"],
+                        lambda e: weights(e + expert_begin), row_scale=perm["w_perm"])
     rows = _rows_to_bf16(y)
     routed_rows = perm["src_of"] >= 0
 
@@ -115,7 +138,10 @@ def moe_layer(logits, hidden_bits, weights, k: int, row_valid=None,
     shared = None
     if shared_weights is not None:
         s13, s2 = shared_weights
-        shared = _rows_to_bf16(expert_ffn(bf16_bits_to_f64(hidden_bits), s13, s2))
+        if fp8_gemm:
+            shared = _rows_to_bf16(expert_ffn_w8a8(hq, hs, s13, s2))
+        else:
+            shared = _rows_to_bf16(expert_ffn(bf16_bits_to_f64(hidden_bits), s13, s2))
 
     out = combine(rows_q, perm["row_of"], T, k, shared)
     return {

@@ -60,7 +60,7 @@ def test_host_only_entry_points():
                                         None) == -1                              # unknown flag
     assert lib.moe_quant_rows_fp8(None, 0, 256, None, None, None, 0, None) == 0  # no rows
     assert lib.moe_quant_rows_fp8(None, 4, 256, None, None, None, 2, None) == -1  # stride < rows
-    assert lib.moe_grouped_ffn_w8a8(None, None, 0, None, None, 4, 256, 128, None, None, None,
-                                    None, None, None, 16, 3, None, 0, None, None) == -1
+    assert lib.moe_grouped_ffn_w8a8(None, None, 0, None, 1, None, None, 4, 256, 128, None, None,
+                                    None, None, None, None, 16, 3, None, 0, None, None) == -1
     assert lib.moe_combine(None, 0, None, None, 0, 1, 128, None, None, None, None) == 0  # T = 0
     assert lib.moe_copy_bytes(None, None, 15, None) == -1

@@ -239,6 +239,46 @@ def test_layer_fp8_weights(variant):
     print(f"{variant}: FP8-weight layer rel err {err:.3e}")
 
 
+@pytest.mark.parametrize("variant", ["tiny_everything", "mid_skewed_shared"])
+def test_layer_fp8_gemm(variant):
+    """The real FP8 path (rows and weights as E4M3 codes, FP8 matrix cores)
+    against the oracle layer's FP8 path: the layer input's codes and scales
+    bit-exact, routing and permute maps exact, the output within 2e-2.  The
+    shared expert runs concurrently from the quantized rows."""
+    base = workloads.CONFIGS["tiny"]
+    cfg = {
+        "tiny_everything": base.with_(pad_rows=5, dispatch_block=128, pad_pow2=True,
+                                      shared_I=256, combine_qdq=True),
+        "mid_skewed_shared": workloads.MoEConfig("mid", 32, T=300, H=512, E=16, K=4, I=256,
+                                                 hot_experts=4, shared_I=128),
+    }[variant]
+    W = Weights(cfg)
+    lg, hd, vd = workloads.logits(cfg), workloads.hidden(cfg), workloads.row_valid(cfg)
+    ref = oracle.moe_layer(lg, hd, lambda e: W.host[e], cfg.K, vd, pad_pow2=cfg.pad_pow2,
+                           shared_weights=W.shared_host, combine_qdq=cfg.combine_qdq,
+                           fp8_gemm=True)
+    layer = MoELayer(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, "cuda", shared_I=cfg.shared_I,
+                     dispatch_block=cfg.dispatch_block, combine_qdq=cfg.combine_qdq,
+                     pad_pow2=cfg.pad_pow2)
+    layer.set_weights(W.w13, W.w2, *(W.shared or (None, None)), fp8="w8a8")
+    if cfg.combine_qdq:
+        layer.combine_scale.fill_(float(ref["combine_scale"]))
+    layer.forward(dev(lg), dev_bf16(hd), None if vd is None else dev(vd))
+    torch.cuda.synchronize()
+    assert layer.dev_error.item() == 0
+    q_want, s_want = oracle.quantize_rows_fp8(hd)
+    outs = layer.stage_outputs()
+    np.testing.assert_array_equal(host(outs["hidden_scales"]).T.view(np.uint32),
+                                  s_want.view(np.uint32))
+    c = host(outs["hidden_codes"]).astype(np.int64)      # E4M3 bit fields, bias 7
+    assert not np.any((c & 0x7F) == 0x7F)
+    e, m = (c >> 3) & 0xF, c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    np.testing.assert_array_equal(np.where(c & 0x80, -mag, mag), q_want)
+    err = _check_layer(cfg, layer, ref, vd)
+    print(f"{variant}: FP8-path layer rel err {err:.3e}")
+
+
 def _sampled(cfg, n_tok, scale=None, seed=0):
     rng = np.random.default_rng(seed)
     lg, hd, vd = workloads.logits(cfg), workloads.hidden(cfg), workloads.row_valid(cfg)

@@ -24,11 +24,18 @@
 //      w_perm for its slots and copies each token row once from HBM into
 //      its K destination rows with 16-byte vector loads and stores; the
 //      workgroups also mark the unused rows up to `capacity`.
+// When the chunk table is small (at most kFuseTable entries: a few
+// thousand routed slots), launch 2 is folded into launch 3: every scatter
+// workgroup scans the table itself from LDS (a few hundred integers), and
+// workgroup 0 writes counts and cu_seqlens — one kernel launch less on the
+// latency-bound small batches.
 #include "common.h"
 
 namespace moe {
 
 constexpr int kChunk = 1024;
+constexpr int kFuseTable = 4096;   // chunk-table entries up to which the scan is fused
+constexpr int kFuseChunks = 16;    // ... and chunks (each workgroup sums its table columns)
 
 __global__ void __launch_bounds__(256) permute_chunk_rank_kernel(
     const int32_t* __restrict__ topk_idx, int64_t TK, int expert_begin, int El, int nbits,
@@ -170,18 +177,89 @@ __global__ void __launch_bounds__(1024) permute_scan_kernel(
   }
 }
 
+// FUSED: `table` holds the chunk_rank totals and the workgroup does the
+// scan's work itself (see the file comment); otherwise `table` holds the
+// absolute first row of every (chunk, expert) pair written by the scan.
+template <bool FUSED>
 __global__ void __launch_bounds__(256) permute_scatter_kernel(
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
     const uint16_t* __restrict__ hidden, int T, int K, int H, int expert_begin, int El,
-    int tok_per_block, int64_t capacity, const int32_t* __restrict__ table,
-    const int32_t* __restrict__ rank, uint16_t* __restrict__ x_perm, int32_t* __restrict__ row_of,
-    int32_t* __restrict__ src_of, float* __restrict__ w_perm, int32_t* __restrict__ dev_error,
-    const int32_t* __restrict__ cu_seqlens) {
+    int tok_per_block, int64_t capacity, const int32_t* __restrict__ table, int nchunks,
+    int pad_pow2, const int32_t* __restrict__ rank, uint16_t* __restrict__ x_perm,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ src_of, float* __restrict__ w_perm,
+    int32_t* __restrict__ dev_error, int32_t* __restrict__ counts,
+    int32_t* __restrict__ cu_seqlens) {
   __shared__ int32_t dest[256];
+  __shared__ int32_t s_tab[FUSED ? kFuseTable : 1];
+  __shared__ int32_t s_start[FUSED ? 1024 : 1];
+  __shared__ int32_t s_tot[FUSED ? 1024 : 1];
+  __shared__ int32_t s_size[FUSED ? 1024 : 1];
+  __shared__ int32_t s_wave[4];
   const int tid = threadIdx.x;
+  int64_t used_end;   // end of the last segment
+  if (FUSED) {
+    const int n = nchunks * El;
+    for (int j = tid; j < n; j += blockDim.x) s_tab[j] = table[j];
+    __syncthreads();
+    // each thread owns experts 4 tid .. 4 tid + 3 (El <= 1024): totals,
+    // sizes, then a block-wide exclusive scan of the sizes
+    int tot[4], sz[4], local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * tid + j;
+      tot[j] = 0;
+      if (e < El)
+        for (int c = 0; c < nchunks; ++c) tot[j] += s_tab[c * El + e];
+      sz[j] = (e < El) ? (pad_pow2 ? next_pow2_dev(tot[j]) : tot[j]) : 0;
+      local += sz[j];
+    }
+    const int lane = tid & 63, wid = tid >> 6;
+    int x = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, kWave);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wave[wid] = x;
+    __syncthreads();
+    int before = x - local;
+    for (int q = 0; q < wid; ++q) before += s_wave[q];
+    const int grand = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+    int run = before;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * tid + j;
+      if (e < El) {
+        s_start[e] = run;
+        s_tot[e] = tot[j];
+        s_size[e] = sz[j];
+        if (blockIdx.x == 0) {
+          counts[e] = tot[j];
+          cu_seqlens[e] = run;
+        }
+      }
+      run += sz[j];
+    }
+    if (blockIdx.x == 0 && tid == 0) {
+      cu_seqlens[El] = grand;
+      if ((int64_t)grand > capacity) raise_error(dev_error, MOE_DEVERR_CAPACITY);
+    }
+    __syncthreads();
+    // pow2 padding rows: workgroup b marks those of experts b, b + grid, ...
+    if (pad_pow2)
+      for (int e = blockIdx.x; e < El; e += gridDim.x)
+        for (int r = s_start[e] + s_tot[e] + tid; r < s_start[e] + s_size[e] && (int64_t)r < capacity;
+             r += blockDim.x) {
+          src_of[r] = -1;
+          w_perm[r] = 0.0f;
+        }
+    used_end = grand;
+  } else {
+    used_end = cu_seqlens[El];
+  }
   // rows past the last segment are unused: mark them as well, so that every
   // row of the caller's buffer has a defined src_of and w_perm
-  for (int64_t r = (int64_t)cu_seqlens[El] + (int64_t)blockIdx.x * blockDim.x + tid; r < capacity;
+  for (int64_t r = used_end + (int64_t)blockIdx.x * blockDim.x + tid; r < capacity;
        r += (int64_t)gridDim.x * blockDim.x) {
     src_of[r] = -1;
     w_perm[r] = 0.0f;
@@ -196,7 +274,14 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
       const int rk = rank[i];
       if (rk >= 0) {
         const int e = topk_idx[i] - expert_begin;
-        const int64_t rr = (int64_t)table[(i / kChunk) * El + e] + rk;
+        int64_t first;   // absolute first row of (chunk of i, e)
+        if (FUSED) {
+          first = s_start[e];
+          for (int c = 0; c < (int)(i / kChunk); ++c) first += s_tab[c * El + e];
+        } else {
+          first = table[(i / kChunk) * El + e];
+        }
+        const int64_t rr = first + rk;
         if (rr < capacity) {
           r = (int)rr;
           src_of[r] = (int32_t)i;
@@ -252,18 +337,25 @@ int launch_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t*
   if (nchunks > 0)
     hipLaunchKernelGGL(permute_chunk_rank_kernel, dim3(nchunks), dim3(256), 0, stream, topk_idx,
                        TK, expert_begin, El, nbits, table, rank);
-  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, stream, table, nchunks, El,
-                     pad_pow2, capacity, counts, cu_seqlens, src_of, w_perm, dev_error);
-  if (T > 0 || capacity > 0) {
-    const int nvec = H / 8;
-    int tpb = 256 / nvec;
-    if (tpb < 1) tpb = 1;
-    if (tpb * K > 256) tpb = 256 / K;
-    const int grid = T > 0 ? (T + tpb - 1) / tpb : 1;
-    hipLaunchKernelGGL(permute_scatter_kernel, dim3(grid), dim3(256), 0, stream, topk_idx, topk_w,
-                       hidden, T, K, H, expert_begin, El, tpb, capacity, table, rank, x_perm,
-                       row_of, src_of, w_perm, dev_error, cu_seqlens);
-  }
+  const bool fused = (int64_t)nchunks * El <= kFuseTable && nchunks <= kFuseChunks && El <= 1024;
+  if (!fused)
+    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, stream, table, nchunks, El,
+                       pad_pow2, capacity, counts, cu_seqlens, src_of, w_perm, dev_error);
+  const int nvec = H / 8;
+  int tpb = 256 / nvec;
+  if (tpb < 1) tpb = 1;
+  if (tpb * K > 256) tpb = 256 / K;
+  const int grid = T > 0 ? (T + tpb - 1) / tpb : 1;
+  if (fused)
+    hipLaunchKernelGGL(permute_scatter_kernel<true>, dim3(grid), dim3(256), 0, stream, topk_idx,
+                       topk_w, hidden, T, K, H, expert_begin, El, tpb, capacity, table, nchunks,
+                       pad_pow2, rank, x_perm, row_of, src_of, w_perm, dev_error, counts,
+                       cu_seqlens);
+  else if (T > 0 || capacity > 0)
+    hipLaunchKernelGGL(permute_scatter_kernel<false>, dim3(grid), dim3(256), 0, stream, topk_idx,
+                       topk_w, hidden, T, K, H, expert_begin, El, tpb, capacity, table, nchunks,
+                       pad_pow2, rank, x_perm, row_of, src_of, w_perm, dev_error, counts,
+                       cu_seqlens);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -279,6 +279,58 @@ def test_layer_fp8_gemm(variant):
     print(f"{variant}: FP8-path layer rel err {err:.3e}")
 
 
+@pytest.mark.parametrize("fp8", [True, "w8a8"])
+def test_layer_fp8_modes_expert_parallel_share(fp8):
+    """One rank's share of experts [3, 7) of 8 with FP8 weights / the FP8
+    path: only its slots are combined, against the oracle's matching mode."""
+    cfg = workloads.CONFIGS["tiny"]
+    W = Weights(cfg)
+    lg, hd = workloads.logits(cfg), workloads.hidden(cfg)
+    layer = MoELayer(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, "cuda", expert_begin=3,
+                     num_local_experts=4)
+    layer.set_weights(W.w13[3:7], W.w2[3:7], fp8=fp8)
+    layer.forward(dev(lg), dev_bf16(hd))
+    torch.cuda.synchronize()
+    assert layer.dev_error.item() == 0
+    ref = oracle.moe_layer(lg, hd, lambda e: W.host[e], cfg.K, None, expert_begin=3,
+                           num_local_experts=4, fp8_weights=fp8 is True,
+                           fp8_gemm=fp8 == "w8a8")
+    _check_layer(cfg, layer, ref, None)
+
+
+@pytest.mark.parametrize("fp8", [True, "w8a8"])
+def test_layer_fp8_modes_graph_replay_matches_eager(fp8):
+    """The FP8 modes captured once into a HIP graph (the shared expert on its
+    side stream, forked after the quantizer on the FP8 path) and replayed
+    several times with eager work in between give the eager bits."""
+    cfg = workloads.CONFIGS["tiny"].with_(shared_I=128, combine_qdq=True, pad_rows=3)
+    W = Weights(cfg)
+    lg, hd = dev(workloads.logits(cfg)), dev_bf16(workloads.hidden(cfg))
+    vd = dev(workloads.row_valid(cfg))
+    layer = MoELayer(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, "cuda", shared_I=cfg.shared_I,
+                     combine_qdq=True)
+    layer.set_weights(W.w13, W.w2, *W.shared, fp8=fp8)
+    layer.calibrate_combine_scale(lg, hd, vd)
+    eager = layer.forward(lg, hd, vd).clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward(lg, hd, vd)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(lg, hd, vd)
+    for i in range(4):
+        layer.out.zero_()
+        layer.y_perm.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.out.view(torch.int16), eager.view(torch.int16)), i
+        layer.forward(lg, hd, vd)
+        torch.cuda.synchronize()
+    assert layer.dev_error.item() == 0
+
+
 def _sampled(cfg, n_tok, scale=None, seed=0):
     rng = np.random.default_rng(seed)
     lg, hd, vd = workloads.logits(cfg), workloads.hidden(cfg), workloads.row_valid(cfg)

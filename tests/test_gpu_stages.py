@@ -338,7 +338,10 @@ def test_combine_random_rows(T, K, H):
     shared = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     _combine_case(rows, row_of, T, K)
     _combine_case(rows, row_of, T, K, shared)
-    _combine_case(rows, row_of, T, K, shared, scale=float(np.float32(3.0 / 448)))
+    # fused QDQ: a typical scale, an arbitrary one, and one outside the
+    # reciprocal's exact range (the kernel then divides)
+    for s in (3.0 / 448, 0.0123, 1e-30):
+        _combine_case(rows, row_of, T, K, shared, scale=float(np.float32(s)))
     # slot-major [K, T, H] layout: row_of[t*K + k] = k*T + t
     t_idx, k_idx = np.divmod(np.arange(T * K), K)
     _combine_case(rows, (k_idx * T + t_idx).astype(np.int32), T, K, shared)

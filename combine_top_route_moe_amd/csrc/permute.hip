@@ -28,7 +28,10 @@
 // thousand routed slots), launch 2 is folded into launch 3: every scatter
 // workgroup scans the table itself from LDS (a few hundred integers), and
 // workgroup 0 writes counts and cu_seqlens — one kernel launch less on the
-// latency-bound small batches.
+// latency-bound small batches.  At most kSmallTK slots, all three are one
+// launch, permute_small_kernel: every workgroup counts all the slots itself
+// (two LDS histograms), which for a few thousand slots costs less than the
+// launches and dependent round trips to memory it saves.
 #include "common.h"
 
 namespace moe {
@@ -313,6 +316,185 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
   }
 }
 
+// The whole permute in one launch, for at most kSmallTK slots and 1024 local
+// experts.  Every workgroup loads all the slot ids and its own tokens' rows
+// at once (neither depends on anything else).  It needs only the per-expert
+// totals and the ranks of its own slots, so it builds two histograms in LDS
+// (no-return atomic adds): of all slots, and of the slots before its first
+// one.  An own slot's rank is the second histogram's count for its expert
+// plus the same-expert own slots before it — its position among the
+// expert's slots in flat-index order, as the multi-launch path ranks them.
+// It then scans the totals as the fused scatter does and copies its tokens'
+// rows to their destinations: one round trip to memory instead of the three
+// of rank -> table -> rows.  Workgroup 0 writes counts and cu_seqlens.
+constexpr int kSmallTK = 4096;
+constexpr int kSmallIds = kSmallTK / 256;          // slot ids per thread
+constexpr int kSmallPre = 4;                       // row vectors per thread loaded up front
+
+__global__ void __launch_bounds__(256) permute_small_kernel(
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
+    const uint16_t* __restrict__ hidden, int T, int K, int H, int expert_begin, int El,
+    int tok_per_block, int pad_pow2, int64_t capacity, uint16_t* __restrict__ x_perm,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ src_of, float* __restrict__ w_perm,
+    int32_t* __restrict__ dev_error, int32_t* __restrict__ counts,
+    int32_t* __restrict__ cu_seqlens) {
+  __shared__ int32_t hist[1024], hist_pre[1024];
+  __shared__ int32_t s_start[1024], s_tot[1024], s_size[1024];
+  __shared__ int32_t own_e[256], dest[256];
+  __shared__ int32_t s_wave[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int TK = T * K;
+  const int t0 = blockIdx.x * tok_per_block;
+  const int i0 = t0 * K;                                   // first slot of this workgroup
+  const int nslots = max(0, min(tok_per_block * K, TK - i0));
+  const int nvec = H / 8;
+  const int total = max(0, min(tok_per_block, T - t0)) * nvec;  // row vectors to copy
+  // the local expert of a slot id, or -1 (padding, or another rank's expert)
+  auto local_expert = [&](int id) {
+    const int le = id - expert_begin;
+    return (id >= 0 && le >= 0 && le < El) ? le : -1;
+  };
+
+  // loads that depend on nothing: the tokens' rows, every slot id, own slots
+  uint4 pre[kSmallPre];
+#pragma unroll
+  for (int j = 0; j < kSmallPre; ++j) {
+    const int idx = tid + j * 256;
+    pre[j] = make_uint4(0, 0, 0, 0);
+    if (idx < total) {
+      const int tl = idx / nvec, c = idx - tl * nvec;
+      pre[j] = reinterpret_cast<const uint4*>(hidden + (int64_t)(t0 + tl) * H)[c];
+    }
+  }
+  int ids[kSmallIds];
+#pragma unroll
+  for (int q = 0; q < kSmallIds; ++q) {
+    const int i = tid + q * 256;
+    ids[q] = i < TK ? topk_idx[i] : -1;
+  }
+  const int own_id = tid < nslots ? topk_idx[i0 + tid] : -1;
+  const float wt = tid < nslots ? topk_w[i0 + tid] : 0.0f;
+
+  for (int e = tid; e < El; e += 256) {
+    hist[e] = 0;
+    hist_pre[e] = 0;
+  }
+  if (tid < 256) own_e[tid] = local_expert(own_id);
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kSmallIds; ++q) {
+    const int i = tid + q * 256;
+    const int e = local_expert(ids[q]);
+    if (e >= 0) {
+      atomicAdd(&hist[e], 1);
+      if (i < i0) atomicAdd(&hist_pre[e], 1);
+    }
+  }
+  __syncthreads();
+
+  // per-expert totals and sizes (thread tid owns experts 4 tid .. 4 tid + 3),
+  // then a block-wide exclusive scan of the sizes
+  int tot[4], sz[4], local = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * tid + j;
+    tot[j] = e < El ? hist[e] : 0;
+    sz[j] = e < El ? (pad_pow2 ? next_pow2_dev(tot[j]) : tot[j]) : 0;
+    local += sz[j];
+  }
+  int x = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_wave[w] = x;
+  __syncthreads();
+  int run = x - local;
+  for (int q = 0; q < w; ++q) run += s_wave[q];
+  const int grand = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * tid + j;
+    if (e < El) {
+      s_start[e] = run;
+      s_tot[e] = tot[j];
+      s_size[e] = sz[j];
+      if (blockIdx.x == 0) {
+        counts[e] = tot[j];
+        cu_seqlens[e] = run;
+      }
+    }
+    run += sz[j];
+  }
+  if (blockIdx.x == 0 && tid == 0) {
+    cu_seqlens[El] = grand;
+    if ((int64_t)grand > capacity) raise_error(dev_error, MOE_DEVERR_CAPACITY);
+  }
+  __syncthreads();
+  // pow2 padding rows (workgroup b marks those of experts b, b + grid, ...)
+  // and the rows past the last segment
+  if (pad_pow2)
+    for (int e = blockIdx.x; e < El; e += gridDim.x)
+      for (int r = s_start[e] + s_tot[e] + tid; r < s_start[e] + s_size[e] && (int64_t)r < capacity;
+           r += blockDim.x) {
+        src_of[r] = -1;
+        w_perm[r] = 0.0f;
+      }
+  for (int64_t r = grand + (int64_t)blockIdx.x * blockDim.x + tid; r < capacity;
+       r += (int64_t)gridDim.x * blockDim.x) {
+    src_of[r] = -1;
+    w_perm[r] = 0.0f;
+  }
+
+  // destinations of the own slots: segment start + rank among the earlier
+  // slots of the same expert (those before the workgroup's first slot, then
+  // the own slots before this one)
+  if (tid < tok_per_block * K) {
+    int r = -1;
+    if (tid < nslots) {
+      const int e = own_e[tid];
+      if (e >= 0) {
+        int rk = hist_pre[e];
+        for (int m = 0; m < tid; ++m) rk += own_e[m] == e;
+        const int64_t rr = (int64_t)s_start[e] + rk;
+        if (rr < capacity) {
+          r = (int)rr;
+          src_of[r] = i0 + tid;
+          w_perm[r] = wt;
+        } else {
+          raise_error(dev_error, MOE_DEVERR_CAPACITY);
+        }
+      }
+      row_of[i0 + tid] = r;
+    }
+    dest[tid] = r;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kSmallPre; ++j) {
+    const int idx = tid + j * 256;
+    if (idx < total) {
+      const int tl = idx / nvec, c = idx - tl * nvec;
+      for (int k = 0; k < K; ++k) {
+        const int r = dest[tl * K + k];
+        if (r >= 0) reinterpret_cast<uint4*>(x_perm + (int64_t)r * H)[c] = pre[j];
+      }
+    }
+  }
+  for (int idx = tid + kSmallPre * 256; idx < total; idx += 256) {  // rows past the preload
+    const int tl = idx / nvec, c = idx - tl * nvec;
+    bool any = false;
+    for (int k = 0; k < K; ++k) any |= dest[tl * K + k] >= 0;
+    if (!any) continue;
+    const uint4 val = reinterpret_cast<const uint4*>(hidden + (int64_t)(t0 + tl) * H)[c];
+    for (int k = 0; k < K; ++k) {
+      const int r = dest[tl * K + k];
+      if (r >= 0) reinterpret_cast<uint4*>(x_perm + (int64_t)r * H)[c] = val;
+    }
+  }
+}
+
 size_t permute_workspace_bytes(int64_t TK, int El) {
   const int64_t nchunks = (TK + kChunk - 1) / kChunk;
   size_t table = (size_t)nchunks * El * sizeof(int32_t);
@@ -334,6 +516,17 @@ int launch_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t*
   int nbits = 1;
   while ((1 << nbits) < El) ++nbits;
 
+  const int nvec = H / 8;
+  int tpb = 256 / nvec;
+  if (tpb < 1) tpb = 1;
+  if (tpb * K > 256) tpb = 256 / K;
+  const int grid = T > 0 ? (T + tpb - 1) / tpb : 1;
+  if (TK <= kSmallTK && El <= 1024) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(grid), dim3(256), 0, stream, topk_idx, topk_w,
+                       hidden, T, K, H, expert_begin, El, tpb, pad_pow2, capacity, x_perm,
+                       row_of, src_of, w_perm, dev_error, counts, cu_seqlens);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
   if (nchunks > 0)
     hipLaunchKernelGGL(permute_chunk_rank_kernel, dim3(nchunks), dim3(256), 0, stream, topk_idx,
                        TK, expert_begin, El, nbits, table, rank);
@@ -341,11 +534,6 @@ int launch_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t*
   if (!fused)
     hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, stream, table, nchunks, El,
                        pad_pow2, capacity, counts, cu_seqlens, src_of, w_perm, dev_error);
-  const int nvec = H / 8;
-  int tpb = 256 / nvec;
-  if (tpb < 1) tpb = 1;
-  if (tpb * K > 256) tpb = 256 / K;
-  const int grid = T > 0 ? (T + tpb - 1) / tpb : 1;
   if (fused)
     hipLaunchKernelGGL(permute_scatter_kernel<true>, dim3(grid), dim3(256), 0, stream, topk_idx,
                        topk_w, hidden, T, K, H, expert_begin, El, tpb, capacity, table, nchunks,

@@ -274,6 +274,26 @@ def test_permute_edge_cases(seed):
         _permute_case(idx, w, hid, E // 2, E // 4, True)
 
 
+@pytest.mark.parametrize("T,K,E,H,El,begin", [
+    (512, 8, 1024, 128, 1024, 0),      # 4096 slots: the single-launch path at its limit
+    (513, 8, 64, 128, 64, 0),          # 4104 slots: the multi-launch path
+    (4096, 1, 5, 128, 5, 0),           # one slot per token
+    (500, 8, 2000, 128, 1000, 500),    # an expert-parallel share of 1000 experts
+    (100, 8, 2048, 128, 1024, 1024),   # the upper half of 2048 experts (1024 is the limit)
+    (3, 2, 4, 8320, 4, 0),             # rows wider than the single launch's up-front loads
+])
+def test_permute_launch_path_boundaries(T, K, E, H, El, begin):
+    """Either side of the single-launch permute's limits (4096 slots, 4 row
+    vectors per thread loaded up front), and at the 1024-local-expert limit:
+    bit-exact."""
+    rng = np.random.default_rng(T * K + E)
+    idx = rng.integers(-1, E, size=(T, K)).astype(np.int32)
+    w = rng.random((T, K)).astype(np.float32)
+    hid = rng.integers(0, 2 ** 16, size=(T, H), dtype=np.uint64).astype(np.uint16)
+    for pow2 in (False, True):
+        _permute_case(idx, w, hid, El, begin, pow2)
+
+
 def test_permute_capacity_overflow_is_flagged_not_written():
     rng = np.random.default_rng(9)
     T, K, E, H = 64, 4, 8, 128

@@ -255,7 +255,7 @@ __device__ __forceinline__ void frag_gemm_body(
     const uint16_t* a_base, const int64_t* a_uoff, const uint32_t* a_voff, int a_chunk_stride,
     int w, int lane, int nks, int nlive,
     int valid, int ct, bool ct_ok, int64_t row_base, int64_t mt_glob, int Nout,
-    const float* tile_scale, uint16_t* __restrict__ Out, int crot) {
+    const float* tile_scale, uint16_t* __restrict__ Out, int crot, bool prio) {
   constexpr int kDmaPerWave = kStageBlocks / NW;
   // every workgroup walks K from its own starting chunk (crot) and wraps
   // around, so the many weight streams do not all hit the same offsets —
@@ -328,7 +328,21 @@ __device__ __forceinline__ void frag_gemm_body(
   static_assert(kPrefetch % kChunkSteps == 0, "chunk boundaries fall on prefetch slots");
   // nks is a multiple of kPrefetch = 4 (K is a multiple of 128)
   int stage = 0;  // ring slot of the current chunk
+  int quarter = -1;
   for (int ks0 = 0; ks0 < nks; ks0 += kPrefetch) {
+    // progress-ordered issue priority (see the kernel): 3, 2, 1, 0 over the
+    // four quarters of K, so a workgroup that has fallen behind the other
+    // one on its CU outranks it
+    if (prio) {
+      const int q = (ks0 * 4) / nks;
+      if (q != quarter) {
+        quarter = q;
+        if (q == 0) __builtin_amdgcn_s_setprio(3);
+        else if (q == 1) __builtin_amdgcn_s_setprio(2);
+        else if (q == 2) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
+    }
 #pragma unroll
     for (int s = 0; s < kPrefetch; ++s) {
       const int ks = ks0 + s;
@@ -518,12 +532,26 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
   // column blocks share the activation tiles through L2.
   const uint32_t rkey = NW == 8 ? (uint32_t)g * 977u : (uint32_t)g * 977u + (uint32_t)cb;
   const int crot = once ? (int)((rkey * 2654435761u) >> 8) % (nks / kChunkSteps) : 0;
+  // When every segment fits one m-tile, all workgroups stream the same
+  // amount, and a CU holds two 4-wave ones that start together; the older
+  // one's waves win the memory-issue arbitration and finish far earlier,
+  // leaving the other to stream alone.  Lowering each wave's priority as it
+  // passes each quarter of K keeps the two in step (measured: balanced
+  // gate/up -3 %).  With longer segments the workgroups' lengths differ and
+  // the same rule is slower, so it is used only when no segment exceeds an
+  // m-tile (the same answer in every workgroup: all read the same counts).
+  bool prio = false;
+  if (NW == 4 && once) {
+    bool fits = true;
+    for (int e = lane; e < G; e += kWave) fits = fits && counts[e] <= kBM;
+    prio = __ballot(!fits) == 0;
+  }
   if (once)
     frag_gemm_body<GATE_UP, true, NW, F8>(As, wp, kstride, sc_g, sc_u, a_base, a_uoff, a_voff, a_chunk_stride, w, lane, nks, nlive, valid,
-                                      ct, ct_ok, row_base, mt_glob, Nout, tile_scale, Out, crot);
+                                      ct, ct_ok, row_base, mt_glob, Nout, tile_scale, Out, crot, prio);
   else
     frag_gemm_body<GATE_UP, false, NW, F8>(As, wp, kstride, sc_g, sc_u, a_base, a_uoff, a_voff, a_chunk_stride, w, lane, nks, nlive, valid,
-                                       ct, ct_ok, row_base, mt_glob, Nout, tile_scale, Out, crot);
+                                       ct, ct_ok, row_base, mt_glob, Nout, tile_scale, Out, crot, false);
 }
 
 // Packing: one thread per 16-byte vector of the source (coalesced reads),

@@ -547,14 +547,14 @@ def test_ffn_deterministic():
 
 
 @pytest.mark.parametrize("H,I,T", [(512, 256, 300), (128, 128, 40), (384, 256, 700),
-                                   (256, 256, 2000)])
+                                   (256, 256, 2000), (384, 256, 1700), (128, 384, 1600)])
 def test_ffn_packed_weights(H, I, T):
     """Packed weights in MFMA fragment order: the packing is the documented
     permutation of the input, and the fragment-streaming GEMM matches the
     oracle.  The cases cover both workgroup widths (4 waves when segments
-    average under 128 rows, 8 above), a partial column block (H/64 not a
-    multiple of the column tiles per workgroup) and several m-tiles per
-    expert."""
+    average under 128 rows, 8 above), a partial column block (H/64 or 2I/64
+    not a multiple of the column tiles per workgroup) and several m-tiles
+    per expert with ragged tails."""
     cfg = workloads.MoEConfig("t", 13, T=T, H=H, E=6, K=2, I=I, hot_experts=2)
     idx, w = oracle.route(workloads.logits(cfg), None, 2)
     hid = workloads.hidden(cfg)

@@ -15,6 +15,8 @@
 
 namespace moe {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes, native vector
+
 // The ordered sum for one 16-byte vector (channels 8c .. 8c+7) of token t,
 // rounded once to bf16.  Returns whether the token has a valid routed slot.
 template <bool QDQ>
@@ -27,6 +29,9 @@ __device__ __forceinline__ bool combine_vec(const uint16_t* __restrict__ rows, i
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
   bool routed = false;
+  // the shared expert's vector depends on nothing: load it first
+  const uint4 sraw =
+      shared ? reinterpret_cast<const uint4*>(shared + t * H)[c] : make_uint4(0, 0, 0, 0);
   // slots in groups of 8: the group's row gathers are all issued before its
   // adds, which then run in slot order
   for (int k0 = 0; k0 < K; k0 += 8) {
@@ -40,10 +45,15 @@ __device__ __forceinline__ bool combine_vec(const uint16_t* __restrict__ rows, i
         r[j] = -1;
       }
     }
+    // every routed row is read exactly once: non-temporal loads (measured:
+    // the 1.1 GB combine of a 16k-token batch 209 -> 186 us)
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      raw[j] = r[j] >= 0 ? reinterpret_cast<const uint4*>(rows + (int64_t)r[j] * H)[c]
-                         : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < 8; ++j) {
+      const u32x4 v = r[j] >= 0 ? __builtin_nontemporal_load(
+                                      reinterpret_cast<const u32x4*>(rows + (int64_t)r[j] * H) + c)
+                                : u32x4{0u, 0u, 0u, 0u};
+      raw[j] = make_uint4(v.x, v.y, v.z, v.w);
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (r[j] < 0) continue;
@@ -60,9 +70,8 @@ __device__ __forceinline__ bool combine_vec(const uint16_t* __restrict__ rows, i
     }
   }
   if (shared) {
-    uint4 raw = reinterpret_cast<const uint4*>(shared + t * H)[c];
     float f[8];
-    unpack8(raw, f);
+    unpack8(sraw, f);
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = acc[j] + f[j];
   }

@@ -36,6 +36,17 @@
 
 namespace moe {
 
+// Permuted rows are written with non-temporal stores: each wave writes whole
+// 1 KB runs of a row, which the grouped GEMM reads next from other XCDs.
+// Measured on the balanced, deepseek and prefill batches: the permute itself
+// within 2 % either way, and the gate/up GEMM that follows 1-4 % faster than
+// after ordinary stores.  (Non-temporal reads of the token rows made the
+// prefill permute slower.)
+typedef uint32_t row_vec_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_row_vec(uint16_t* row, int c, const uint4& v) {
+  __builtin_nontemporal_store(row_vec_t{v.x, v.y, v.z, v.w}, reinterpret_cast<row_vec_t*>(row) + c);
+}
+
 constexpr int kChunk = 1024;
 constexpr int kFuseTable = 4096;   // chunk-table entries up to which the scan is fused
 constexpr int kFuseChunks = 16;    // ... and chunks (each workgroup sums its table columns)
@@ -311,7 +322,7 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
     const uint4 val = reinterpret_cast<const uint4*>(hidden + (int64_t)t * H)[c];
     for (int k = 0; k < K; ++k) {
       const int r = dest[tl * K + k];
-      if (r >= 0) reinterpret_cast<uint4*>(x_perm + (int64_t)r * H)[c] = val;
+      if (r >= 0) store_row_vec(x_perm + (int64_t)r * H, c, val);
     }
   }
 }
@@ -478,7 +489,7 @@ __global__ void __launch_bounds__(256) permute_small_kernel(
       const int tl = idx / nvec, c = idx - tl * nvec;
       for (int k = 0; k < K; ++k) {
         const int r = dest[tl * K + k];
-        if (r >= 0) reinterpret_cast<uint4*>(x_perm + (int64_t)r * H)[c] = pre[j];
+        if (r >= 0) store_row_vec(x_perm + (int64_t)r * H, c, pre[j]);
       }
     }
   }
@@ -490,7 +501,7 @@ __global__ void __launch_bounds__(256) permute_small_kernel(
     const uint4 val = reinterpret_cast<const uint4*>(hidden + (int64_t)(t0 + tl) * H)[c];
     for (int k = 0; k < K; ++k) {
       const int r = dest[tl * K + k];
-      if (r >= 0) reinterpret_cast<uint4*>(x_perm + (int64_t)r * H)[c] = val;
+      if (r >= 0) store_row_vec(x_perm + (int64_t)r * H, c, val);
     }
   }
 }

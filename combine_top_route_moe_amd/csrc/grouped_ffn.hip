@@ -244,6 +244,18 @@ __device__ __forceinline__ bf16x8_t dequant8(u32x2_t c, float s) {
   return __builtin_bit_cast(bf16x8_t, w);
 }
 
+// The epilogue's 16-byte output stores.  The gate/up activations, read once
+// by the down GEMM, are stored non-temporally; the down projection's rows
+// with ordinary stores (the combine that reads them next is faster when part
+// of them is still cached: measured, non-temporal there cost it 6 %).
+template <bool NT>
+__device__ __forceinline__ void epi_store(u32x4_t* p, const u32x4_t& v) {
+  if (NT)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+
 // The weight element of a B-fragment lane: 16 bytes of bf16, or 8 FP8 codes.
 template <bool F8>
 using WFrag = typename std::conditional<F8, u32x2_t, u32x4_t>::type;
@@ -255,7 +267,7 @@ __device__ __forceinline__ void frag_gemm_body(
     const uint16_t* a_base, const int64_t* a_uoff, const uint32_t* a_voff, int a_chunk_stride,
     int w, int lane, int nks, int nlive,
     int valid, int ct, bool ct_ok, int64_t row_base, int64_t mt_glob, int Nout,
-    const float* tile_scale, uint16_t* __restrict__ Out, int crot, bool prio) {
+    const float* tile_scale, uint16_t* __restrict__ Out, int crot, bool prio, uint16_t* epi) {
   constexpr int kDmaPerWave = kStageBlocks / NW;
   // every workgroup walks K from its own starting chunk (crot) and wraps
   // around, so the many weight streams do not all hit the same offsets —
@@ -395,37 +407,57 @@ __device__ __forceinline__ void frag_gemm_body(
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA may outlive the workgroup
   if (!ct_ok) return;
 
-  // epilogue: lane holds D[4*(lane/16) + q][lane%16] of every 16x16 tile
+  // epilogue: lane holds D[4*(lane/16) + q][lane%16] of every 16x16 tile.
+  // Each 16-row subtile goes through the wave's LDS staging area (rows padded
+  // so the 2-byte writes are conflict-free), and is stored back as 16-byte
+  // vectors: whole 128-byte row pieces instead of 2-byte scattered stores.
+  // Rows past the segment end are neither staged nor stored.
+  constexpr int kEpiStride = GATE_UP ? 40 : 72;  // bf16 per staged row (32 or 64 + 8)
 #pragma unroll
   for (int i = 0; i < kMsub; ++i) {
     if (i >= nlive) break;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int r = i * 16 + 4 * (lane >> 4) + q;
+      const int rr = 4 * (lane >> 4) + q;
+      const int r = i * 16 + rr;
       if (r >= valid) continue;
-      const int64_t orow = row_base + r;
       if (GATE_UP) {
-        // a is written in the down GEMM's activation fragment order: block
-        // (m-tile, m-subtile i, K-step ct) of 64 lanes x 8 values, where lane
-        // L = row%16 + 16*(col%32 / 8) holds columns 8*(col%32 / 8) .. +8
-        uint16_t* blk = Out + ((mt_glob * kMsub + i) * (int64_t)(Nout / 32) + ct) * (kWave * 8);
-        const int rr = 4 * (lane >> 4) + q;
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int c32 = f * 16 + (lane & 15);
-          blk[(rr + 16 * (c32 >> 3)) * 8 + (c32 & 7)] =
+        for (int f = 0; f < 2; ++f)
+          epi[rr * kEpiStride + f * 16 + (lane & 15)] =
               (uint16_t)f32_to_bf16(silu_f(acc[i][f][q]) * acc[i][f + 2][q]);
-        }
-        (void)orow;
       } else {
         const float sc = tile_scale ? tile_scale[r] : 1.0f;
 #pragma unroll
-        for (int f = 0; f < kFrags; ++f) {
-          const int col = ct * 64 + f * 16 + (lane & 15);
-          Out[orow * Nout + col] = (uint16_t)f32_to_bf16(sc * acc[i][f][q]);
+        for (int f = 0; f < kFrags; ++f)
+          epi[rr * kEpiStride + f * 16 + (lane & 15)] = (uint16_t)f32_to_bf16(sc * acc[i][f][q]);
+      }
+    }
+    // the staging area is the wave's own: its LDS operations run in order,
+    // and the fences keep the compiler from moving them across each other
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    if (GATE_UP) {
+      // a is written in the down GEMM's activation fragment order: block
+      // (m-tile, m-subtile i, K-step ct) of 64 lanes x 8 values, where lane
+      // L = row%16 + 16*(col%32 / 8) holds columns 8*(col%32 / 8) .. +8
+      const int row = lane & 15;
+      if (i * 16 + row < valid) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&epi[row * kEpiStride + 8 * (lane >> 4)]);
+        uint16_t* blk = Out + ((mt_glob * kMsub + i) * (int64_t)(Nout / 32) + ct) * (kWave * 8);
+        epi_store<true>(reinterpret_cast<u32x4_t*>(blk) + lane, v);
+      }
+    } else {
+      // 16 rows x 64 columns = 128 pieces of 8 columns, two per lane
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int piece = lane + h * kWave, row = piece >> 3, c8 = piece & 7;
+        if (i * 16 + row < valid) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&epi[row * kEpiStride + 8 * c8]);
+          epi_store<false>(reinterpret_cast<u32x4_t*>(Out + (row_base + i * 16 + row) * Nout + ct * 64) + c8, v);
         }
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   }
 }
 
@@ -438,6 +470,7 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
     int Kdim, int Nw /* weight rows per group */, int Nout, const float* __restrict__ row_scale,
     uint16_t* __restrict__ Out, int64_t capacity, int32_t* __restrict__ dev_error) {
   __shared__ __attribute__((aligned(16))) u32x4_t As[kStages][kStageBlocks][kWave];
+  __shared__ __attribute__((aligned(16))) uint16_t Epi[NW][16 * 72];  // per-wave output staging
 
   const int n_ct = Nw / 64;              // column tiles per group
   const int n_cb = (n_ct + NW - 1) / NW;  // workgroups per m-tile
@@ -548,10 +581,12 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
   }
   if (once)
     frag_gemm_body<GATE_UP, true, NW, F8>(As, wp, kstride, sc_g, sc_u, a_base, a_uoff, a_voff, a_chunk_stride, w, lane, nks, nlive, valid,
-                                      ct, ct_ok, row_base, mt_glob, Nout, tile_scale, Out, crot, prio);
+                                      ct, ct_ok, row_base, mt_glob, Nout, tile_scale, Out, crot, prio,
+                                      Epi[w]);
   else
     frag_gemm_body<GATE_UP, false, NW, F8>(As, wp, kstride, sc_g, sc_u, a_base, a_uoff, a_voff, a_chunk_stride, w, lane, nks, nlive, valid,
-                                       ct, ct_ok, row_base, mt_glob, Nout, tile_scale, Out, crot, false);
+                                       ct, ct_ok, row_base, mt_glob, Nout, tile_scale, Out, crot, false,
+                                       Epi[w]);
 }
 
 // Packing: one thread per 16-byte vector of the source (coalesced reads),

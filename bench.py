@@ -73,17 +73,20 @@ def algorithmic(cfg, counts: np.ndarray, fp8=None) -> dict:
 
 STAGE_SOURCES = {
     "route": ["route.hip"], "dispatch_qdq": ["fake_quant.hip"], "permute": ["permute.hip"],
-    "dispatch_quant": ["fp8_ffn.hip"],
-    "ffn_gate_up": ["grouped_ffn.hip", "fp8_ffn.hip", "gemm_common.h"],
-    "ffn_down": ["grouped_ffn.hip", "fp8_ffn.hip", "gemm_common.h"],
-    "shared_ffn": ["grouped_ffn.hip", "fp8_ffn.hip", "gemm_common.h"], "combine": ["combine.hip"],
+    "dispatch_quant": ["fp8_ffn.hip"], "combine": ["combine.hip"],
 }
+# the grouped GEMMs: the BF16 and FP8-weight kernels, or the FP8 path's
+GEMM_SOURCES = {None: ["grouped_ffn.hip", "gemm_common.h"],
+                "weights": ["grouped_ffn.hip", "gemm_common.h"],
+                "w8a8": ["fp8_ffn.hip", "gemm_common.h"]}
 
 
-def kernel_source_hash(stage: str) -> str:
-    """Hash of the sources a stage's kernels are built from (plus common.h)."""
+def kernel_source_hash(stage: str, fp8=None) -> str:
+    """Hash of the sources a stage's kernels are built from (plus common.h),
+    for the weight/activation mode ``fp8`` (None, "weights" or "w8a8")."""
+    names = STAGE_SOURCES.get(stage) or GEMM_SOURCES[fp8]
     h = hashlib.sha256()
-    for name in STAGE_SOURCES[stage] + ["common.h"]:
+    for name in names + ["common.h"]:
         with open(os.path.join(ROOT, "combine_top_route_moe_amd", "csrc", name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -93,13 +96,14 @@ def committed_traffic(stage: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
     taken on the kernel as it is now (same source hash); else None.
     ``workload`` names the summary (the workload, plus "_fp8w" for FP8
-    weights)."""
+    weights or "_w8a8" for the FP8 path)."""
     path = os.path.join(PROFILES, f"hbm_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f).get(stage)
-    if not d or d.get("source_hash") != kernel_source_hash(stage):
+    fp8 = "w8a8" if workload.endswith("_w8a8") else "weights" if workload.endswith("_fp8w") else None
+    if not d or d.get("source_hash") != kernel_source_hash(stage, fp8):
         return None
     return d.get("hbm_bytes_per_launch")
 

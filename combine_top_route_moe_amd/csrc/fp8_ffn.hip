@@ -127,7 +127,11 @@ constexpr int kQNW = 8;                 // waves per workgroup
 constexpr int kQTiles = 4;              // column tiles per workgroup
 constexpr int kQSub = kQMsub / 2;       // m-subtiles per wave
 
-template <bool GATE_UP>
+// SKIP_IDLE: compiled with the early exit for idle waves below (used when
+// segments average under one m-tile, where the second row half is often
+// empty); the other instantiation keeps the main loop as compiled without
+// that path, which measured 1-3 % faster on long segments.
+template <bool GATE_UP, bool SKIP_IDLE>
 __global__ void __launch_bounds__(kQNW * kWave, 2) w8a8_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ Ascale, int64_t sstride,
     const int32_t* __restrict__ smap, int sdiv,
@@ -260,6 +264,22 @@ __global__ void __launch_bounds__(kQNW * kWave, 2) w8a8_gemm_kernel(
 
 #pragma unroll
   for (int c = 0; c < kQStages - 1; ++c) issue_chunk(min(c, nkb - 1), c);
+  // A wave of the second row half whose m-tile has at most 64 rows has no
+  // live subtile: it streams no weights, only keeps the workgroup's barriers
+  // (one per K-block, plus the gate/up epilogue's) and, for gate/up, zeroes
+  // its half's row scales; it issues no DMA (wave 0 is never idle).
+  // Measured on segments averaging 64 rows: gate/up -1 to -10 %, down -4 to
+  // -8 % (the idle waves no longer duplicate their column tile's weights).
+  if (SKIP_IDLE && my_live == 0) {
+    for (int kb = 0; kb < nkb; ++kb) lds_barrier();
+    if (GATE_UP) {
+      __syncthreads();
+      float* srow = OutS + (mt_glob * (Nout / 128) + cb) * kBM;
+      if (cw == 0)
+        for (int r = i0 * 16 + lane; r < (i0 + kQSub) * 16; r += kWave) srow[r] = 0.0f;
+    }
+    return;
+  }
 #pragma unroll
   for (int s = 0; s < kQPrefetch; ++s) fill(s, min(s, nkb - 1));
   asm volatile("" ::: "memory");
@@ -432,21 +452,28 @@ int launch_grouped_ffn_w8a8(const uint8_t* xq, const float* xs, int64_t sstride,
   auto grid_for = [&](int64_t n_tiles) {
     return (m_tiles * n_tiles + grid_unit - 1) / grid_unit * grid_unit;
   };
+  // segments averaging under one m-tile: the instantiation whose idle
+  // second-half waves leave early
+  const bool short_segs = capacity / G < kBM;
   if (flags & MOE_FFN_GATE_UP) {
     const int64_t blocks = grid_for((2 * I / 64 + kQTiles - 1) / kQTiles);
     if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(w8a8_gemm_kernel<true>, dim3((unsigned)blocks), dim3(kQNW * kWave), 0,
-                       stream, xq, xs, sstride, smap, sdiv, w13q, w13s, cu_seqlens, counts, G, H,
-                       2 * I, I,
-                       nullptr, aq, as, nullptr, capacity, dev_error);
+#define MOE_W8A8_GU(SKIP)                                                                        \
+  hipLaunchKernelGGL((w8a8_gemm_kernel<true, SKIP>), dim3((unsigned)blocks), dim3(kQNW * kWave), 0, \
+                     stream, xq, xs, sstride, smap, sdiv, w13q, w13s, cu_seqlens, counts, G, H,    \
+                     2 * I, I, nullptr, aq, as, nullptr, capacity, dev_error)
+    if (short_segs) MOE_W8A8_GU(true); else MOE_W8A8_GU(false);
+#undef MOE_W8A8_GU
   }
   if (flags & MOE_FFN_DOWN) {
     const int64_t blocks = grid_for((H / 64 + kQTiles - 1) / kQTiles);
     if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(w8a8_gemm_kernel<false>, dim3((unsigned)blocks), dim3(kQNW * kWave), 0,
-                       stream, aq, as, (int64_t)0, (const int32_t*)nullptr, 1, w2q, w2s,
-                       cu_seqlens, counts, G, I, H, H,
-                       row_scale, nullptr, nullptr, y, capacity, dev_error);
+#define MOE_W8A8_DN(SKIP)                                                                         \
+  hipLaunchKernelGGL((w8a8_gemm_kernel<false, SKIP>), dim3((unsigned)blocks), dim3(kQNW * kWave), 0, \
+                     stream, aq, as, (int64_t)0, (const int32_t*)nullptr, 1, w2q, w2s, cu_seqlens,  \
+                     counts, G, I, H, H, row_scale, nullptr, nullptr, y, capacity, dev_error)
+    if (short_segs) MOE_W8A8_DN(true); else MOE_W8A8_DN(false);
+#undef MOE_W8A8_DN
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

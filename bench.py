@@ -48,8 +48,10 @@ def algorithmic(cfg, counts: np.ndarray, fp8=None) -> dict:
     st["route"] = dict(bytes=4 * T * E + 8 * T * K + (T if cfg.pad_rows else 0))
     if w8a8:
         st["dispatch_quant"] = dict(bytes=2 * T * H + T * H + T * H // 32)
-    elif cfg.dispatch_block:
+    elif cfg.dispatch_block and cfg.dispatch_block != 128:
         st["dispatch_qdq"] = dict(bytes=4 * Tv * H)
+    # (the 1 x 128 FP8 dispatch quantizer runs inside the permute, whose
+    # bytes are unchanged: each valid token row is still read once)
     xb = 1 if w8a8 else 2                                  # bytes per row element
     st["permute"] = dict(bytes=8 * T * K + xb * Tv * H + xb * N * H + 4 * T * K + 8 * N + 8 * E)
     wb = 1 + 4 / (128 * 128) if fp8 else 2                 # bytes per weight

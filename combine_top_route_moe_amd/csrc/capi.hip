@@ -17,7 +17,7 @@ int launch_combine_check(const uint16_t*, int64_t, const int32_t*, const uint16_
                          const uint16_t*, int32_t*, int32_t*, hipStream_t);
 size_t permute_workspace_bytes(int64_t, int);
 int launch_permute(const int32_t*, const float*, const uint16_t*, int, int, int, int, int, int,
-                   int64_t, int32_t*, int32_t*, uint16_t*, int32_t*, int32_t*, float*, void*,
+                   int, int64_t, int32_t*, int32_t*, uint16_t*, int32_t*, int32_t*, float*, void*,
                    int32_t*, hipStream_t);
 size_t grouped_ffn_workspace_bytes(int64_t, int, int);
 int launch_grouped_ffn(const uint16_t*, const int32_t*, const int32_t*, int, int, int,
@@ -106,7 +106,7 @@ int moe_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t* hi
                 int32_t* dev_error, void* stream) {
   if (T < 0 || K < 1 || H < 1 || num_local_experts < 1 || capacity < 0 || expert_begin < 0)
     return MOE_ERR_INVALID_ARG;
-  if (flags & ~MOE_PERMUTE_PAD_POW2) return MOE_ERR_INVALID_ARG;
+  if (flags & ~(MOE_PERMUTE_PAD_POW2 | MOE_PERMUTE_DISPATCH_FP8)) return MOE_ERR_INVALID_ARG;
   if (H % 128 || num_local_experts > 1024 || K > 64) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)T * K > 0x7fffffffLL || capacity > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
   if (!counts || !cu_seqlens) return MOE_ERR_INVALID_ARG;
@@ -116,7 +116,8 @@ int moe_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t* hi
   const size_t need = permute_workspace_bytes((int64_t)T * K, num_local_experts);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
   return launch_permute(topk_idx, topk_w, hidden, T, K, H, expert_begin, num_local_experts,
-                        (flags & MOE_PERMUTE_PAD_POW2) ? 1 : 0, capacity, counts, cu_seqlens,
+                        (flags & MOE_PERMUTE_PAD_POW2) ? 1 : 0,
+                        (flags & MOE_PERMUTE_DISPATCH_FP8) ? 1 : 0, capacity, counts, cu_seqlens,
                         x_perm, row_of, src_of, w_perm, workspace, dev_error, as_stream(stream));
 }
 

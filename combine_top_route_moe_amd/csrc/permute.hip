@@ -47,6 +47,26 @@ __device__ __forceinline__ void store_row_vec(uint16_t* row, int c, const uint4&
   __builtin_nontemporal_store(row_vec_t{v.x, v.y, v.z, v.w}, reinterpret_cast<row_vec_t*>(row) + c);
 }
 
+// FP8 fake-quant of a 16-byte vector (8 channels) of a 1 x 128 block whose
+// 16 vectors sit in 16 consecutive lanes, all of which call this together:
+// the block amax by a butterfly over them, s = amax / 448 (IEEE), an
+// all-zero block gives +0, else qdq8_rcp — the block mode of the dispatch
+// fake-quantizer, value for value.
+__device__ __forceinline__ uint4 fq_block128_vec(const uint4& raw) {
+  float f[8];
+  unpack8(raw, f);
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(f[j]));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+  const float s = m / 448.0f;  // IEEE division
+  if (!(s > 0.0f)) return make_uint4(0, 0, 0, 0);
+  uint32_t w[4];
+  qdq8_rcp(f, s, 1.0f / s, rcp_scale_ok(s), w);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 constexpr int kChunk = 1024;
 constexpr int kFuseTable = 4096;   // chunk-table entries up to which the scan is fused
 constexpr int kFuseChunks = 16;    // ... and chunks (each workgroup sums its table columns)
@@ -194,7 +214,12 @@ __global__ void __launch_bounds__(1024) permute_scan_kernel(
 // FUSED: `table` holds the chunk_rank totals and the workgroup does the
 // scan's work itself (see the file comment); otherwise `table` holds the
 // absolute first row of every (chunk, expert) pair written by the scan.
-template <bool FUSED>
+// QDQ (both scatter kernels): each row vector is the dispatch FP8
+// fake-quant's output (fq_block128_vec).  The 16 vectors of a 1 x 128 block
+// are 16 consecutive indices of the copy loop, so 16 consecutive lanes of
+// one wave, which take every branch of the loop together (H / 8 and the
+// loop stride are multiples of 16).
+template <bool FUSED, bool QDQ>
 __global__ void __launch_bounds__(256) permute_scatter_kernel(
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
     const uint16_t* __restrict__ hidden, int T, int K, int H, int expert_begin, int El,
@@ -319,7 +344,8 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
     bool any = false;
     for (int k = 0; k < K; ++k) any |= dest[tl * K + k] >= 0;
     if (!any) continue;
-    const uint4 val = reinterpret_cast<const uint4*>(hidden + (int64_t)t * H)[c];
+    uint4 val = reinterpret_cast<const uint4*>(hidden + (int64_t)t * H)[c];
+    if (QDQ) val = fq_block128_vec(val);
     for (int k = 0; k < K; ++k) {
       const int r = dest[tl * K + k];
       if (r >= 0) store_row_vec(x_perm + (int64_t)r * H, c, val);
@@ -342,6 +368,7 @@ constexpr int kSmallTK = 4096;
 constexpr int kSmallIds = kSmallTK / 256;          // slot ids per thread
 constexpr int kSmallPre = 4;                       // row vectors per thread loaded up front
 
+template <bool QDQ>
 __global__ void __launch_bounds__(256) permute_small_kernel(
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
     const uint16_t* __restrict__ hidden, int T, int K, int H, int expert_begin, int El,
@@ -487,9 +514,10 @@ __global__ void __launch_bounds__(256) permute_small_kernel(
     const int idx = tid + j * 256;
     if (idx < total) {
       const int tl = idx / nvec, c = idx - tl * nvec;
+      const uint4 v = QDQ ? fq_block128_vec(pre[j]) : pre[j];
       for (int k = 0; k < K; ++k) {
         const int r = dest[tl * K + k];
-        if (r >= 0) store_row_vec(x_perm + (int64_t)r * H, c, pre[j]);
+        if (r >= 0) store_row_vec(x_perm + (int64_t)r * H, c, v);
       }
     }
   }
@@ -498,7 +526,8 @@ __global__ void __launch_bounds__(256) permute_small_kernel(
     bool any = false;
     for (int k = 0; k < K; ++k) any |= dest[tl * K + k] >= 0;
     if (!any) continue;
-    const uint4 val = reinterpret_cast<const uint4*>(hidden + (int64_t)(t0 + tl) * H)[c];
+    uint4 val = reinterpret_cast<const uint4*>(hidden + (int64_t)(t0 + tl) * H)[c];
+    if (QDQ) val = fq_block128_vec(val);
     for (int k = 0; k < K; ++k) {
       const int r = dest[tl * K + k];
       if (r >= 0) store_row_vec(x_perm + (int64_t)r * H, c, val);
@@ -515,7 +544,8 @@ size_t permute_workspace_bytes(int64_t TK, int El) {
 }
 
 int launch_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t* hidden, int T,
-                   int K, int H, int expert_begin, int El, int pad_pow2, int64_t capacity,
+                   int K, int H, int expert_begin, int El, int pad_pow2, int dispatch_fp8,
+                   int64_t capacity,
                    int32_t* counts, int32_t* cu_seqlens, uint16_t* x_perm, int32_t* row_of,
                    int32_t* src_of, float* w_perm, void* workspace, int32_t* dev_error,
                    hipStream_t stream) {
@@ -533,9 +563,12 @@ int launch_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t*
   if (tpb * K > 256) tpb = 256 / K;
   const int grid = T > 0 ? (T + tpb - 1) / tpb : 1;
   if (TK <= kSmallTK && El <= 1024) {
-    hipLaunchKernelGGL(permute_small_kernel, dim3(grid), dim3(256), 0, stream, topk_idx, topk_w,
-                       hidden, T, K, H, expert_begin, El, tpb, pad_pow2, capacity, x_perm,
-                       row_of, src_of, w_perm, dev_error, counts, cu_seqlens);
+#define MOE_PERMUTE_SMALL(Q)                                                                   \
+  hipLaunchKernelGGL(permute_small_kernel<Q>, dim3(grid), dim3(256), 0, stream, topk_idx, topk_w, \
+                     hidden, T, K, H, expert_begin, El, tpb, pad_pow2, capacity, x_perm, row_of,   \
+                     src_of, w_perm, dev_error, counts, cu_seqlens)
+    if (dispatch_fp8) MOE_PERMUTE_SMALL(true); else MOE_PERMUTE_SMALL(false);
+#undef MOE_PERMUTE_SMALL
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   }
   if (nchunks > 0)
@@ -545,16 +578,16 @@ int launch_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t*
   if (!fused)
     hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, stream, table, nchunks, El,
                        pad_pow2, capacity, counts, cu_seqlens, src_of, w_perm, dev_error);
-  if (fused)
-    hipLaunchKernelGGL(permute_scatter_kernel<true>, dim3(grid), dim3(256), 0, stream, topk_idx,
-                       topk_w, hidden, T, K, H, expert_begin, El, tpb, capacity, table, nchunks,
-                       pad_pow2, rank, x_perm, row_of, src_of, w_perm, dev_error, counts,
-                       cu_seqlens);
-  else if (T > 0 || capacity > 0)
-    hipLaunchKernelGGL(permute_scatter_kernel<false>, dim3(grid), dim3(256), 0, stream, topk_idx,
-                       topk_w, hidden, T, K, H, expert_begin, El, tpb, capacity, table, nchunks,
-                       pad_pow2, rank, x_perm, row_of, src_of, w_perm, dev_error, counts,
-                       cu_seqlens);
+#define MOE_PERMUTE_SCATTER(F, Q)                                                               \
+  hipLaunchKernelGGL((permute_scatter_kernel<F, Q>), dim3(grid), dim3(256), 0, stream, topk_idx,  \
+                     topk_w, hidden, T, K, H, expert_begin, El, tpb, capacity, table, nchunks,     \
+                     pad_pow2, rank, x_perm, row_of, src_of, w_perm, dev_error, counts, cu_seqlens)
+  if (fused) {
+    if (dispatch_fp8) MOE_PERMUTE_SCATTER(true, true); else MOE_PERMUTE_SCATTER(true, false);
+  } else if (T > 0 || capacity > 0) {
+    if (dispatch_fp8) MOE_PERMUTE_SCATTER(false, true); else MOE_PERMUTE_SCATTER(false, false);
+  }
+#undef MOE_PERMUTE_SCATTER
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -35,7 +35,9 @@ class MoELayer:
                  pad_pow2: bool = False, renormalize: bool = True, expert_begin: int = 0,
                  num_local_experts: Optional[int] = None, dispatch_fp4: Optional[str] = None,
                  combine_fp4: Optional[str] = None):
-        """``dispatch_block`` (128) selects the FP8 dispatch quantizer and
+        """``dispatch_block`` (128) selects the FP8 dispatch quantizer (run
+        inside the permute as it copies the rows: the same bits as quantizing
+        first) and
         ``combine_qdq`` the FP8 combine quantizer; ``dispatch_fp4`` /
         ``combine_fp4`` ("nvfp4" or "mxfp4") the FP4 ones instead.  NVFP4
         tensor scales live in ``dispatch_scale`` / ``combine_scale`` (device
@@ -60,7 +62,11 @@ class MoELayer:
 
         self.topk_idx = torch.empty(T, K, **i32)
         self.topk_w = torch.empty(T, K, **f32)
-        self.hidden_q = torch.empty(T, H, **bf) if (dispatch_block or dispatch_fp4) else None
+        # the FP8 dispatch quantizer in 1 x 128 blocks runs inside the permute
+        # (MOE_PERMUTE_DISPATCH_FP8); the other quantizers write hidden_q first
+        self.fuse_dispatch = dispatch_block == 128 and not dispatch_fp4
+        self.hidden_q = (torch.empty(T, H, **bf)
+                         if (dispatch_block or dispatch_fp4) and not self.fuse_dispatch else None)
         self.dispatch_scale = torch.zeros(1, **f32) if dispatch_fp4 == "nvfp4" else None
         self.capacity = ops.moe_permute_capacity(T, K, self.El, pad_pow2)
         self.perm = ops.alloc_permuted(T, K, H, self.El, self.capacity, dev)
@@ -213,12 +219,13 @@ class MoELayer:
             mode, block = _FP4[self.dispatch_fp4]
             st.append(("dispatch_qdq", lambda: ops.moe_fake_quant_rows(
                 hidden, self.hidden_q, None, mode, block, self.dispatch_scale)))
-        elif self.dispatch_block:
+        elif self.dispatch_block and not self.fuse_dispatch:
             st.append(("dispatch_qdq", lambda: ops.moe_fake_quant_rows(
                 hidden, self.hidden_q, None, ops.MOE_FQ_BLOCK, self.dispatch_block)))
+        fuse = self.fuse_dispatch and not self.w8a8
         st.append(("permute", lambda: ops.moe_permute(
             self.topk_idx, self.topk_w, x, self.El, self.expert_begin, self.pad_pow2,
-            self.capacity, p, self.perm_ws, self.dev_error)))
+            self.capacity, p, self.perm_ws, self.dev_error, dispatch_fp8=fuse)))
         st.append(("ffn_gate_up", lambda: self._ffn(
             x_ffn, p.cu_seqlens, p.counts, self.w13, self.w2, p.w_perm, self.y_perm,
             ops.MOE_FFN_GATE_UP, self.ffn_ws)))

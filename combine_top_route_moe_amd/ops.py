@@ -17,6 +17,7 @@ from ._lib import load, check
 
 MOE_ROUTE_RENORM = 1
 MOE_PERMUTE_PAD_POW2 = 1
+MOE_PERMUTE_DISPATCH_FP8 = 2
 MOE_FFN_GATE_UP, MOE_FFN_DOWN, MOE_FFN_ALL, MOE_FFN_PACKED_WEIGHTS = 1, 2, 3, 4
 MOE_FQ_PER_TENSOR, MOE_FQ_BLOCK, MOE_FQ_NVFP4, MOE_FQ_MXFP4 = 0, 1, 2, 3
 MOE_DEVERR_ROW_RANGE, MOE_DEVERR_CAPACITY, MOE_DEVERR_LAYOUT = 1, 2, 3
@@ -98,13 +99,16 @@ def moe_permute(topk_idx: torch.Tensor, topk_w: torch.Tensor, hidden: torch.Tens
                 num_local_experts: int, expert_begin: int = 0, pad_pow2: bool = False,
                 capacity: Optional[int] = None, out: Optional[Permuted] = None,
                 workspace: Optional[torch.Tensor] = None,
-                dev_error: Optional[torch.Tensor] = None, stream=None) -> Permuted:
+                dev_error: Optional[torch.Tensor] = None, stream=None,
+                dispatch_fp8: bool = False) -> Permuted:
+    """``dispatch_fp8``: the rows are written FP8 fake-quantized in 1 x 128
+    blocks (MOE_PERMUTE_DISPATCH_FP8)."""
     _want(topk_idx, torch.int32, "topk_idx")
     _want(topk_w, torch.float32, "topk_w")
     _want(hidden, torch.bfloat16, "hidden")
     T, K = topk_idx.shape
     H = hidden.shape[1]
-    flags = MOE_PERMUTE_PAD_POW2 if pad_pow2 else 0
+    flags = (MOE_PERMUTE_PAD_POW2 if pad_pow2 else 0) | (MOE_PERMUTE_DISPATCH_FP8 if dispatch_fp8 else 0)
     lib = load()
     if capacity is None:
         capacity = out.x_perm.shape[0] if out is not None else lib.moe_permute_capacity(

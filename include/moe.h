@@ -65,7 +65,9 @@ enum {
 
 /* ---- flags -------------------------------------------------------------- */
 enum { MOE_ROUTE_RENORM = 1 };        /* moe_route: renormalise over top-k */
-enum { MOE_PERMUTE_PAD_POW2 = 1 };    /* moe_permute: pow2 segment buckets */
+enum { MOE_PERMUTE_PAD_POW2 = 1,      /* moe_permute: pow2 segment buckets */
+       MOE_PERMUTE_DISPATCH_FP8 = 2   /* moe_permute: FP8 fake-quant of the rows (1x128) */
+};
 enum { MOE_FFN_GATE_UP = 1,           /* moe_grouped_ffn flags: stages ... */
        MOE_FFN_DOWN = 2,
        MOE_FFN_ALL = 3,
@@ -127,11 +129,20 @@ int moe_route(const float* logits, const uint8_t* row_valid, int T, int E, int K
  *                  every unused row in [cu_seqlens[num_local_experts], capacity)
  *   w_perm[r]      topk_w[src_of[r]], 0 for padding and unused rows
  *   x_perm[r, :]   hidden[src_of[r] / K, :]; padding and unused rows are not
- *                  written
+ *                  written.  With MOE_PERMUTE_DISPATCH_FP8 the row is the
+ *                  dispatch quantizer's output instead ([P1] PR summary and
+ *                  "How it works": the dispatch rows are fake-quantized to
+ *                  FP8 before the experts' staging; [P2] review thread on the
+ *                  low-latency dispatch: 1x128 blocks): bit for bit what
+ *                  moe_fake_quant_rows(MOE_FQ_BLOCK, block 128) writes for
+ *                  that hidden row, so quantizing `hidden` first and
+ *                  permuting the result gives the same x_perm.  The block
+ *                  scales are not returned.
  *
  *   topk_idx [T, K] int32   topk_w [T, K] float32   hidden [T, H] bf16
- *   (rows are copied as opaque 2-byte units, so any 2H-byte row payload can
- *   be permuted this way — FP8 codes of 2H channels, for instance)
+ *   (without MOE_PERMUTE_DISPATCH_FP8 rows are copied as opaque 2-byte
+ *   units, so any 2H-byte row payload can be permuted this way — FP8 codes
+ *   of 2H channels, for instance)
  *   counts [E_l] int32, cu_seqlens [E_l + 1] int32, row_of [T*K] int32,
  *   src_of [capacity] int32, w_perm [capacity] float32,
  *   x_perm [capacity, H] bf16 — all outputs.

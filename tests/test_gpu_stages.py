@@ -294,6 +294,38 @@ def test_permute_launch_path_boundaries(T, K, E, H, El, begin):
         _permute_case(idx, w, hid, El, begin, pow2)
 
 
+@pytest.mark.parametrize("T,K,E,H,pow2,begin_el", [
+    (64, 2, 8, 256, False, None),        # one launch
+    (300, 8, 16, 512, True, (4, 8)),     # one launch, pow2 buckets, an expert-parallel share
+    (700, 8, 32, 384, False, None),      # 5600 slots: the multi-launch path
+    (3, 2, 4, 8320, True, None),         # rows wider than the one launch's up-front loads
+])
+def test_permute_dispatch_fp8_equals_quantize_then_permute(T, K, E, H, pow2, begin_el):
+    """MOE_PERMUTE_DISPATCH_FP8: the permuted rows are the 1x128 FP8 dispatch
+    fake-quant of the token rows (the oracle's block quantizer, then its
+    permute), bit for bit; rows include all-zero blocks, negative zeros,
+    subnormals and large magnitudes."""
+    rng = np.random.default_rng(T + H)
+    idx = rng.integers(-1, E, size=(T, K)).astype(np.int32)
+    w = rng.random((T, K)).astype(np.float32)
+    vals = rng.standard_normal((T, H)).astype(np.float32) * rng.choice([1e-3, 1.0, 1e4], (T, 1))
+    hid = f32_to_bf16_bits(vals.astype(np.float32))
+    hid[0, :128] = 0                                 # an all-zero block
+    hid[0, 128:136] = 0x8000                         # negative zeros
+    hid[-1, :16] = np.arange(1, 17, dtype=np.uint16)  # subnormals
+    begin, El = begin_el if begin_el else (0, E)
+    hq, _ = oracle.fake_quant_block(hid, 128)
+    ref = oracle.permute(idx, w, hq, El, begin, pow2)
+    cap = ops.moe_permute_capacity(T, K, El, pow2)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    p = ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), El, begin, pow2, cap, dev_error=err,
+                        dispatch_fp8=True)
+    assert host(err)[0] == 0
+    np.testing.assert_array_equal(host(p.row_of), ref["row_of"])
+    rows = np.nonzero(ref["src_of"] >= 0)[0]
+    np.testing.assert_array_equal(host_bits(p.x_perm)[rows], ref["x_perm"][rows])
+
+
 def test_permute_capacity_overflow_is_flagged_not_written():
     rng = np.random.default_rng(9)
     T, K, E, H = 64, 4, 8, 128

@@ -400,17 +400,23 @@ def test_layer_deepseek_full_size_sampled():
     print(f"deepseek sampled rel err {err:.3e}")
 
 
-def test_layer_graph_replay_matches_eager():
+@pytest.mark.parametrize("variant", ["shared_combine_qdq", "dispatch_fp8_pow2"])
+def test_layer_graph_replay_matches_eager(variant):
     """The whole layer captured once into a HIP graph and replayed several
     times, with eager work and synchronizations in between, gives the eager
-    result bit for bit every time."""
-    cfg = workloads.CONFIGS["tiny"].with_(shared_I=128, combine_qdq=True, pad_rows=3)
+    result bit for bit every time (also with the FP8 dispatch quantizer
+    running inside the permute, pow2 buckets and padding rows)."""
+    tiny = workloads.CONFIGS["tiny"]
+    cfg = {"shared_combine_qdq": tiny.with_(shared_I=128, combine_qdq=True, pad_rows=3),
+           "dispatch_fp8_pow2": tiny.with_(dispatch_block=128, pad_pow2=True, pad_rows=5)}[variant]
     W = Weights(cfg)
     lg, hd, vd = dev(workloads.logits(cfg)), dev_bf16(workloads.hidden(cfg)), dev(workloads.row_valid(cfg))
     layer = MoELayer(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, "cuda", shared_I=cfg.shared_I,
-                     combine_qdq=True)
-    layer.set_weights(W.w13, W.w2, *W.shared)
-    layer.calibrate_combine_scale(lg, hd, vd)
+                     combine_qdq=cfg.combine_qdq, dispatch_block=cfg.dispatch_block,
+                     pad_pow2=cfg.pad_pow2)
+    layer.set_weights(W.w13, W.w2, *(W.shared or (None, None)))
+    if cfg.combine_qdq:
+        layer.calibrate_combine_scale(lg, hd, vd)
     eager = layer.forward(lg, hd, vd).clone()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())

@@ -32,6 +32,12 @@
 // launch, permute_small_kernel: every workgroup counts all the slots itself
 // (two LDS histograms), which for a few thousand slots costs less than the
 // launches and dependent round trips to memory it saves.
+//
+// With MOE_PERMUTE_DISPATCH_FP8 the copies also apply the dispatch FP8
+// fake-quant ("Add MoE dispatch/combine fake quantization for vLLM's
+// DeepGEMM Mega-MoE", PR summary and "How it works"; 1 x 128 blocks as in
+// "[Kernel] DeepEP dispatch-combine kernel integration", review thread on
+// the low-latency dispatch) to each row vector on its way.
 #include "common.h"
 
 namespace moe {

@@ -324,35 +324,53 @@ def main():
     # cache state of a real step, and the events time GPU work only.
     stages = layer.stages(logits, hidden, row_valid)
     spin_cycles = calibrate_spin(stream)
-    per_stage = {name: [] for name, _ in stages}
-    for _ in range(args.steps):
-        torch.cuda._sleep(spin_cycles)
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-        evs[0].record(stream)
-        for i, (name, enqueue) in enumerate(stages):
-            enqueue()
-            evs[i + 1].record(stream)
-        torch.cuda.synchronize()
-        for i, (name, _) in enumerate(stages):
-            per_stage[name].append(evs[i].elapsed_time(evs[i + 1]))
-    stage_ms = {k: float(np.median(v)) for k, v in per_stage.items()}
+
+    def time_stages(flush=None):
+        per_stage = {name: [] for name, _ in stages}
+        for _ in range(args.steps):
+            if flush is not None:
+                flush.fill_(1)             # evicts L2 and the infinity cache
+            torch.cuda._sleep(spin_cycles)
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+            evs[0].record(stream)
+            for i, (name, enqueue) in enumerate(stages):
+                enqueue()
+                evs[i + 1].record(stream)
+            torch.cuda.synchronize()
+            for i, (name, _) in enumerate(stages):
+                per_stage[name].append(evs[i].elapsed_time(evs[i + 1]))
+        return {k: float(np.median(v)) for k, v in per_stage.items()}
+
+    stage_ms = time_stages()
+    # Timed region 3 (stages_cold): the same with 1 GiB written before every
+    # step, so each stage starts from cold caches (the small workloads'
+    # permute and combine otherwise find part of their data in the infinity
+    # cache); reported beside the in-context figures, not instead of them.
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    stage_ms_cold = time_stages(flush)
+    del flush
     assert layer.dev_error.item() == 0, "device error word set during the stage timing"
 
     counts = layer.perm.counts.cpu().numpy()
     alg = algorithmic(cfg, counts, args.fp8)
     peak_mfma = PEAK_FP8_TFLOPS if args.fp8 == "w8a8" else PEAK_BF16_TFLOPS
-    stages = {}
-    for name, ms in stage_ms.items():
-        a = alg.get(name, {})
-        d = {"ms": round(ms, 5)}
-        if "bytes" in a:
-            d["alg_bytes"] = a["bytes"]
-            d["GBps"] = round(a["bytes"] / (ms * 1e-3) / 1e9, 1)
-            d["hbm_frac"] = round(d["GBps"] / PEAK_HBM_GBPS, 4)
-        if "flops" in a:
-            d["TFLOPs"] = round(a["flops"] / (ms * 1e-3) / 1e12, 2)
-            d["mfma_util"] = round(d["TFLOPs"] / peak_mfma, 4)
-        stages[name] = d
+    def stage_report(times):
+        out = {}
+        for name, ms in times.items():
+            a = alg.get(name, {})
+            d = {"ms": round(ms, 5)}
+            if "bytes" in a:
+                d["alg_bytes"] = a["bytes"]
+                d["GBps"] = round(a["bytes"] / (ms * 1e-3) / 1e9, 1)
+                d["hbm_frac"] = round(d["GBps"] / PEAK_HBM_GBPS, 4)
+            if "flops" in a:
+                d["TFLOPs"] = round(a["flops"] / (ms * 1e-3) / 1e12, 2)
+                d["mfma_util"] = round(d["TFLOPs"] / peak_mfma, 4)
+            out[name] = d
+        return out
+
+    stages = stage_report(stage_ms)
+    stages_cold = stage_report(stage_ms_cold)
 
     dom = max(stage_ms, key=stage_ms.get)
     a = alg[dom]
@@ -400,13 +418,16 @@ def main():
         "permute_GBps": stages["permute"]["GBps"],
         "combine_GBps": stages["combine"]["GBps"],
         "stages": stages,
+        "stages_cold": stages_cold,
         "roofline": roof,
         "timing": {"value": ("HIP-graph replay of the whole layer" if graph is not None
                              else "eager launches of the whole layer"),
                    "stages": "eager steps queued behind a GPU spin kernel, HIP events between "
                              "stages on the launch stream, median over steps; stages run "
                              "one after another (the layer itself runs the shared expert "
-                             "concurrently with the routed path)"},
+                             "concurrently with the routed path)",
+                   "stages_cold": "the same, with 1 GiB written before every step (cold L2 "
+                                  "and infinity cache)"},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -222,6 +222,9 @@ def main():
     ap.add_argument("--config", default="balanced",
                     help="tiny | balanced | skewed | deepseek | prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-stages", action="store_true",
+                    help="also time the stages with 1 GiB written before every step (cold "
+                         "caches) and report them as stages_cold")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the steps as eager launches instead of HIP-graph replays")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
@@ -342,13 +345,17 @@ def main():
         return {k: float(np.median(v)) for k, v in per_stage.items()}
 
     stage_ms = time_stages()
-    # Timed region 3 (stages_cold): the same with 1 GiB written before every
-    # step, so each stage starts from cold caches (the small workloads'
-    # permute and combine otherwise find part of their data in the infinity
-    # cache); reported beside the in-context figures, not instead of them.
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    stage_ms_cold = time_stages(flush)
-    del flush
+    # Timed region 3 (--cold-stages, stages_cold): the same with 1 GiB
+    # written before every step, so each stage starts from cold caches (a
+    # replayed layer otherwise finds part of its weights, and the small
+    # workloads part of their rows, in the infinity cache); reported beside
+    # the in-context figures, not instead of them.  Off by default, so that
+    # the default run's kernels are the in-context ones only.
+    stage_ms_cold = None
+    if args.cold_stages:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        stage_ms_cold = time_stages(flush)
+        del flush
     assert layer.dev_error.item() == 0, "device error word set during the stage timing"
 
     counts = layer.perm.counts.cpu().numpy()
@@ -370,7 +377,7 @@ def main():
         return out
 
     stages = stage_report(stage_ms)
-    stages_cold = stage_report(stage_ms_cold)
+    stages_cold = stage_report(stage_ms_cold) if stage_ms_cold else None
 
     dom = max(stage_ms, key=stage_ms.get)
     a = alg[dom]
@@ -418,7 +425,7 @@ def main():
         "permute_GBps": stages["permute"]["GBps"],
         "combine_GBps": stages["combine"]["GBps"],
         "stages": stages,
-        "stages_cold": stages_cold,
+        **({"stages_cold": stages_cold} if stages_cold else {}),
         "roofline": roof,
         "timing": {"value": ("HIP-graph replay of the whole layer" if graph is not None
                              else "eager launches of the whole layer"),
@@ -426,8 +433,8 @@ def main():
                              "stages on the launch stream, median over steps; stages run "
                              "one after another (the layer itself runs the shared expert "
                              "concurrently with the routed path)",
-                   "stages_cold": "the same, with 1 GiB written before every step (cold L2 "
-                                  "and infinity cache)"},
+                   **({"stages_cold": "the same, with 1 GiB written before every step "
+                                      "(cold L2 and infinity cache)"} if stages_cold else {})},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

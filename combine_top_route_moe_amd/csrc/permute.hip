@@ -18,12 +18,13 @@
 //   2. scan: one workgroup (each expert's chunk column split over
 //      1024 / El threads) turns the chunk totals into per-expert counts,
 //      segment sizes (optionally next_pow2), cu_seqlens, and the absolute
-//      first row of every (chunk, expert) pair; it also marks pow2 padding
-//      rows (src_of = -1, w_perm = 0) and checks the capacity.
+//      first row of every (chunk, expert) pair, and checks the capacity.
 //   3. scatter: one workgroup per token group computes row_of / src_of /
 //      w_perm for its slots and copies each token row once from HBM into
 //      its K destination rows with 16-byte vector loads and stores; the
-//      workgroups also mark the unused rows up to `capacity`.
+//      workgroups also mark the pow2 padding rows (workgroup b those of
+//      expert b) and the unused rows up to `capacity` (src_of = -1,
+//      w_perm = 0).
 // When the chunk table is small (at most kFuseTable entries: a few
 // thousand routed slots), launch 2 is folded into launch 3: every scatter
 // workgroup scans the table itself from LDS (a few hundred integers), and
@@ -55,17 +56,29 @@ __device__ __forceinline__ void store_row_vec(uint16_t* row, int c, const uint4&
 
 // FP8 fake-quant of a 16-byte vector (8 channels) of a 1 x 128 block whose
 // 16 vectors sit in 16 consecutive lanes, all of which call this together:
-// the block amax by a butterfly over them, s = amax / 448 (IEEE), an
+// the block amax across them in registers, s = amax / 448 (IEEE), an
 // all-zero block gives +0, else qdq8_rcp — the block mode of the dispatch
 // fake-quantizer, value for value.
+// One DPP lane movement within each row of 16 lanes (every lane active).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ uint4 fq_block128_vec(const uint4& raw) {
   float f[8];
   unpack8(raw, f);
   float m = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(f[j]));
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+  // the block's 16 lanes are one DPP row: the max over it by two quad
+  // permutations (lane ^ 1, lane ^ 2), the half-row mirror (lane i <-> 7 - i)
+  // and the row mirror (lane i <-> 15 - i), all in registers; max is exact,
+  // so the order does not matter
+  m = fmaxf(m, dpp_f32<0xB1>(m));   // quad_perm [1, 0, 3, 2]
+  m = fmaxf(m, dpp_f32<0x4E>(m));   // quad_perm [2, 3, 0, 1]
+  m = fmaxf(m, dpp_f32<0x141>(m));  // row_half_mirror
+  m = fmaxf(m, dpp_f32<0x140>(m));  // row_mirror
   const float s = m / 448.0f;  // IEEE division
   if (!(s > 0.0f)) return make_uint4(0, 0, 0, 0);
   uint32_t w[4];
@@ -140,13 +153,18 @@ __device__ __forceinline__ int next_pow2_dev(int n) {
 // One workgroup of 1024 threads.  Each expert's column of chunk counts is
 // split into P = 1024 / El contiguous blocks of chunks, one thread each
 // (thread p*El + e: reads stay coalesced across experts), so no thread walks
-// more than ceil(nchunks / P) chunks; the partial sums meet in LDS.
+// more than ceil(nchunks / P) chunks; the partial sums meet in LDS.  Up to
+// kScanRegs chunks per thread, a thread loads its whole block into registers
+// at once and later overwrites it from there: one round trip to memory
+// instead of one per chunk (and per chunk again for the load-then-store
+// pass, whose loads and stores the compiler cannot reorder).
+constexpr int kScanRegs = 32;
 __global__ void __launch_bounds__(1024) permute_scan_kernel(
     int32_t* __restrict__ table, int nchunks, int El, int pad_pow2, int64_t capacity,
     int32_t* __restrict__ counts, int32_t* __restrict__ cu_seqlens, int32_t* __restrict__ src_of,
     float* __restrict__ w_perm, int32_t* __restrict__ dev_error) {
   __shared__ int32_t part[1024];   // [P][El] partial sums
-  __shared__ int32_t s_start[1024], s_total[1024], s_size[1024];
+  __shared__ int32_t s_start[1024];
   __shared__ int32_t s_wave[16];
   const int tid = threadIdx.x;
   const int P = max(1, 1024 / El);
@@ -154,9 +172,32 @@ __global__ void __launch_bounds__(1024) permute_scan_kernel(
   const int e = act ? tid % El : 0, p = act ? tid / El : 0;
   const int L = (nchunks + P - 1) / P;
   const int c0 = min(p * L, nchunks), c1 = min(c0 + L, nchunks);
+  const bool in_regs = L <= kScanRegs;   // the same for every thread
+  int vals[kScanRegs];
   if (act) {
     int sum = 0;
-    for (int c = c0; c < c1; ++c) sum += table[(int64_t)c * El + e];
+    if (in_regs) {
+      // groups of 8 loads under a uniform guard, each load unconditional
+      // with its index clamped into the thread's block (so all are issued
+      // before the first wait); entries past the block count 0
+      const int n = c1 - c0;
+      const int64_t last = (int64_t)(c1 - 1) * El + e;
+#pragma unroll
+      for (int g = 0; g < kScanRegs / 8; ++g) {
+        if (8 * g < L && n > 0) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            vals[8 * g + u] = table[min((int64_t)(c0 + 8 * g + u) * El + e, last)];
+        } else {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) vals[8 * g + u] = 0;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kScanRegs; ++j) sum += j < n ? vals[j] : 0;
+    } else {
+      for (int c = c0; c < c1; ++c) sum += table[(int64_t)c * El + e];
+    }
     part[tid] = sum;
   }
   __syncthreads();
@@ -188,8 +229,6 @@ __global__ void __launch_bounds__(1024) permute_scan_kernel(
   if (tid < El) {
     const int start = incl - size;
     s_start[tid] = start;
-    s_total[tid] = total;
-    s_size[tid] = size;
     counts[tid] = total;
     cu_seqlens[tid] = start;
     if (tid == El - 1) {
@@ -202,19 +241,26 @@ __global__ void __launch_bounds__(1024) permute_scan_kernel(
     // absolute first row of every (chunk, expert) pair in this thread's block
     int running = s_start[e];
     for (int q = 0; q < p; ++q) running += part[q * El + e];
-    for (int c = c0; c < c1; ++c) {
-      const int64_t k = (int64_t)c * El + e;
-      const int cnt = table[k];
-      table[k] = running;
-      running += cnt;
-    }
-    // pow2 padding rows of expert e, shared among its P threads
-    const int pad0 = s_start[e] + s_total[e], pad1 = s_start[e] + s_size[e];
-    for (int r = pad0 + p; r < pad1 && (int64_t)r < capacity; r += P) {
-      src_of[r] = -1;
-      w_perm[r] = 0.0f;
+    if (in_regs) {
+#pragma unroll
+      for (int j = 0; j < kScanRegs; ++j) {
+        if (j < c1 - c0) {
+          table[(int64_t)(c0 + j) * El + e] = running;
+          running += vals[j];
+        }
+      }
+    } else {
+      for (int c = c0; c < c1; ++c) {
+        const int64_t k = (int64_t)c * El + e;
+        const int cnt = table[k];
+        table[k] = running;
+        running += cnt;
+      }
     }
   }
+  // the pow2 padding rows are marked by the scatter kernel's workgroups
+  // (one workgroup, one expert per lane, made every store instruction touch
+  // 64 cache lines: 23 us of a 128-expert batch's 245 us permute)
 }
 
 // FUSED: `table` holds the chunk_rank totals and the workgroup does the
@@ -301,6 +347,16 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
     used_end = grand;
   } else {
     used_end = cu_seqlens[El];
+    // pow2 padding rows: workgroup b marks those of experts b, b + grid, ...
+    if (pad_pow2)
+      for (int e = blockIdx.x; e < El; e += gridDim.x) {
+        const int r1 = cu_seqlens[e + 1];
+        for (int r = cu_seqlens[e] + counts[e] + tid; r < r1 && (int64_t)r < capacity;
+             r += blockDim.x) {
+          src_of[r] = -1;
+          w_perm[r] = 0.0f;
+        }
+      }
   }
   // rows past the last segment are unused: mark them as well, so that every
   // row of the caller's buffer has a defined src_of and w_perm

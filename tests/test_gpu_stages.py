@@ -281,10 +281,14 @@ def test_permute_edge_cases(seed):
     (500, 8, 2000, 128, 1000, 500),    # an expert-parallel share of 1000 experts
     (100, 8, 2048, 128, 1024, 1024),   # the upper half of 2048 experts (1024 is the limit)
     (3, 2, 4, 8320, 4, 0),             # rows wider than the single launch's up-front loads
+    (4096, 8, 1024, 128, 1024, 0),     # 32 chunks per scan thread: its register path at the limit
+    (4300, 8, 1024, 128, 1024, 0),     # 34 chunks per scan thread: its loop path
+    (2100, 8, 128, 128, 128, 0),       # 17 chunks over 8 scan threads: a short and an empty block
 ])
 def test_permute_launch_path_boundaries(T, K, E, H, El, begin):
     """Either side of the single-launch permute's limits (4096 slots, 4 row
-    vectors per thread loaded up front), and at the 1024-local-expert limit:
+    vectors per thread loaded up front), at the 1024-local-expert limit, and
+    either side of the scan kernel's 32 chunks per thread held in registers:
     bit-exact."""
     rng = np.random.default_rng(T * K + E)
     idx = rng.integers(-1, E, size=(T, K)).astype(np.int32)

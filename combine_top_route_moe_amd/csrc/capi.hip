@@ -137,6 +137,7 @@ int moe_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32_t*
   const int stages = flags & MOE_FFN_ALL;
   if (H % 128 || I % 128 || num_groups > 1024) return MOE_ERR_UNSUPPORTED;
   if (capacity > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  if (capacity == 0) return MOE_OK;   // no rows: nothing to read or write
   if (!cu_seqlens || !counts) return MOE_ERR_INVALID_ARG;
   if ((stages & MOE_FFN_GATE_UP) && (!x || !w13)) return MOE_ERR_INVALID_ARG;
   if ((stages & MOE_FFN_DOWN) && (!y || !w2)) return MOE_ERR_INVALID_ARG;
@@ -160,6 +161,7 @@ int moe_grouped_ffn_fp8(const uint16_t* x, const int32_t* cu_seqlens, const int3
   if ((flags & ~MOE_FFN_ALL) || !(flags & MOE_FFN_ALL)) return MOE_ERR_INVALID_ARG;
   if (H % 128 || I % 128 || num_groups > 1024) return MOE_ERR_UNSUPPORTED;
   if (capacity > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  if (capacity == 0) return MOE_OK;   // no rows: nothing to read or write
   if (!cu_seqlens || !counts) return MOE_ERR_INVALID_ARG;
   if ((flags & MOE_FFN_GATE_UP) && (!x || !w13q || !w13_scales)) return MOE_ERR_INVALID_ARG;
   if ((flags & MOE_FFN_DOWN) && (!y || !w2q || !w2_scales)) return MOE_ERR_INVALID_ARG;
@@ -217,6 +219,7 @@ int moe_grouped_ffn_w8a8(const uint8_t* xq, const float* x_scales, int64_t scale
   if ((flags & ~MOE_FFN_ALL) || !(flags & MOE_FFN_ALL)) return MOE_ERR_INVALID_ARG;
   if (H % 128 || I % 128 || num_groups > 1024) return MOE_ERR_UNSUPPORTED;
   if (capacity > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  if (capacity == 0) return MOE_OK;   // no rows: nothing to read or write
   if (!cu_seqlens || !counts) return MOE_ERR_INVALID_ARG;
   if ((flags & MOE_FFN_GATE_UP) &&
       (!xq || !x_scales || !w13q || !w13_scales || scale_stride < 1 ||

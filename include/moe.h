@@ -181,7 +181,9 @@ int moe_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t* hi
  * get the workspace a GATE_UP call with the same segments filled — and, with
  * MOE_FFN_PACKED_WEIGHTS, says that w13 and w2 are in the packed layout
  * moe_pack_ffn_weights() produces.  Segments that reach past `capacity` are
- * skipped and raise MOE_DEVERR_ROW_RANGE.
+ * skipped and raise MOE_DEVERR_ROW_RANGE.  capacity 0 (an empty batch)
+ * returns MOE_OK after the scalar checks, touching no pointer (the FP8 and
+ * FP8-path variants below behave the same).
  * Requires H % 128 == 0, I % 128 == 0, 1 <= G <= 1024. */
 size_t moe_grouped_ffn_workspace_bytes(int64_t capacity, int num_groups, int H, int I);
 int moe_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32_t* counts,

@@ -127,6 +127,42 @@ def test_layer_tiny_variants(variant):
         assert abs(s_gpu - float(ref["combine_scale"])) <= TOL * float(ref["combine_scale"])
 
 
+@pytest.mark.parametrize("variant", ["plain", "everything"])
+def test_layer_all_padding(variant):
+    """Every token a padding row: no slot is routed, every segment is empty
+    (pow2 buckets too), the combine-row scale calibrates to 0 as the
+    oracle's does, and the output is +0 (no shared expert) or exactly the
+    shared expert's row (its slot is the only one)."""
+    base = workloads.CONFIGS["tiny"]
+    cfg = {"plain": base.with_(pad_rows=base.T),
+           "everything": base.with_(pad_rows=base.T, dispatch_block=128, pad_pow2=True,
+                                    shared_I=256, combine_qdq=True)}[variant]
+    W = Weights(cfg)
+    lg, hd, vd = workloads.logits(cfg), workloads.hidden(cfg), workloads.row_valid(cfg)
+    assert not vd.any()
+    kw = dict(dispatch_block=cfg.dispatch_block or None, pad_pow2=cfg.pad_pow2,
+              shared_weights=W.shared_host, combine_qdq=cfg.combine_qdq)
+    ref = oracle.moe_layer(lg, hd, lambda e: W.host[e], cfg.K, vd, **kw)
+    layer = _gpu_layer(cfg, W, lg, hd, vd)                 # calibrates its own scale
+    np.testing.assert_array_equal(host(layer.topk_idx), ref["topk_idx"])
+    np.testing.assert_array_equal(host(layer.topk_w), ref["topk_w"])
+    p = ref["perm"]
+    for name in ("counts", "cu_seqlens", "row_of"):
+        np.testing.assert_array_equal(host(getattr(layer.perm, name)), p[name])
+    assert int(p["cu_seqlens"][-1]) == 0
+    if cfg.combine_qdq:
+        assert float(host(layer.combine_scale)[0]) == float(ref["combine_scale"]) == 0.0
+    if cfg.shared_I:
+        got, want = bf16_bits_to_f64(host_bits(layer.out)), bf16_bits_to_f64(ref["out"])
+        assert rel_err(got, want) <= TOL
+        # +0 + s rounds to s (a -0 to +0): the output is the GPU's own
+        # shared-expert row
+        sb = host_bits(layer.stage_outputs()["shared"])
+        np.testing.assert_array_equal(host_bits(layer.out), np.where(sb == 0x8000, 0, sb))
+    else:
+        assert np.all(host_bits(layer.out) == 0) and np.all(ref["out"] == 0)
+
+
 @pytest.mark.parametrize("dfmt,cfmt,shared_I", [("nvfp4", "nvfp4", 0), ("mxfp4", "mxfp4", 128),
                                                  ("nvfp4", "mxfp4", 0), (None, "nvfp4", 256)])
 def test_layer_fp4_quantizers(dfmt, cfmt, shared_I):

@@ -330,6 +330,33 @@ def test_permute_dispatch_fp8_equals_quantize_then_permute(T, K, E, H, pow2, beg
     np.testing.assert_array_equal(host_bits(p.x_perm)[rows], ref["x_perm"][rows])
 
 
+def test_empty_batch_every_stage():
+    """T = 0 through route, permute, both FFN modes and combine: no error,
+    empty outputs, all-zero counts and cu_seqlens."""
+    E, K, H, I = 8, 2, 256, 128
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    idx, w = ops.moe_route(torch.zeros(0, E, device="cuda"), K)
+    assert tuple(idx.shape) == (0, K) and tuple(w.shape) == (0, K)
+    hid = torch.zeros(0, H, dtype=torch.bfloat16, device="cuda")
+    for pow2 in (False, True):
+        p = ops.moe_permute(idx, w, hid, E, 0, pow2, dev_error=err)
+        np.testing.assert_array_equal(host(p.counts), np.zeros(E, np.int32))
+        np.testing.assert_array_equal(host(p.cu_seqlens), np.zeros(E + 1, np.int32))
+        assert p.x_perm.shape[0] == 0
+    w13 = torch.zeros(E, 2 * I, H, dtype=torch.bfloat16, device="cuda")
+    w2 = torch.zeros(E, H, I, dtype=torch.bfloat16, device="cuda")
+    y = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13, w2, p.w_perm, dev_error=err)
+    assert tuple(y.shape) == (0, H)
+    w13p, w2p = ops.moe_pack_ffn_weights(w13, w2)
+    y = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13p, w2p, p.w_perm, dev_error=err,
+                            flags=ops.MOE_FFN_ALL | ops.MOE_FFN_PACKED_WEIGHTS)
+    assert tuple(y.shape) == (0, H)
+    out = ops.moe_combine(y, p.row_of, 0, K, dev_error=err)
+    assert tuple(out.shape) == (0, H)
+    torch.cuda.synchronize()
+    assert host(err)[0] == 0
+
+
 def test_permute_capacity_overflow_is_flagged_not_written():
     rng = np.random.default_rng(9)
     T, K, E, H = 64, 4, 8, 128

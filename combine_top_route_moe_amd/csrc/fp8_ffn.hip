@@ -61,6 +61,12 @@ __device__ __forceinline__ uint2 e4m3x8(const float* r) {
 
 __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
 
+// One DPP lane movement within each row of 16 lanes (every lane active).
+template <int kCtrl>
+__device__ __forceinline__ float row16_dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
 // ---------------------------------------------------------------------------
 // Rows to FP8: one 16-byte vector (8 channels) per thread, 16 lanes per
 // 128-channel block.  s = amax / 448 (IEEE), code = e4m3(clamp(x / s))
@@ -84,15 +90,34 @@ __global__ void __launch_bounds__(256) quant_rows_fp8_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(f[j]));
   }
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+  // the block's 16 lanes are one DPP row: its max in registers by two quad
+  // permutations (lane ^ 1, lane ^ 2), the half-row mirror and the row
+  // mirror (max is exact, the order does not matter)
+  m = fmaxf(m, row16_dpp<0xB1>(m));   // quad_perm [1, 0, 3, 2]
+  m = fmaxf(m, row16_dpp<0x4E>(m));   // quad_perm [2, 3, 0, 1]
+  m = fmaxf(m, row16_dpp<0x141>(m));  // row_half_mirror
+  m = fmaxf(m, row16_dpp<0x140>(m));  // row_mirror
   const float s = m / 448.0f;
   if (!in_range) return;
   uint2 q = make_uint2(0, 0);
   if (s > 0.0f) {
     float rq[8];
+    if (rcp_scale_ok(s)) {
+      // x / s from the reciprocal by one correction step, clamped, with the
+      // sign of x (the quotient steps of qdq8_rcp): the same E4M3 value as
+      // the IEEE quotient clamped to +-448, zeros' signs included
+      const float inv_s = 1.0f / s;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) rq[j] = clamp448(f[j] / s);
+      for (int j = 0; j < 8; ++j) {
+        const float a = __builtin_amdgcn_fmed3f(f[j] * inv_s, -512.0f, 512.0f);
+        const float res = __builtin_fmaf(a, s, -f[j]);
+        rq[j] = __builtin_copysignf(
+            __builtin_amdgcn_fmed3f(__builtin_fmaf(-res, inv_s, a), -448.0f, 448.0f), f[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) rq[j] = clamp448(f[j] / s);
+    }
     q = e4m3x8(rq);
   }
   reinterpret_cast<uint2*>(codes)[v] = q;

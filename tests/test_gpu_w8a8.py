@@ -65,6 +65,34 @@ def test_quant_rows_fp8_matches_oracle():
     np.testing.assert_array_equal(np.signbit(vals), np.signbit(q_want))
 
 
+@pytest.mark.parametrize("arrange", ["shuffled", "sorted"])
+def test_quant_rows_fp8_exhaustive(arrange):
+    """Every finite bfloat16 value once, in 1 x 128 blocks of mixed magnitude
+    (shuffled) or of similar magnitude (sorted: every scale range, including
+    the subnormal and the largest blocks, whose scales lie outside the
+    reciprocal's exact range, where the kernel divides): codes, their signs
+    and the scales bit-exact with the oracle."""
+    bits = np.arange(2 ** 16, dtype=np.uint32).astype(np.uint16)
+    bits = bits[np.isfinite(bf16_bits_to_f32(bits))]
+    if arrange == "shuffled":
+        bits = np.random.default_rng(13).permutation(bits)
+    else:
+        bits = bits[np.argsort(np.abs(bf16_bits_to_f32(bits)), kind="stable")]
+    H = 512
+    bits = np.concatenate([bits, np.zeros((-len(bits)) % H, np.uint16)]).reshape(-1, H)
+    R = bits.shape[0]
+    codes, scales = ops.moe_quant_rows_fp8(dev_bf16(bits))
+    torch.cuda.synchronize()
+    q_want, s_want = oracle.quantize_rows_fp8(bits)
+    s_got = host(scales)[:, :R].T
+    if arrange == "sorted":                 # both fallback ranges are reached
+        assert s_got[s_got > 0].min() < 2.0 ** -90 and s_got.max() > 2.0 ** 90
+    np.testing.assert_array_equal(s_got.view(np.uint32), s_want.view(np.uint32))
+    vals = e4m3_decode(host(codes))
+    np.testing.assert_array_equal(vals, q_want)
+    np.testing.assert_array_equal(np.signbit(vals), np.signbit(q_want))
+
+
 def unpack_k128(q: np.ndarray, gate_up: bool, G: int, N: int, Kdim: int) -> np.ndarray:
     """K=128-layout codes back to row-major [G, N, Kdim]: 16-byte unit
     ((((g * Kdim/128 + kb) * n_ct + ct) * 4 + f) * 2 + h) * 64 + l holds row

@@ -399,8 +399,12 @@ __global__ void __launch_bounds__(kQNW * kWave, 2) w8a8_gemm_kernel(
           av[ii][f][q] = __uint_as_float(f32_to_bf16(v) << 16);
           m = fmaxf(m, fabsf(av[ii][f][q]));
         }
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+        // the row's 16 lanes are one DPP row (my_live is the same for the
+        // whole wave, so all of them are here): its max in registers
+        m = fmaxf(m, row16_dpp<0xB1>(m));
+        m = fmaxf(m, row16_dpp<0x4E>(m));
+        m = fmaxf(m, row16_dpp<0x141>(m));
+        m = fmaxf(m, row16_dpp<0x140>(m));
         if ((lane & 15) == 0) red[cw][(i0 + ii) * 16 + 4 * (lane >> 4) + q] = m;
       }
     }

@@ -239,7 +239,7 @@ def main():
                          "bandwidth; its byte counters scale the PMC traffic figures")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the MoE layer here runs on one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU expert-parallel exchange is not implemented", file=sys.stderr)
         sys.exit(2)
 

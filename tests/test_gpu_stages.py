@@ -56,6 +56,21 @@ def test_route_shapes_and_ties(T, E, K):
     _route_case(logits2, K, valid)
 
 
+@pytest.mark.parametrize("E", [64, 128, 256, 1000])
+def test_route_signed_zero_ties(E):
+    """Rows of mostly +0 and -0 logits (equal in the order: the lower index
+    wins) with a few positive and negative ones, spread over every lane group
+    of the wave: the argmax kernels (E > 64) and the rank kernel (E = 64)
+    pick the oracle's slots."""
+    rng = np.random.default_rng(E)
+    T, K = 40, 8
+    logits = np.where(rng.random((T, E)) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+    hot = rng.random((T, E)) < 0.03
+    logits[hot] = rng.choice([-1.0, 0.5, 1.0], hot.sum()).astype(np.float32)
+    _route_case(logits, K)
+    _route_case(logits, K, renorm=False)
+
+
 def test_route_rejects_bad_args():
     x = torch.zeros(4, 8, device="cuda")
     with pytest.raises(RuntimeError):

@@ -21,7 +21,7 @@ SIGNATURES = {
     "moe_permute_capacity": (_c_i64, [_c_int, _c_int, _c_int, _c_int]),
     "moe_permute_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "moe_permute": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
-                             _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp, _vp]),
+                             _c_int, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp, _vp]),
     "moe_grouped_ffn_workspace_bytes": (_c_size, [_c_i64, _c_int, _c_int, _c_int]),
     "moe_grouped_ffn": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp,
                                  _c_i64, _c_int, _vp, _c_size, _vp, _vp]),
@@ -37,7 +37,7 @@ SIGNATURES = {
                                       _c_size, _vp, _vp]),
     "moe_fake_quant_rows": (_c_int, [_vp, _vp, _c_i64, _c_int, _vp, _c_int, _c_int, _vp, _vp,
                                      _vp, _vp]),
-    "moe_scale_from_amax": (_c_int, [_vp, _vp, _vp]),
+    "moe_scale_from_amax": (_c_int, [_vp, _vp, _c_int, _vp]),
     "moe_combine": (_c_int, [_vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp,
                              _vp]),
     "moe_combine_check": (_c_int, [_vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp,

@@ -10,13 +10,13 @@ namespace moe {
 int launch_route(const float*, const uint8_t*, int, int, int, int, int32_t*, float*, hipStream_t);
 int launch_fake_quant(const uint16_t*, uint16_t*, int64_t, int, const int32_t*, int, const float*,
                       float*, float*, hipStream_t);
-int launch_scale_from_amax(const float*, float*, hipStream_t);
+int launch_scale_from_amax(const float*, float*, int, hipStream_t);
 int launch_combine(const uint16_t*, int64_t, const int32_t*, const uint16_t*, int, int, int,
                    const float*, uint16_t*, int32_t*, hipStream_t);
 int launch_combine_check(const uint16_t*, int64_t, const int32_t*, const uint16_t*, int, int, int,
                          const uint16_t*, int32_t*, int32_t*, hipStream_t);
 size_t permute_workspace_bytes(int64_t, int);
-int launch_permute(const int32_t*, const float*, const uint16_t*, int, int, int, int, int, int,
+int launch_permute(const int32_t*, const float*, const uint16_t*, int, int, int, int, int, int, int,
                    int, int64_t, int32_t*, int32_t*, uint16_t*, int32_t*, int32_t*, float*, void*,
                    int32_t*, hipStream_t);
 size_t grouped_ffn_workspace_bytes(int64_t, int, int);
@@ -99,13 +99,17 @@ size_t moe_permute_workspace_bytes(int T, int K, int num_local_experts, int flag
   return permute_workspace_bytes((int64_t)T * K, num_local_experts);
 }
 
-int moe_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t* hidden, int T, int K,
-                int H, int expert_begin, int num_local_experts, int flags, int64_t capacity,
-                int32_t* counts, int32_t* cu_seqlens, uint16_t* x_perm, int32_t* row_of,
-                int32_t* src_of, float* w_perm, void* workspace, size_t workspace_bytes,
-                int32_t* dev_error, void* stream) {
+// Argument checks of moe_permute (scalars and
+// pointers only).
+static int check_permute_args(const int32_t* topk_idx, const float* topk_w, const uint16_t* hidden,
+                              int T, int K, int H, int num_experts, int expert_begin,
+                              int num_local_experts, int flags, int64_t capacity,
+                              const int32_t* counts, const int32_t* cu_seqlens,
+                              const uint16_t* x_perm, const int32_t* row_of,
+                              const int32_t* src_of, const float* w_perm) {
   if (T < 0 || K < 1 || H < 1 || num_local_experts < 1 || capacity < 0 || expert_begin < 0)
     return MOE_ERR_INVALID_ARG;
+  if ((int64_t)expert_begin + num_local_experts > (int64_t)num_experts) return MOE_ERR_INVALID_ARG;
   if (flags & ~(MOE_PERMUTE_PAD_POW2 | MOE_PERMUTE_DISPATCH_FP8)) return MOE_ERR_INVALID_ARG;
   if (H % 128 || num_local_experts > 1024 || K > 64) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)T * K > 0x7fffffffLL || capacity > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
@@ -113,10 +117,22 @@ int moe_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t* hi
   if (T > 0 && (!topk_idx || !topk_w || !hidden || !row_of)) return MOE_ERR_INVALID_ARG;
   if (capacity > 0 && (!x_perm || !src_of || !w_perm)) return MOE_ERR_INVALID_ARG;
   if ((hidden && !aligned16(hidden)) || (x_perm && !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int moe_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t* hidden, int T, int K,
+                int H, int num_experts, int expert_begin, int num_local_experts, int flags,
+                int64_t capacity, int32_t* counts, int32_t* cu_seqlens, uint16_t* x_perm,
+                int32_t* row_of, int32_t* src_of, float* w_perm, void* workspace,
+                size_t workspace_bytes, int32_t* dev_error, void* stream) {
+  const int st = check_permute_args(topk_idx, topk_w, hidden, T, K, H, num_experts, expert_begin,
+                                    num_local_experts, flags, capacity, counts, cu_seqlens,
+                                    x_perm, row_of, src_of, w_perm);
+  if (st != MOE_OK) return st;
   const size_t need = permute_workspace_bytes((int64_t)T * K, num_local_experts);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
-  return launch_permute(topk_idx, topk_w, hidden, T, K, H, expert_begin, num_local_experts,
-                        (flags & MOE_PERMUTE_PAD_POW2) ? 1 : 0,
+  return launch_permute(topk_idx, topk_w, hidden, T, K, H, num_experts, expert_begin,
+                        num_local_experts, (flags & MOE_PERMUTE_PAD_POW2) ? 1 : 0,
                         (flags & MOE_PERMUTE_DISPATCH_FP8) ? 1 : 0, capacity, counts, cu_seqlens,
                         x_perm, row_of, src_of, w_perm, workspace, dev_error, as_stream(stream));
 }
@@ -271,9 +287,10 @@ int moe_fake_quant_rows(const uint16_t* in, uint16_t* out, int64_t n_rows, int H
                            as_stream(stream));
 }
 
-int moe_scale_from_amax(const float* amax, float* scale, void* stream) {
+int moe_scale_from_amax(const float* amax, float* scale, int mode, void* stream) {
   if (!amax || !scale) return MOE_ERR_INVALID_ARG;
-  return launch_scale_from_amax(amax, scale, as_stream(stream));
+  if (mode != MOE_FQ_PER_TENSOR && mode != MOE_FQ_NVFP4) return MOE_ERR_INVALID_ARG;
+  return launch_scale_from_amax(amax, scale, mode, as_stream(stream));
 }
 
 int moe_combine(const uint16_t* rows, int64_t num_rows, const int32_t* row_of,

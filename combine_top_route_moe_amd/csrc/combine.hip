@@ -1,9 +1,10 @@
 // Ordered combine of the per-(token, slot) rows.
 //
 // Source: "Add MoE dispatch/combine fake quantization for vLLM's DeepGEMM
-// Mega-MoE", PR summary and "How it works": valid slots in ascending order,
-// FP32 starting from zero, one BF16 rounding, a fused shared expert's slot
-// last and unquantized.
+// Mega-MoE", PR summary and "How it works": the order is fixed there — the
+// token's routed rows are added slot by slot, lowest slot index first, into
+// a float32 sum that begins at zero; the result is rounded to bf16 once; a
+// fused shared expert comes after all routed slots and is never quantized.
 //
 // Each thread owns 8 consecutive channels of one token (a 16-byte vector):
 // it walks the token's K slots in order, gathers one vector per valid slot

@@ -133,12 +133,17 @@ __global__ void __launch_bounds__(256) fake_quant_kernel(
   reinterpret_cast<uint4*>(out)[v] = res;
 }
 
-__global__ void scale_from_amax_kernel(const float* __restrict__ amax, float* __restrict__ scale) {
-  if (threadIdx.x == 0) scale[0] = amax[0] / 448.0f;
+// The per-tensor scale from a calibrated amax, one IEEE division by the
+// format's largest code magnitude: 448 for E4M3 (FP8), 6 * 448 = 2688 for
+// the NVFP4 tensor scale (E2M1's 6 under an E4M3 block scale's 448).
+__global__ void scale_from_amax_kernel(const float* __restrict__ amax, float* __restrict__ scale,
+                                       float divisor) {
+  if (threadIdx.x == 0) scale[0] = amax[0] / divisor;
 }
 
-int launch_scale_from_amax(const float* amax, float* scale, hipStream_t stream) {
-  hipLaunchKernelGGL(scale_from_amax_kernel, dim3(1), dim3(64), 0, stream, amax, scale);
+int launch_scale_from_amax(const float* amax, float* scale, int mode, hipStream_t stream) {
+  const float divisor = mode == MOE_FQ_NVFP4 ? 6.0f * 448.0f : 448.0f;
+  hipLaunchKernelGGL(scale_from_amax_kernel, dim3(1), dim3(64), 0, stream, amax, scale, divisor);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -90,9 +90,17 @@ constexpr int kChunk = 1024;
 constexpr int kFuseTable = 4096;   // chunk-table entries up to which the scan is fused
 constexpr int kFuseChunks = 16;    // ... and chunks (each workgroup sums its table columns)
 
+// An id at or past the layer's expert count names no expert: it is not
+// routed (the local-range test below already excludes it, since the local
+// experts lie inside [0, num_experts)) and the error word records it.
+__device__ __forceinline__ void check_expert_id(int id, int num_experts, int32_t* dev_error) {
+  if (id >= num_experts) raise_error(dev_error, MOE_DEVERR_EXPERT_RANGE);
+}
+
 __global__ void __launch_bounds__(256) permute_chunk_rank_kernel(
-    const int32_t* __restrict__ topk_idx, int64_t TK, int expert_begin, int El, int nbits,
-    int32_t* __restrict__ table /* [nchunks][El] */, int32_t* __restrict__ rank /* [TK] */) {
+    const int32_t* __restrict__ topk_idx, int64_t TK, int num_experts, int expert_begin, int El,
+    int nbits, int32_t* __restrict__ table /* [nchunks][El] */,
+    int32_t* __restrict__ rank /* [TK] */, int32_t* __restrict__ dev_error) {
   // wave w ranks slots [256 w, 256 w + 256) of the chunk, 64 at a time, with
   // its own running per-expert counts; afterwards each slot adds the counts
   // of the waves before it
@@ -111,6 +119,7 @@ __global__ void __launch_bounds__(256) permute_chunk_rank_kernel(
       const int id = topk_idx[i];
       const int le = id - expert_begin;
       if (id >= 0 && le >= 0 && le < El) e = le;
+      check_expert_id(id, num_experts, dev_error);
     }
     uint64_t peers = __ballot(e >= 0);
     for (int b = 0; b < nbits; ++b) {
@@ -433,7 +442,8 @@ constexpr int kSmallPre = 4;                       // row vectors per thread loa
 template <bool QDQ>
 __global__ void __launch_bounds__(256) permute_small_kernel(
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
-    const uint16_t* __restrict__ hidden, int T, int K, int H, int expert_begin, int El,
+    const uint16_t* __restrict__ hidden, int T, int K, int H, int num_experts, int expert_begin,
+    int El,
     int tok_per_block, int pad_pow2, int64_t capacity, uint16_t* __restrict__ x_perm,
     int32_t* __restrict__ row_of, int32_t* __restrict__ src_of, float* __restrict__ w_perm,
     int32_t* __restrict__ dev_error, int32_t* __restrict__ counts,
@@ -480,6 +490,7 @@ __global__ void __launch_bounds__(256) permute_small_kernel(
     hist_pre[e] = 0;
   }
   if (tid < 256) own_e[tid] = local_expert(own_id);
+  if (tid < nslots) check_expert_id(own_id, num_experts, dev_error);   // each slot once
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < kSmallIds; ++q) {
@@ -606,7 +617,8 @@ size_t permute_workspace_bytes(int64_t TK, int El) {
 }
 
 int launch_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t* hidden, int T,
-                   int K, int H, int expert_begin, int El, int pad_pow2, int dispatch_fp8,
+                   int K, int H, int num_experts, int expert_begin, int El, int pad_pow2,
+                   int dispatch_fp8,
                    int64_t capacity,
                    int32_t* counts, int32_t* cu_seqlens, uint16_t* x_perm, int32_t* row_of,
                    int32_t* src_of, float* w_perm, void* workspace, int32_t* dev_error,
@@ -627,15 +639,15 @@ int launch_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t*
   if (TK <= kSmallTK && El <= 1024) {
 #define MOE_PERMUTE_SMALL(Q)                                                                   \
   hipLaunchKernelGGL(permute_small_kernel<Q>, dim3(grid), dim3(256), 0, stream, topk_idx, topk_w, \
-                     hidden, T, K, H, expert_begin, El, tpb, pad_pow2, capacity, x_perm, row_of,   \
-                     src_of, w_perm, dev_error, counts, cu_seqlens)
+                     hidden, T, K, H, num_experts, expert_begin, El, tpb, pad_pow2, capacity,      \
+                     x_perm, row_of, src_of, w_perm, dev_error, counts, cu_seqlens)
     if (dispatch_fp8) MOE_PERMUTE_SMALL(true); else MOE_PERMUTE_SMALL(false);
 #undef MOE_PERMUTE_SMALL
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   }
   if (nchunks > 0)
     hipLaunchKernelGGL(permute_chunk_rank_kernel, dim3(nchunks), dim3(256), 0, stream, topk_idx,
-                       TK, expert_begin, El, nbits, table, rank);
+                       TK, num_experts, expert_begin, El, nbits, table, rank, dev_error);
   const bool fused = (int64_t)nchunks * El <= kFuseTable && nchunks <= kFuseChunks && El <= 1024;
   if (!fused)
     hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, stream, table, nchunks, El,

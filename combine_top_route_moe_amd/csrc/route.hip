@@ -56,6 +56,17 @@ __device__ __forceinline__ double sum_lanes_below(double x, int n) {
   return s;
 }
 
+// A NaN logit ranks as -inf: it can never hide a real candidate from the
+// argmax (every comparison with a NaN is false) and the order stays total.
+__device__ __forceinline__ float rank_value(float x) { return x != x ? -__builtin_inff() : x; }
+
+// exp(l - l_max) in double, with an l equal to l_max counting exp(0) even
+// when both are infinite (inf - inf would be NaN): the limit of the softmax
+// as the infinite logits grow, and for finite logits the same value.
+__device__ __forceinline__ double weight_term(float l, float lmax) {
+  return l == lmax ? 1.0 : exp((double)l - (double)lmax);
+}
+
 // EPL: experts per lane (E <= 64 * EPL).
 template <int EPL>
 __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ logits,
@@ -81,7 +92,7 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     int e = lane + j * kWave;
-    v[j] = e < E ? row[e] : 0.0f;
+    v[j] = e < E ? rank_value(row[e]) : 0.0f;
   }
   uint32_t taken = 0;  // bit j: expert lane + 64 j already chosen (or absent)
 #pragma unroll
@@ -128,14 +139,14 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
 
   // weights: exp(l_k - l_max) / sum, in double
   double num = 0.0;
-  if (lane < K) num = exp((double)sel_v - (double)lmax);
+  if (lane < K) num = weight_term(sel_v, lmax);
   double den = 0.0;
   if (renorm) {
     den = sum_lanes_below(num, K);   // the K slot terms, slot order
   } else {
 #pragma unroll
     for (int j = 0; j < EPL; ++j)
-      if (lane + j * kWave < E) den += exp((double)v[j] - (double)lmax);
+      if (lane + j * kWave < E) den += weight_term(v[j], lmax);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, kWave);
   }
@@ -176,7 +187,7 @@ __global__ void __launch_bounds__(256) route_rank_kernel(const float* __restrict
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + j * kWave;
-    v[j] = e < E ? row[e] : 0.0f;
+    v[j] = e < E ? rank_value(row[e]) : 0.0f;
     row_lds[wv][e] = v[j];
   }
   // one wave owns row_lds[wv]; its writes are visible to its own later reads
@@ -208,16 +219,16 @@ __global__ void __launch_bounds__(256) route_rank_kernel(const float* __restrict
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   // weights: exp(l_k - l_max) / sum, in double; lane k < K holds slot k
-  const double lmax = (double)sel_lds[wv][0];
+  const float lmax = sel_lds[wv][0];
   double num = 0.0;
-  if (lane < K) num = exp((double)sel_lds[wv][lane] - lmax);
+  if (lane < K) num = weight_term(sel_lds[wv][lane], lmax);
   double den = 0.0;
   if (renorm) {
     den = sum_lanes_below(num, K);   // the K slot terms, slot order
   } else {
 #pragma unroll
     for (int j = 0; j < EPL; ++j)
-      if (lane + j * kWave < E) den += exp((double)v[j] - lmax);
+      if (lane + j * kWave < E) den += weight_term(v[j], lmax);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, kWave);
   }

@@ -20,7 +20,6 @@ from __future__ import annotations
 
 from typing import Callable, Dict, List, Optional, Tuple
 
-import numpy as np
 import torch
 
 from . import ops
@@ -225,7 +224,8 @@ class MoELayer:
         fuse = self.fuse_dispatch and not self.w8a8
         st.append(("permute", lambda: ops.moe_permute(
             self.topk_idx, self.topk_w, x, self.El, self.expert_begin, self.pad_pow2,
-            self.capacity, p, self.perm_ws, self.dev_error, dispatch_fp8=fuse)))
+            self.capacity, p, self.perm_ws, self.dev_error, dispatch_fp8=fuse,
+            num_experts=self.E)))
         st.append(("ffn_gate_up", lambda: self._ffn(
             x_ffn, p.cu_seqlens, p.counts, self.w13, self.w2, p.w_perm, self.y_perm,
             ops.MOE_FFN_GATE_UP, self.ffn_ws)))
@@ -273,7 +273,8 @@ class MoELayer:
     def calibrate_combine_scale(self, logits, hidden, row_valid=None) -> torch.Tensor:
         """One-time max calibration of the constant combine-row scale: run the
         layer without combine-row QDQ, take max|row| over the routed rows and
-        store amax/448 (FP8) or amax/(6*448) (NVFP4) on the device."""
+        amax/448 (FP8) or amax/(6*448) (NVFP4) into the device scalar, all on
+        the device (``moe_scale_from_amax``): no host round trip."""
         qdq, fp4 = self.combine_qdq, self.combine_fp4
         self.combine_qdq, self.combine_fp4 = False, None
         self.forward(logits, hidden, row_valid)
@@ -283,13 +284,8 @@ class MoELayer:
                                 128, None, None, self.amax)
         if self.combine_scale is None:
             self.combine_scale = torch.zeros(1, dtype=torch.float32, device=self.device)
-        if self.combine_fp4 == "nvfp4":
-            # one-time, outside the layer's hot path (a host sync is fine here):
-            # the IEEE float32 quotient amax / (6 * 448)
-            g = np.float32(np.float32(self.amax.item()) / np.float32(6.0 * 448.0))
-            self.combine_scale.fill_(float(g))
-        else:
-            ops.moe_scale_from_amax(self.amax, self.combine_scale)
+        mode = ops.MOE_FQ_NVFP4 if self.combine_fp4 == "nvfp4" else ops.MOE_FQ_PER_TENSOR
+        ops.moe_scale_from_amax(self.amax, self.combine_scale, mode=mode)
         return self.combine_scale
 
     def stage_outputs(self) -> Dict[str, torch.Tensor]:

@@ -20,7 +20,7 @@ MOE_PERMUTE_PAD_POW2 = 1
 MOE_PERMUTE_DISPATCH_FP8 = 2
 MOE_FFN_GATE_UP, MOE_FFN_DOWN, MOE_FFN_ALL, MOE_FFN_PACKED_WEIGHTS = 1, 2, 3, 4
 MOE_FQ_PER_TENSOR, MOE_FQ_BLOCK, MOE_FQ_NVFP4, MOE_FQ_MXFP4 = 0, 1, 2, 3
-MOE_DEVERR_ROW_RANGE, MOE_DEVERR_CAPACITY, MOE_DEVERR_LAYOUT = 1, 2, 3
+MOE_DEVERR_ROW_RANGE, MOE_DEVERR_CAPACITY, MOE_DEVERR_LAYOUT, MOE_DEVERR_EXPERT_RANGE = 1, 2, 3, 4
 MOE_FP8_LAYOUT_K128 = 1
 
 
@@ -100,15 +100,19 @@ def moe_permute(topk_idx: torch.Tensor, topk_w: torch.Tensor, hidden: torch.Tens
                 capacity: Optional[int] = None, out: Optional[Permuted] = None,
                 workspace: Optional[torch.Tensor] = None,
                 dev_error: Optional[torch.Tensor] = None, stream=None,
-                dispatch_fp8: bool = False) -> Permuted:
+                dispatch_fp8: bool = False, num_experts: Optional[int] = None) -> Permuted:
     """``dispatch_fp8``: the rows are written FP8 fake-quantized in 1 x 128
-    blocks (MOE_PERMUTE_DISPATCH_FP8)."""
+    blocks (MOE_PERMUTE_DISPATCH_FP8).  ``num_experts``: the layer's total
+    expert count (ids at or past it raise MOE_DEVERR_EXPERT_RANGE); by
+    default the end of the local range, i.e. all experts local."""
     _want(topk_idx, torch.int32, "topk_idx")
     _want(topk_w, torch.float32, "topk_w")
     _want(hidden, torch.bfloat16, "hidden")
     T, K = topk_idx.shape
     H = hidden.shape[1]
     flags = (MOE_PERMUTE_PAD_POW2 if pad_pow2 else 0) | (MOE_PERMUTE_DISPATCH_FP8 if dispatch_fp8 else 0)
+    if num_experts is None:
+        num_experts = expert_begin + num_local_experts
     lib = load()
     if capacity is None:
         capacity = out.x_perm.shape[0] if out is not None else lib.moe_permute_capacity(
@@ -119,7 +123,8 @@ def moe_permute(topk_idx: torch.Tensor, topk_w: torch.Tensor, hidden: torch.Tens
     if workspace is None:
         workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=hidden.device)
     check("moe_permute", lib.moe_permute(
-        _ptr(topk_idx), _ptr(topk_w), _ptr(hidden), T, K, H, expert_begin, num_local_experts,
+        _ptr(topk_idx), _ptr(topk_w), _ptr(hidden), T, K, H, num_experts, expert_begin,
+        num_local_experts,
         flags, capacity, _ptr(out.counts), _ptr(out.cu_seqlens), _ptr(out.x_perm),
         _ptr(out.row_of), _ptr(out.src_of), _ptr(out.w_perm), _ptr(workspace),
         workspace.numel(), _ptr(dev_error), _stream(stream)))
@@ -337,10 +342,12 @@ def moe_fake_quant_rows(inp: torch.Tensor, out: Optional[torch.Tensor] = None,
 
 
 def moe_scale_from_amax(amax: torch.Tensor, scale: Optional[torch.Tensor] = None,
-                        stream=None) -> torch.Tensor:
+                        stream=None, mode: int = MOE_FQ_PER_TENSOR) -> torch.Tensor:
+    """``mode``: MOE_FQ_PER_TENSOR (FP8 scale) or MOE_FQ_NVFP4 (tensor scale)."""
     _want(amax, torch.float32, "amax")
     scale = torch.empty(1, dtype=torch.float32, device=amax.device) if scale is None else scale
-    check("moe_scale_from_amax", load().moe_scale_from_amax(_ptr(amax), _ptr(scale), _stream(stream)))
+    check("moe_scale_from_amax", load().moe_scale_from_amax(_ptr(amax), _ptr(scale), mode,
+                                                            _stream(stream)))
     return scale
 
 

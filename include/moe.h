@@ -59,8 +59,9 @@ enum {
 enum {
   MOE_DEVERR_ROW_RANGE = 1, /* a row index points outside its buffer       */
   MOE_DEVERR_CAPACITY = 2,  /* the segments need more rows than `capacity` */
-  MOE_DEVERR_LAYOUT = 3     /* moe_combine_check: rows do not reproduce the
+  MOE_DEVERR_LAYOUT = 3,    /* moe_combine_check: rows do not reproduce the
                                output they were checked against          */
+  MOE_DEVERR_EXPERT_RANGE = 4 /* moe_permute: a router id >= num_experts */
 };
 
 /* ---- flags -------------------------------------------------------------- */
@@ -103,7 +104,11 @@ int moe_device_check(int device);
  *   logits    [T, E] float32        row_valid  [T] uint8 or NULL
  *   topk_idx  [T, K] int32 (out)    topk_w     [T, K] float32 (out)
  * Requires 1 <= K <= min(E, 32), E <= 1024.  T = 0 enqueues nothing.
- * NaN logits are unsupported (their slot choice is unspecified). */
+ * Non-finite logits: a NaN ranks as -inf (below every number, ties among
+ * them to the lower index), so every id written lies in [0, E); in the
+ * weights, a logit equal to l_max counts exp(0) = 1 even when both are
+ * infinite (a row whose chosen logits are all -inf or NaN gets 1/K each,
+ * with MOE_ROUTE_RENORM), and a -inf below a finite l_max counts 0. */
 int moe_route(const float* logits, const uint8_t* row_valid, int T, int E, int K,
               int flags, int32_t* topk_idx, float* topk_w, void* stream);
 
@@ -116,8 +121,15 @@ int moe_route(const float* logits, const uint8_t* row_valid, int T, int E, int K
  * buckets, the permuted hidden states in a caller buffer).
  *
  * Slot (t, k) with flat index i = t*K + k is routed to local expert
- * e = topk_idx[i] - expert_begin when 0 <= e < num_local_experts; any other
- * value (negative = padding, or another rank's expert) is not routed here.
+ * e = topk_idx[i] - expert_begin when 0 <= e < num_local_experts.  A
+ * negative id is a padding slot ([P1] review thread on the buffer check: a
+ * slot is valid iff its id is >= 0); an id in [0, num_experts) outside the
+ * local range belongs to another rank's expert; both are not routed here.
+ * An id >= num_experts (the layer's total expert count) names no expert at
+ * all: it is not routed either, and raises MOE_DEVERR_EXPERT_RANGE, so a
+ * corrupt router output fails closed instead of silently vanishing from the
+ * combine ([P1] review thread on graph capture: a device-side check that
+ * records the failure without destroying the context).
  *   counts[e]      number of rows routed to e
  *   cu_seqlens[e]  first row of segment e; segment sizes are counts[e], or
  *                  next_pow2(counts[e]) (0 stays 0) with MOE_PERMUTE_PAD_POW2;
@@ -151,11 +163,13 @@ int moe_route(const float* logits, const uint8_t* row_valid, int T, int E, int K
  * need more rows, rows at or past `capacity` are not written and
  * MOE_DEVERR_CAPACITY is raised.  `workspace` holds
  * moe_permute_workspace_bytes() bytes of scratch (contents on entry are
- * ignored).  Requires H % 128 == 0, 1 <= num_local_experts <= 1024. */
+ * ignored).  Requires H % 128 == 0, 1 <= num_local_experts <= 1024,
+ * 0 <= expert_begin and expert_begin + num_local_experts <= num_experts. */
 int64_t moe_permute_capacity(int T, int K, int num_local_experts, int flags);
 size_t moe_permute_workspace_bytes(int T, int K, int num_local_experts, int flags);
 int moe_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t* hidden,
-                int T, int K, int H, int expert_begin, int num_local_experts, int flags,
+                int T, int K, int H, int num_experts, int expert_begin, int num_local_experts,
+                int flags,
                 int64_t capacity, int32_t* counts, int32_t* cu_seqlens, uint16_t* x_perm,
                 int32_t* row_of, int32_t* src_of, float* w_perm, void* workspace,
                 size_t workspace_bytes, int32_t* dev_error, void* stream);
@@ -334,11 +348,16 @@ int moe_fake_quant_rows(const uint16_t* in, uint16_t* out, int64_t n_rows, int H
  *     448) ), S = fl32(b * g), x' = bf16( fl32( e2m1(clamp(fl32(x / S), -6,
  *     6)) * S ) ); S == 0 gives +0; block_scales [n_rows, H/16] receives b. */
 
-/* scale[0] = fl32(amax[0] / 448) (IEEE division) on the device: turns a
- * calibrated amax into the constant per-tensor E4M3FN scale ([P1] "How it
- * works": a calibrated (max) or constant global combine scale; the
- * workloads' 1/448 * max|row|).  Both are device scalars. */
-int moe_scale_from_amax(const float* amax, float* scale, void* stream);
+/* The constant per-tensor scale from a calibrated amax, on the device, so
+ * that it never leaves the GPU ([P1] "How it works": a calibrated (max) or
+ * constant global combine scale; the workloads' 1/448 * max|row|):
+ *   mode MOE_FQ_PER_TENSOR (FP8):  scale[0] = fl32(amax[0] / 448)
+ *   mode MOE_FQ_NVFP4:             scale[0] = fl32(amax[0] / 2688), the
+ *        NVFP4 tensor scale (6, the largest E2M1 magnitude, times 448, the
+ *        largest E4M3 block scale)
+ * one IEEE float32 division each.  Both pointers are device scalars.  Any
+ * other mode: MOE_ERR_INVALID_ARG. */
+int moe_scale_from_amax(const float* amax, float* scale, int mode, void* stream);
 
 /* ---- combine ------------------------------------------------------------
  * out[t, :] = bf16( ((+0 + r_{t,k0}) + r_{t,k1}) + ... + shared[t, :] )
@@ -346,8 +365,10 @@ int moe_scale_from_amax(const float* amax, float* scale, void* stream);
  * each r_{t,k} = rows[row_of[t*K + k], :], every add one IEEE float32
  * add in exactly this order, then one round-to-nearest-even to bf16; the
  * shared expert's row is added last and never quantized ([P1] PR summary
- * and "How it works": ascending slot, FP32 from zero, one BF16 rounding,
- * a fused shared expert's slot last and unquantized).
+ * and "How it works" fix this order: the kernel re-adds each token's
+ * routed rows slot by slot in increasing slot index into a float32 sum
+ * that begins at zero, rounds to bf16 once at the end, and places a fused
+ * shared expert after every routed slot, without quantizing it).
  * row_qdq_scale != NULL fake-quantizes each routed row with that per-tensor
  * device scalar before it is added (the same bits as moe_fake_quant_rows
  * in MOE_FQ_PER_TENSOR mode followed by this call).

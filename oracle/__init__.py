@@ -36,7 +36,8 @@ from .quant import fake_quant_block, fake_quant_per_tensor, calibrate_amax, quan
 from .fp4 import e2m1_round, fake_quant_mxfp4, fake_quant_nvfp4, nvfp4_tensor_scale
 from .permute import permute, next_pow2
 from .ffn import expert_ffn, grouped_ffn
-from .fp8_gemm import quantize_rows_fp8, block_scaled_matmul, expert_ffn_w8a8, grouped_ffn_w8a8
+from .fp8_gemm import (quantize_rows_fp8, block_scaled_matmul, expert_ffn_w8a8,
+                       expert_ffn_w8a8_steps, grouped_ffn_w8a8)
 from .combine import combine
 from .layer import moe_layer
 
@@ -46,5 +47,5 @@ __all__ = [
     "route", "fake_quant_block", "fake_quant_per_tensor", "calibrate_amax",
     "permute", "next_pow2", "expert_ffn", "grouped_ffn", "combine", "moe_layer",
     "quantize_weight_blocks", "quantize_rows_fp8", "block_scaled_matmul", "expert_ffn_w8a8",
-    "grouped_ffn_w8a8",
+    "expert_ffn_w8a8_steps", "grouped_ffn_w8a8",
 ]

@@ -4,9 +4,10 @@ Test infrastructure only (see the package docstring).
 
 Source: "Add MoE dispatch/combine fake quantization for vLLM's DeepGEMM
 Mega-MoE", PR summary and "How it works": the per-(token, slot) rows are
-summed again in the kernel's order — valid slots in ascending order, in FP32
-starting from zero, one BF16 rounding at the end, and a fused shared
-expert's slot last (and never quantized).  A slot is valid iff its
+re-added in the order the fused kernel uses — slot by slot with the lowest
+valid slot index first, into a float32 sum that begins at zero, with a
+single rounding to bf16 after the last add; a fused shared expert is added
+after all routed slots and is never quantized.  A slot is valid iff its
 ``topk_idx >= 0`` (review thread on the buffer check).
 
 Every add below is a numpy float32 elementwise add, i.e. one IEEE binary32
@@ -30,7 +31,7 @@ def combine(rows_bits, row_of, T: int, K: int, shared_bits=None):
     row_of = np.asarray(row_of, dtype=np.int64).reshape(T, K)
     H = rows_bits.shape[1]
     acc = np.zeros((T, H), dtype=np.float32)             # +0.0
-    for k in range(K):                                   # ascending slot
+    for k in range(K):                                   # slot 0 first
         r = row_of[:, k]
         valid = r >= 0
         if not valid.any():

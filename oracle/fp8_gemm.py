@@ -81,11 +81,14 @@ def block_scaled_matmul(qa, sa, qb, sb, block: int = 128):
     return out
 
 
-def expert_ffn_w8a8(qx, sx, w13_bits, w2_bits):
+def expert_ffn_w8a8_steps(qx, sx, w13_bits, w2_bits):
     """One expert's FFN on FP8 rows ``(qx, sx)`` [n, H] with the bfloat16
-    weights quantized to 128 x 128 tiles: gate/up block-scaled product,
-    ``a = bf16(silu(g) * u)``, ``a`` quantized per 1 x 128 block, down
-    block-scaled product.  Returns float64 [n, H] (before the router weight)."""
+    weights quantized to 128 x 128 tiles, step by step: gate/up block-scaled
+    product, ``a = bf16(silu(g) * u)``, ``a`` quantized per 1 x 128 block
+    into ``(qa, sa)``, down block-scaled product ``y`` (float64 [n, H],
+    before the router weight).  Returns ``{"qa", "sa", "y", "w2q"}`` where
+    ``w2q = (q2, s2)`` is the down projection's quantized weight, so that a
+    caller can also run the down product on other intermediate codes."""
     q13, s13, _ = quantize_weight_blocks(w13_bits)
     q2, s2, _ = quantize_weight_blocks(w2_bits)
     h = block_scaled_matmul(qx, sx, q13, s13)
@@ -93,7 +96,13 @@ def expert_ffn_w8a8(qx, sx, w13_bits, w2_bits):
     a = silu(h[:, :inter]) * h[:, inter:]
     a_bits = f32_to_bf16_bits(a.astype(np.float32))
     qa, sa = quantize_rows_fp8(a_bits)
-    return block_scaled_matmul(qa, sa, q2, s2)
+    return {"qa": qa, "sa": sa, "y": block_scaled_matmul(qa, sa, q2, s2), "w2q": (q2, s2)}
+
+
+def expert_ffn_w8a8(qx, sx, w13_bits, w2_bits):
+    """``expert_ffn_w8a8_steps(...)["y"]``: float64 [n, H] before the router
+    weight."""
+    return expert_ffn_w8a8_steps(qx, sx, w13_bits, w2_bits)["y"]
 
 
 def grouped_ffn_w8a8(qx, sx, cu_seqlens, counts, weights, row_scale=None):

@@ -11,7 +11,7 @@ DeepGEMM Mega-MoE", "How it works") -> permute into expert segments
 "Purpose") -> grouped SwiGLU FFN with the route weight applied before the
 down projection (same page, commit message adding the modular experts) ->
 BF16 per-(token, slot) rows, fake-quantized by the combine quantizer with a
-calibrated or constant scale -> combine in ascending slot order with the
+calibrated or constant scale -> combine, lowest slot index first, with the
 shared expert's unquantized slot last (first page, PR summary).
 
 Readings where the pages are silent:
@@ -106,7 +106,7 @@ def moe_layer(logits, hidden_bits, weights, k: int, row_valid=None,
     else:
         hidden_q, dscales = hidden_bits, None
 
-    perm = permute(topk_idx, topk_w, hidden_q, El, expert_begin, pad_pow2)
+    perm = permute(topk_idx, topk_w, hidden_q, El, expert_begin, pad_pow2, num_experts=E)
     if fp8_gemm:
         src = perm["src_of"]
         tok = np.where(src >= 0, src // k, 0)

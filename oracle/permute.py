@@ -4,9 +4,9 @@ Test infrastructure only (see the package docstring).
 
 Sources:
 * "[Distributed][MoonEP] BF16 integration of MoonEP balanced EP backend",
-  "Purpose": the expert compute receives tokens already grouped per expert
-  row as ``[NvS, H]`` plus ``cu_seqlens`` and no per-token ids, so the
-  expert compute is a grouped GEMM over the ``cu_seqlens`` segments.
+  "Purpose": the experts are handed rows that are already sorted by expert,
+  an ``[NvS, H]`` matrix described by ``cu_seqlens`` with no per-token ids,
+  so each expert works on one contiguous segment of it (a grouped GEMM).
 * "[Bugfix][MoE] Size the permute scratch from its inputs", PR summary and
   "Details": the permute metadata is int32 arrays over the expanded rows,
   sized from the rows actually received (not predicted from a config), the
@@ -22,7 +22,12 @@ Readings where the pages are silent:
   two (an empty segment stays empty); the valid rows come first and the
   padding rows after them carry ``src_of = -1`` and weight 0;
 * an expert-parallel share is ``[expert_begin, expert_begin + E_local)``;
-  slots routed elsewhere get ``row_of = -1``.
+  slots routed elsewhere get ``row_of = -1``;
+* a negative id is a padding slot (the buffer-check thread's validity
+  test); an id at or past the layer's expert count names no expert, is not
+  routed, and is reported (``expert_range_error``) — a corrupt router output
+  fails closed (the same page's review thread on graph capture: a
+  device-side check that records the failure).
 """
 
 import numpy as np
@@ -39,8 +44,12 @@ def next_pow2(n: int) -> int:
 
 
 def permute(topk_idx, topk_w, hidden_bits, num_local_experts: int,
-            expert_begin: int = 0, pad_pow2: bool = False):
+            expert_begin: int = 0, pad_pow2: bool = False, num_experts=None):
     """Group the routed (token, slot) pairs by expert.
+
+    ``num_experts`` (default: the end of the local range) is the layer's
+    expert count; ``expert_range_error`` in the result says whether any id
+    reached it.
 
     Returns a dict with ``counts [E_l]``, ``cu_seqlens [E_l+1]`` (int32),
     ``row_of [T*K]``, ``src_of [cap]`` (int32), ``w_perm [cap]`` (float32)
@@ -54,9 +63,11 @@ def permute(topk_idx, topk_w, hidden_bits, num_local_experts: int,
     H = hidden_bits.shape[1]
     El = num_local_experts
 
+    if num_experts is None:
+        num_experts = expert_begin + El
     flat = topk_idx.reshape(-1).astype(np.int64)
     local = flat - expert_begin
-    routed = (flat >= 0) & (local >= 0) & (local < El)
+    routed = (flat >= 0) & (flat < num_experts) & (local >= 0) & (local < El)
 
     counts = np.bincount(local[routed], minlength=El).astype(np.int64)
     sizes = np.array([next_pow2(int(c)) for c in counts], dtype=np.int64) if pad_pow2 else counts
@@ -84,4 +95,5 @@ def permute(topk_idx, topk_w, hidden_bits, num_local_experts: int,
         "src_of": src_of,
         "w_perm": w_perm,
         "x_perm": x_perm,
+        "expert_range_error": bool((flat >= num_experts).any()),
     }

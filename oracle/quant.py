@@ -7,8 +7,9 @@ Sources:
   PR summary and "How it works": the dispatch quantizer fake-quantizes the
   experts' input tokens before the FP8 staging; the combine quantizer
   fake-quantizes the router-weighted per-(token, slot) BF16 rows; serving
-  needs a calibrated (max) or constant global combine scale because each
-  rank re-quantizes rows from all expert ranks; "Testing": the calibrated
+  needs a calibrated (max) or constant global combine scale, since the rows
+  a rank quantizes were produced on every expert rank, not just its own;
+  "Testing": the calibrated
   amax equals the max of what the quantizer saw.
 * "[Kernel] DeepEP dispatch-combine kernel integration", review thread on
   the low-latency prepare/finalize: FP8 dispatch with a ``block_shape`` and

@@ -17,11 +17,16 @@ Sources:
 
 Readings where the pages are silent:
 * slot 0 holds the largest logit, slots follow in descending logit order
-  (the combine's "ascending slot" order presupposes some slot order);
+  (the combine adds slots in increasing slot index, which presupposes some
+  order of the slots);
 * ties between equal logits go to the lower expert index;
 * selection compares the float32 logits themselves (softmax is monotone, so
   this is the same ranking as by probability, and it is exact);
-* with ``renormalize=False`` the weights are the full softmax over all E.
+* with ``renormalize=False`` the weights are the full softmax over all E;
+* non-finite logits: a NaN ranks as -inf (below every number); a logit
+  equal to the row's largest chosen logit counts ``exp(0) = 1`` even when
+  both are infinite (the limit of the softmax; for finite logits the same
+  value), so a row whose chosen logits are all -inf gets ``1/k`` each.
 """
 
 import numpy as np
@@ -37,6 +42,7 @@ def route(logits, row_valid=None, k: int = 1, renormalize: bool = True):
     (renormalised) or over all E.
     """
     logits = np.asarray(logits, dtype=np.float32)
+    logits = np.where(np.isnan(logits), np.float32(-np.inf), logits)
     T, E = logits.shape
     if not (1 <= k <= E):
         raise ValueError("need 1 <= k <= E")
@@ -48,11 +54,16 @@ def route(logits, row_valid=None, k: int = 1, renormalize: bool = True):
     l64 = logits.astype(np.float64)
     sel_l = np.take_along_axis(l64, order, axis=1)
     lmax = sel_l[:, :1]
-    num = np.exp(sel_l - lmax)
+
+    def term(l):
+        with np.errstate(invalid="ignore"):
+            return np.where(l == lmax, 1.0, np.exp(l - lmax))
+
+    num = term(sel_l)
     if renormalize:
         den = num.sum(axis=1, keepdims=True)
     else:
-        den = np.exp(l64 - lmax).sum(axis=1, keepdims=True)
+        den = term(l64).sum(axis=1, keepdims=True)
     valid = np.ones(T, dtype=bool) if row_valid is None else np.asarray(row_valid).astype(bool)
     idx[valid] = order[valid]
     w[valid] = (num / den)[valid].astype(np.float32)

@@ -17,7 +17,7 @@ import oracle
 import workloads
 from combine_top_route_moe_amd import ops
 from oracle.numerics import bf16_bits_to_f32
-from tests.gpu_util import need_gpu, dev_bf16, host_bits, dev, host, rel_err, stacked_weights
+from tests.gpu_util import need_gpu, dev_bf16, host_bits, dev, host, stacked_weights, check_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -141,4 +141,4 @@ def test_ffn_fp8_weights_equal_bf16_on_dequantized(H, I, T, hot, pow2):
             continue
         x = oracle.bf16_bits_to_f64(ref["x_perm"][r0:r0 + n])
         want = oracle.expert_ffn(x, d13[e], d2[e]) * ref["w_perm"][r0:r0 + n, None].astype(np.float64)
-        assert rel_err(bf16_bits_to_f32(host_bits(y8[r0:r0 + n])), want) <= FFN_TOL, e
+        check_rows(bf16_bits_to_f32(host_bits(y8[r0:r0 + n])), want, FFN_TOL, what=f"expert {e}")

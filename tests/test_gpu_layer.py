@@ -1,10 +1,23 @@
 """Whole-layer parity (GPU through the C ABI vs the oracle), graph capture
 and determinism.
 
-Exact: top-k ids, permute maps.  Layer output: Frobenius relative error
-<= 2e-2 over valid tokens; padding tokens exactly +0 without a shared
-expert.  Full-size deepseek and prefill compare sampled tokens, which the
-oracle evaluates one by one (their rows need only the experts they hit).
+Exact: top-k ids, permute maps.  Layer output over valid tokens: the
+Frobenius relative error, every token's relative error and every element
+(relative to its token's largest reference magnitude) within 2e-2; padding
+tokens exactly +0 without a shared expert.
+
+With the FP8 combine-row quantizer the end-to-end element bound does not
+hold by construction: a bf16 row that differs from the oracle's in its last
+bit can round to the neighbouring E4M3 code, one step of 6-12 % of that
+value (a CPU simulation with 3e-3 noise on the rows gives ~2 % worst token
+error and ~8 % of the row maximum per element).  Those layers are checked
+in pieces instead, each to the strict bar: the GPU's routed rows before
+quantization (and its shared expert's rows) against the oracle's rows per
+row and element; the quantizer and the combine bit for bit on the GPU's own
+rows and scale; and the end-to-end Frobenius error.
+
+Full-size deepseek and prefill compare sampled tokens and sampled experts'
+rows, which the oracle evaluates one at a time.
 """
 
 import numpy as np
@@ -15,7 +28,8 @@ import oracle
 import workloads
 from combine_top_route_moe_amd import MoELayer, ops
 from oracle.numerics import bf16_bits_to_f64
-from tests.gpu_util import need_gpu, dev_bf16, host_bits, dev, host, rel_err
+from tests.gpu_util import (need_gpu, dev_bf16, host_bits, dev, host, rel_err, check_rows,
+                            w8a8_intermediate, check_fp8_intermediate)
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -65,7 +79,93 @@ def _gpu_layer(cfg, W, logits, hidden, valid, scale=None, expert_begin=0, num_lo
     return layer
 
 
-def _check_layer(cfg, layer, ref, valid):
+def _check_w8a8_layer(cfg, layer, ref, valid, hd, W):
+    """The FP8-path layer: routing and permute maps exact; every expert's
+    and the shared expert's rows in pieces; the combine (with its QDQ) bit
+    for bit on the GPU's own rows and scale; the output's norm end to end."""
+    np.testing.assert_array_equal(host(layer.topk_idx), ref["topk_idx"])
+    np.testing.assert_allclose(host(layer.topk_w), ref["topk_w"], rtol=1e-6)
+    p = ref["perm"]
+    for key in ("counts", "cu_seqlens", "row_of"):
+        np.testing.assert_array_equal(host(getattr(layer.perm, key)), p[key])
+    experts = range(layer.expert_begin, layer.expert_begin + layer.El)
+    _check_w8a8_rows(cfg, layer, hd, W.host, experts, W.shared_host, np.arange(cfg.T))
+    src = host(layer.perm.src_of)
+    rows = host_bits(layer.y_perm)
+    if cfg.combine_qdq:
+        rows = oracle.fake_quant_per_tensor(rows, np.float32(host(layer.combine_scale)[0]),
+                                            row_mask=src >= 0)
+    shared = host_bits(layer.shared_out) if cfg.shared_I else None
+    np.testing.assert_array_equal(host_bits(layer.out),
+                                  oracle.combine(rows, host(layer.perm.row_of), cfg.T, cfg.K, shared))
+    tok = np.ones(cfg.T, bool) if valid is None else valid.astype(bool)
+    err = rel_err(bf16_bits_to_f64(host_bits(layer.out))[tok], bf16_bits_to_f64(ref["out"])[tok])
+    assert err <= TOL, err
+    return err
+
+
+def _check_qdq_pieces(cfg, layer, ref):
+    """The FP8 combine-row layer in pieces: pre-quantization routed rows and
+    shared rows against the oracle per row and element; then the quantizer
+    and the ordered combine bit for bit on the GPU's own rows and scale."""
+    src = host(layer.perm.src_of)
+    routed = np.nonzero(src >= 0)[0]
+    y_gpu = host_bits(layer.y_perm)
+    check_rows(bf16_bits_to_f64(y_gpu[routed]), ref["y"][routed], TOL, what="routed rows")
+    shared = None
+    if cfg.shared_I:
+        shared = host_bits(layer.shared_out)
+        check_rows(bf16_bits_to_f64(shared), bf16_bits_to_f64(ref["shared"]), TOL,
+                   what="shared expert rows")
+    s = np.float32(host(layer.combine_scale)[0])
+    q = oracle.fake_quant_per_tensor(y_gpu, s, row_mask=src >= 0)
+    np.testing.assert_array_equal(host_bits(layer.out),
+                                  oracle.combine(q, host(layer.perm.row_of), cfg.T, cfg.K, shared))
+
+
+def _check_w8a8_rows(cfg, layer, hd, host_w, experts, shared_host=None, shared_tokens=None):
+    """The FP8 path's rows in pieces (see the module notes on one flipped
+    intermediate code): for each expert in ``experts`` (global ids), its
+    intermediate codes against the oracle's (rare neighbouring-code flips
+    only), its down projection on the GPU's own intermediate per row and
+    element, and its rows end to end in norm; the same for the shared
+    expert's rows of ``shared_tokens``."""
+    K = cfg.K
+    counts, cu = host(layer.perm.counts), host(layer.perm.cu_seqlens)
+    src, wp = host(layer.perm.src_of), host(layer.perm.w_perm)
+    qa_g, sa_g = w8a8_intermediate(layer.ffn_ws, layer.capacity, layer.El, cfg.I, counts, cu)
+    y = layer.y_perm
+    for e in experts:
+        le = e - layer.expert_begin
+        n, r0 = int(counts[le]), int(cu[le])
+        if n == 0:
+            continue
+        qx, sx = oracle.quantize_rows_fp8(hd[src[r0:r0 + n] // K])
+        st = oracle.expert_ffn_w8a8_steps(qx, sx, *host_w[e])
+        rs = wp[r0:r0 + n, None].astype(np.float64)
+        check_fp8_intermediate(qa_g[r0:r0 + n], sa_g[r0:r0 + n], st["qa"], st["sa"], f"expert {e}")
+        got = bf16_bits_to_f64(host_bits(y[r0:r0 + n]))
+        own = oracle.block_scaled_matmul(qa_g[r0:r0 + n], sa_g[r0:r0 + n], *st["w2q"]) * rs
+        check_rows(got, own, TOL, what=f"expert {e} ({n} rows), down on the GPU's intermediate")
+        assert rel_err(got, st["y"] * rs) <= TOL, e
+    if shared_host is not None:
+        T, Is = cfg.T, cfg.shared_I
+        qa_s, sa_s = w8a8_intermediate(layer.shared_ws, T, 1, Is, [T], [0, T])
+        toks = np.asarray(shared_tokens)
+        qx, sx = oracle.quantize_rows_fp8(hd[toks])
+        st = oracle.expert_ffn_w8a8_steps(qx, sx, *shared_host)
+        check_fp8_intermediate(qa_s[toks], sa_s[toks], st["qa"], st["sa"], "shared expert")
+        got = bf16_bits_to_f64(host_bits(layer.shared_out[torch.from_numpy(toks).cuda()]))
+        own = oracle.block_scaled_matmul(qa_s[toks], sa_s[toks], *st["w2q"])
+        check_rows(got, own, TOL, what="shared expert, down on the GPU's intermediate")
+        assert rel_err(got, st["y"]) <= TOL
+
+
+def _check_layer(cfg, layer, ref, valid, hd=None, W=None):
+    """``hd`` and ``W`` (the host inputs and weights) are needed for the FP8
+    path, whose rows are checked in pieces."""
+    if layer.w8a8:
+        return _check_w8a8_layer(cfg, layer, ref, valid, hd, W)
     np.testing.assert_array_equal(host(layer.topk_idx), ref["topk_idx"])
     np.testing.assert_allclose(host(layer.topk_w), ref["topk_w"], rtol=1e-6)
     p = ref["perm"]
@@ -75,8 +175,15 @@ def _check_layer(cfg, layer, ref, valid):
     out = bf16_bits_to_f64(host_bits(layer.out))
     want = bf16_bits_to_f64(ref["out"])
     tok = np.ones(cfg.T, bool) if valid is None else valid.astype(bool)
-    err = rel_err(out[tok], want[tok])
-    assert err <= TOL, err
+    if cfg.combine_qdq:
+        _check_qdq_pieces(cfg, layer, ref)
+        err = rel_err(out[tok], want[tok])
+        assert err <= TOL, err
+    else:
+        st = check_rows(out[tok], want[tok], TOL, what=f"{cfg.name} layer output")
+        err = st["frob"]
+        print(f"{cfg.name}: worst token rel err {st['worst_row']:.3e}, "
+              f"worst element / token max {st['worst_elem']:.3e}")
     if not cfg.shared_I and valid is not None:
         assert np.all(host_bits(layer.out)[~tok] == 0)
     return err
@@ -122,9 +229,12 @@ def test_layer_tiny_variants(variant):
     layer = _gpu_layer(cfg, W, lg, hd, vd, scale=ref["combine_scale"])
     _check_layer(cfg, layer, ref, vd)
     if cfg.combine_qdq:
+        # the GPU's own calibration: exactly fl32(max|its routed rows| / 448),
+        # within the FFN tolerance of the oracle's, and the layer in pieces
         own = _gpu_layer(cfg, W, lg, hd, vd)
-        s_gpu = float(host(own.combine_scale)[0])
+        s_gpu = float(_gpu_calibrated_scale(own))
         assert abs(s_gpu - float(ref["combine_scale"])) <= TOL * float(ref["combine_scale"])
+        _check_qdq_pieces(cfg, own, ref)
 
 
 @pytest.mark.parametrize("variant", ["plain", "everything"])
@@ -312,7 +422,7 @@ def test_layer_fp8_gemm(variant):
     e, m = (c >> 3) & 0xF, c & 7
     mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7))
     np.testing.assert_array_equal(np.where(c & 0x80, -mag, mag), q_want)
-    err = _check_layer(cfg, layer, ref, vd)
+    err = _check_layer(cfg, layer, ref, vd, hd, W)
     print(f"{variant}: FP8-path layer rel err {err:.3e}")
 
 
@@ -332,7 +442,7 @@ def test_layer_fp8_modes_expert_parallel_share(fp8):
     ref = oracle.moe_layer(lg, hd, lambda e: W.host[e], cfg.K, None, expert_begin=3,
                            num_local_experts=4, fp8_weights=fp8 is True,
                            fp8_gemm=fp8 == "w8a8")
-    _check_layer(cfg, layer, ref, None)
+    _check_layer(cfg, layer, ref, None, hd, W)
 
 
 @pytest.mark.parametrize("fp8", [True, "w8a8"])
@@ -368,14 +478,98 @@ def test_layer_fp8_modes_graph_replay_matches_eager(fp8):
     assert layer.dev_error.item() == 0
 
 
-def _sampled(cfg, n_tok, scale=None, seed=0):
+def _gpu_calibrated_scale(layer):
+    """The GPU's own calibrated combine scale must be fl32(max|row| / 448)
+    over exactly its routed rows: the max (exact in any order) is taken here
+    on the device over the rows src_of marks, the division in numpy."""
+    routed = torch.nonzero(layer.perm.src_of >= 0).squeeze(1)
+    amax = np.float32(layer.y_perm[routed].float().abs().max().item())
+    s = np.float32(host(layer.combine_scale)[0])
+    assert s == np.float32(amax / np.float32(448.0)), (s, amax)
+    return s
+
+
+def _expert_rows(cfg, layer, idx, w, x_rows, toks, weights, ffn):
+    """Oracle rows (float64, router weight applied) of every slot of the
+    sampled tokens, evaluated expert by expert: {(t, k): row}."""
+    by_e = {}
+    for t in toks:
+        for k in range(cfg.K):
+            if idx[t, k] >= 0:
+                by_e.setdefault(int(idx[t, k]), []).append((int(t), k))
+    out = {}
+    for e, slots in by_e.items():
+        ts = np.array([t for t, _ in slots])
+        y = ffn(x_rows(ts), *weights(e))
+        for (t, k), row in zip(slots, y):
+            out[(t, k)] = row * float(w[t, k])
+    return out
+
+
+def _check_sampled_tokens(cfg, layer, idx, oracle_rows, toks, shared_ref, scale):
+    """Sampled tokens of a full-size layer: without combine QDQ the output
+    against the oracle's per token and element; with it, the pieces (the
+    GPU's rows before QDQ and its shared rows per row and element, the QDQ
+    and combine bit for bit on the GPU's rows) and the end-to-end norm."""
+    row_of = host(layer.perm.row_of).reshape(cfg.T, cfg.K)
+    got = bf16_bits_to_f64(host_bits(layer.out)[toks])
+    want = np.zeros_like(got)
+    gpu_rows, ref_rows = [], []
+    tidx = torch.from_numpy(np.asarray(toks)).cuda()
+    shared_gpu = host_bits(layer.shared_out[tidx]) if cfg.shared_I else None
+    for j, t in enumerate(toks):
+        ks = [k for k in range(cfg.K) if idx[t, k] >= 0]
+        rows = np.array([oracle.f32_to_bf16_bits(oracle_rows[(t, k)].astype(np.float32))
+                         for k in ks], np.uint16).reshape(-1, cfg.H)
+        if cfg.combine_qdq and len(rows):
+            rows = oracle.fake_quant_per_tensor(rows, scale)
+        sh = None if shared_ref is None else shared_ref[j][None]
+        if len(rows) == 0:
+            rows = np.zeros((1, cfg.H), np.uint16)
+        ro = np.array(list(range(len(ks))) + [-1] * (cfg.K - len(ks)), np.int32)
+        want[j] = bf16_bits_to_f64(oracle.combine(rows, ro, 1, cfg.K, sh))[0]
+        for k in ks:
+            gpu_rows.append(row_of[t, k])
+            ref_rows.append(oracle_rows[(t, k)])
+    if not cfg.combine_qdq:
+        st = check_rows(got, want, TOL, what=f"{cfg.name} sampled tokens")
+        return st["frob"]
+    # pieces: rows before QDQ, shared rows, then QDQ + combine bit for bit
+    rsel = torch.from_numpy(np.array(gpu_rows, np.int64)).cuda()
+    check_rows(bf16_bits_to_f64(host_bits(layer.y_perm[rsel])), np.array(ref_rows), TOL,
+               what=f"{cfg.name} sampled routed rows")
+    if cfg.shared_I:
+        check_rows(bf16_bits_to_f64(shared_gpu), bf16_bits_to_f64(np.array(shared_ref)), TOL,
+                   what=f"{cfg.name} sampled shared rows")
+    _check_combine_on_gpu_rows(cfg, layer, toks, scale)
+    err = rel_err(got, want)
+    assert err <= TOL, err
+    return err
+
+
+def _check_combine_on_gpu_rows(cfg, layer, toks, scale):
+    """out[t] == combine(QDQ(the GPU's own rows of t)) bit for bit."""
+    row_of = host(layer.perm.row_of).reshape(cfg.T, cfg.K)[toks]
+    rsel = np.where(row_of >= 0, row_of, 0).reshape(-1)
+    rows = host_bits(layer.y_perm[torch.from_numpy(rsel.astype(np.int64)).cuda()])
+    local_of = np.where(row_of.reshape(-1) >= 0, np.arange(len(rsel)), -1).astype(np.int32)
+    if cfg.combine_qdq:
+        rows = oracle.fake_quant_per_tensor(rows, scale, row_mask=local_of >= 0)
+    tidx = torch.from_numpy(np.asarray(toks)).cuda()
+    shared = host_bits(layer.shared_out[tidx]) if cfg.shared_I else None
+    np.testing.assert_array_equal(host_bits(layer.out[tidx]),
+                                  oracle.combine(rows, local_of, len(toks), cfg.K, shared))
+
+
+def _sampled(cfg, n_tok, seed=0):
     rng = np.random.default_rng(seed)
     lg, hd, vd = workloads.logits(cfg), workloads.hidden(cfg), workloads.row_valid(cfg)
     idx, w = oracle.route(lg, vd, cfg.K)
     toks = np.sort(rng.choice(cfg.T, n_tok, replace=False))
     keep = set(int(e) for e in idx[toks].reshape(-1) if e >= 0)
     W = Weights(cfg, keep=keep)
-    layer = _gpu_layer(cfg, W, lg, hd, vd, scale=scale)
+    layer = _gpu_layer(cfg, W, lg, hd, vd)            # the GPU calibrates its own scale
+    scale = _gpu_calibrated_scale(layer) if cfg.combine_qdq else None
     # exact stages over the whole batch
     np.testing.assert_array_equal(host(layer.topk_idx), idx)
     hq = hd
@@ -395,45 +589,105 @@ def _sampled(cfg, n_tok, scale=None, seed=0):
     perm = oracle.permute(idx, w, hq, cfg.E, 0, cfg.pad_pow2)
     for key in ("counts", "cu_seqlens", "row_of"):
         np.testing.assert_array_equal(host(getattr(layer.perm, key)), perm[key])
-    # the sampled tokens, one by one
-    got = bf16_bits_to_f64(host_bits(layer.out)[toks])
-    want = np.zeros_like(got)
     x = oracle.bf16_bits_to_f64(hq)
-    for j, t in enumerate(toks):
-        rows = []
-        for k in range(cfg.K):
-            e = idx[t, k]
-            if e < 0:
-                continue
-            y = oracle.expert_ffn(x[t:t + 1], *W.host[int(e)])[0] * float(w[t, k])
-            rows.append(oracle.f32_to_bf16_bits(y.astype(np.float32)))
-        rows = np.array(rows, np.uint16).reshape(-1, cfg.H)
-        if cfg.combine_qdq:
-            rows = oracle.fake_quant_per_tensor(rows, np.float32(scale))
-        shared = None
-        if cfg.shared_I:
-            s = oracle.expert_ffn(oracle.bf16_bits_to_f64(hd[t:t + 1]), *W.shared_host)[0]
-            shared = oracle.f32_to_bf16_bits(s.astype(np.float32))[None]
-        n = len(rows)
-        if n == 0:
-            rows = np.zeros((1, cfg.H), np.uint16)
-        ro = np.array(list(range(n)) + [-1] * (cfg.K - n), np.int32)
-        want[j] = bf16_bits_to_f64(oracle.combine(rows, ro, 1, cfg.K, shared))[0]
-    err = rel_err(got, want)
-    assert err <= TOL, err
+    orows = _expert_rows(cfg, layer, idx, w, lambda ts: x[ts], toks, lambda e: W.host[e],
+                         oracle.expert_ffn)
+    shared_ref = None
+    if cfg.shared_I:
+        s = oracle.expert_ffn(oracle.bf16_bits_to_f64(hd[toks]), *W.shared_host)
+        shared_ref = oracle.f32_to_bf16_bits(s.astype(np.float32))
+    err = _check_sampled_tokens(cfg, layer, idx, orows, toks, shared_ref, scale)
+    if cfg.combine_qdq:                              # and a wider sample of the exact combine
+        more = np.sort(rng.choice(cfg.T, 256, replace=False))
+        _check_combine_on_gpu_rows(cfg, layer, more, scale)
     return err
 
 
 def test_layer_prefill_full_size_sampled():
-    err = _sampled(workloads.CONFIGS["prefill"], 24)
+    err = _sampled(workloads.CONFIGS["prefill"], 64)
     print(f"prefill sampled rel err {err:.3e}")
 
 
 def test_layer_deepseek_full_size_sampled():
-    # a constant per-tensor combine scale (the page allows calibrated or
-    # constant); 2^-8 puts the largest routed rows near the top of the e4m3 range
-    err = _sampled(workloads.CONFIGS["deepseek"], 12, scale=2.0 ** -8)
+    """Full-size deepseek with the combine-row scale the GPU calibrates
+    itself (checked bit for bit against its own rows' amax), as the bench
+    runs it."""
+    err = _sampled(workloads.CONFIGS["deepseek"], 32)
     print(f"deepseek sampled rel err {err:.3e}")
+
+
+@pytest.mark.parametrize("name", ["deepseek", "prefill"])
+@pytest.mark.parametrize("fp8", [True, "w8a8"])
+def test_layer_fp8_modes_full_size(name, fp8):
+    """FP8 expert weights and the real FP8 path at full deepseek and prefill
+    shape: routing and permute maps exact; every routed row of three
+    experts (the smallest, a middle and the largest segment) against the
+    oracle's matching mode per row and element; the shared expert's rows of
+    sampled tokens the same way; the combine (with the GPU-calibrated FP8
+    combine scale on deepseek, checked against its own rows) bit for bit on
+    the GPU's rows for 256 sampled tokens."""
+    cfg = workloads.CONFIGS[name]
+    rng = np.random.default_rng(7)
+    lg, hd, vd = workloads.logits(cfg), workloads.hidden(cfg), workloads.row_valid(cfg)
+    idx, w = oracle.route(lg, vd, cfg.K)
+    counts = np.bincount(idx[idx >= 0], minlength=cfg.E)
+    order = np.argsort(counts, kind="stable")
+    experts = [int(order[0]), int(order[cfg.E // 2]), int(order[-1])]
+    W = Weights(cfg, keep=set(experts))
+    layer = MoELayer(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, "cuda", shared_I=cfg.shared_I,
+                     dispatch_block=cfg.dispatch_block, combine_qdq=cfg.combine_qdq,
+                     pad_pow2=cfg.pad_pow2)
+    layer.set_weights(W.w13, W.w2, *(W.shared or (None, None)), fp8=fp8)
+    lgd, hdd = dev(lg), dev_bf16(hd)
+    vdd = None if vd is None else dev(vd)
+    if cfg.combine_qdq:
+        layer.calibrate_combine_scale(lgd, hdd, vdd)
+    layer.forward(lgd, hdd, vdd)
+    torch.cuda.synchronize()
+    assert layer.dev_error.item() == 0
+    scale = _gpu_calibrated_scale(layer) if cfg.combine_qdq else None
+    np.testing.assert_array_equal(host(layer.topk_idx), idx)
+    valid_tok = (idx >= 0).any(axis=1)
+    perm = oracle.permute(idx, w, hd, cfg.E, 0, cfg.pad_pow2)
+    for key in ("counts", "cu_seqlens", "row_of"):
+        np.testing.assert_array_equal(host(getattr(layer.perm, key)), perm[key])
+    deq = lambda m: oracle.quantize_weight_blocks(m)[2]  # noqa: E731
+    if fp8 == "w8a8":
+        def rows_of(ts):
+            return oracle.quantize_rows_fp8(hd[ts])
+
+        def ffn(ts, w13, w2):
+            qx, sx = rows_of(ts)
+            return oracle.expert_ffn_w8a8(qx, sx, w13, w2)
+    else:
+        hq = hd
+        if cfg.dispatch_block:
+            hq, _ = oracle.fake_quant_block(hd, cfg.dispatch_block, row_mask=valid_tok)
+
+        def ffn(ts, w13, w2):
+            return oracle.expert_ffn(oracle.bf16_bits_to_f64(hq[ts]), deq(w13), deq(w2))
+    toks = np.sort(rng.choice(np.nonzero(valid_tok)[0], 256, replace=False))
+    if fp8 == "w8a8":
+        _check_w8a8_rows(cfg, layer, hd, W.host, experts, W.shared_host, toks[:32])
+        _check_combine_on_gpu_rows(cfg, layer, toks, scale)
+        return
+    y = layer.y_perm
+    for e in experts:
+        r0, n = int(perm["cu_seqlens"][e]), int(perm["counts"][e])
+        src = perm["src_of"][r0:r0 + n]
+        want = ffn(src // cfg.K, *W.host[e]) * perm["w_perm"][r0:r0 + n, None].astype(np.float64)
+        st = check_rows(bf16_bits_to_f64(host_bits(y[r0:r0 + n])), want, TOL,
+                        what=f"{name} {fp8} expert {e} ({n} rows)")
+        print(f"{name} fp8={fp8} expert {e} ({n} rows): worst row {st['worst_row']:.3e}")
+    if cfg.shared_I:
+        sample = toks[:32]
+        s13, s2 = W.shared_host
+        # the shared expert reads the layer input itself (its codes on the FP8 path)
+        want = (oracle.expert_ffn_w8a8(*rows_of(sample), s13, s2) if fp8 == "w8a8"
+                else oracle.expert_ffn(oracle.bf16_bits_to_f64(hd[sample]), deq(s13), deq(s2)))
+        got = host_bits(layer.shared_out[torch.from_numpy(sample).cuda()])
+        check_rows(bf16_bits_to_f64(got), want, TOL, what=f"{name} {fp8} shared rows")
+    _check_combine_on_gpu_rows(cfg, layer, toks, scale)
 
 
 @pytest.mark.parametrize("variant", ["shared_combine_qdq", "dispatch_fp8_pow2"])

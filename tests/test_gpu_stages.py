@@ -2,8 +2,9 @@
 
 Bit-exact: top-k indices, permute counts / cu_seqlens / maps / rows, FP8
 fake-quant outputs and scales, combine outputs given identical rows.
-Router weights: rtol 1e-6.  Grouped FFN: Frobenius relative error <= 2e-2
-against the float64 oracle over the valid rows.
+Router weights: rtol 1e-6.  Grouped FFN, per expert against the float64
+oracle: Frobenius relative error, every row's relative error and every
+element (relative to its row's largest reference magnitude) within 2e-2.
 """
 
 import json
@@ -17,7 +18,8 @@ import oracle
 import workloads
 from combine_top_route_moe_amd import ops
 from oracle.numerics import bf16_bits_to_f32, f32_to_bf16_bits
-from tests.gpu_util import need_gpu, dev_bf16, host_bits, dev, host, rel_err, stacked_weights
+from tests.gpu_util import (need_gpu, dev_bf16, host_bits, dev, host, rel_err, stacked_weights,
+                            check_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,6 +71,29 @@ def test_route_signed_zero_ties(E):
     logits[hot] = rng.choice([-1.0, 0.5, 1.0], hot.sum()).astype(np.float32)
     _route_case(logits, K)
     _route_case(logits, K, renorm=False)
+
+
+@pytest.mark.parametrize("E", [8, 64, 256])
+def test_route_nan_and_infinite_logits(E):
+    """NaN logits rank as -inf (never hiding a real expert, every id in
+    range) and equal infinite logits weigh as equals, as the oracle defines:
+    rows with scattered NaNs, all-NaN rows, rows with fewer than K finite
+    logits and rows with several +inf, through the rank kernel (E <= 64) and
+    the argmax kernel (E > 64)."""
+    rng = np.random.default_rng(E + 1)
+    T, K = 48, 8
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[rng.random((T, E)) < 0.2] = np.nan
+    logits[3] = np.nan
+    logits[4] = -np.inf
+    logits[5, :] = np.nan
+    logits[5, [1, 6]] = [0.5, -2.0]                  # two finite logits, K = 8
+    logits[6, [0, 3, 7]] = np.inf
+    logits[7, [2, 5]] = [-np.inf, np.nan]
+    for renorm in (True, False):
+        _route_case(logits, K, renorm=renorm)
+    idx, _ = ops.moe_route(dev(logits), K)
+    assert host(idx).min() >= 0 and host(idx).max() < E
 
 
 def test_route_rejects_bad_args():
@@ -229,20 +254,29 @@ def test_fake_quant_row_skip_inplace_and_amax():
     assert host(amax)[0] == oracle.calibrate_amax(x)
     sc = ops.moe_scale_from_amax(amax)
     assert host(sc)[0] == np.float32(oracle.calibrate_amax(x) / np.float32(448))
+    # the NVFP4 tensor scale, also on the device: the oracle's closed form
+    g = ops.moe_scale_from_amax(amax, mode=ops.MOE_FQ_NVFP4)
+    assert host(g)[0] == oracle.nvfp4_tensor_scale(oracle.calibrate_amax(x))
+    with pytest.raises(RuntimeError):
+        ops.moe_scale_from_amax(amax, mode=ops.MOE_FQ_BLOCK)
 
 
 # -------------------------------------------------------------------- permute
 
-def _permute_case(idx, w, hid, El, begin=0, pow2=False, capacity=None, check_rows=None):
+def _permute_case(idx, w, hid, El, begin=0, pow2=False, capacity=None, sample_rows=None,
+                  num_experts=None):
+    """``num_experts``: the layer's expert count (ids past it are errors);
+    by default the end of the local range."""
     T, K = idx.shape
-    ref = oracle.permute(idx, w, hid, El, begin, pow2)
+    ref = oracle.permute(idx, w, hid, El, begin, pow2, num_experts=num_experts)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     cap = ops.moe_permute_capacity(T, K, El, pow2) if capacity is None else capacity
     out = ops.alloc_permuted(T, K, hid.shape[1], El, cap, "cuda")
     for t in (out.counts, out.cu_seqlens, out.row_of, out.src_of):
         t.fill_(12345)                               # stale contents must not leak
     out.w_perm.fill_(7.0)
-    p = ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), El, begin, pow2, cap, out, dev_error=err)
+    p = ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), El, begin, pow2, cap, out, dev_error=err,
+                        num_experts=num_experts)
     assert host(err)[0] == 0
     np.testing.assert_array_equal(host(p.counts), ref["counts"])
     np.testing.assert_array_equal(host(p.cu_seqlens), ref["cu_seqlens"])
@@ -252,8 +286,8 @@ def _permute_case(idx, w, hid, El, begin=0, pow2=False, capacity=None, check_row
     np.testing.assert_array_equal(host(p.w_perm)[:used], ref["w_perm"])
     assert np.all(host(p.src_of)[used:] == -1) and np.all(host(p.w_perm)[used:] == 0)
     valid = np.nonzero(ref["src_of"] >= 0)[0]
-    if check_rows is not None and len(valid) > check_rows:
-        valid = np.sort(np.random.default_rng(0).choice(valid, check_rows, replace=False))
+    if sample_rows is not None and len(valid) > sample_rows:
+        valid = np.sort(np.random.default_rng(0).choice(valid, sample_rows, replace=False))
     got = host_bits(p.x_perm[torch.from_numpy(valid).cuda()]) if len(valid) else np.zeros((0, hid.shape[1]), np.uint16)
     np.testing.assert_array_equal(got, ref["x_perm"][valid])
     return ref
@@ -265,7 +299,7 @@ def test_permute_workloads(name):
     idx, w = oracle.route(workloads.logits(cfg), workloads.row_valid(cfg), cfg.K)
     hid = workloads.hidden(cfg)
     ref = _permute_case(idx, w, hid, cfg.E, 0, cfg.pad_pow2,
-                        check_rows=None if cfg.T <= 512 else 4096)
+                        sample_rows=None if cfg.T <= 512 else 4096)
     if name == "prefill":
         assert int(ref["cu_seqlens"][-1]) == 131072
 
@@ -286,7 +320,7 @@ def test_permute_edge_cases(seed):
     for pow2 in (False, True):
         _permute_case(idx, w, hid, E, 0, pow2)
     if E > 2:                                         # an expert-parallel share
-        _permute_case(idx, w, hid, E // 2, E // 4, True)
+        _permute_case(idx, w, hid, E // 2, E // 4, True, num_experts=E)
 
 
 @pytest.mark.parametrize("T,K,E,H,El,begin", [
@@ -310,7 +344,7 @@ def test_permute_launch_path_boundaries(T, K, E, H, El, begin):
     w = rng.random((T, K)).astype(np.float32)
     hid = rng.integers(0, 2 ** 16, size=(T, H), dtype=np.uint64).astype(np.uint16)
     for pow2 in (False, True):
-        _permute_case(idx, w, hid, El, begin, pow2)
+        _permute_case(idx, w, hid, El, begin, pow2, num_experts=E)
 
 
 @pytest.mark.parametrize("T,K,E,H,pow2,begin_el", [
@@ -338,7 +372,7 @@ def test_permute_dispatch_fp8_equals_quantize_then_permute(T, K, E, H, pow2, beg
     cap = ops.moe_permute_capacity(T, K, El, pow2)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     p = ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), El, begin, pow2, cap, dev_error=err,
-                        dispatch_fp8=True)
+                        dispatch_fp8=True, num_experts=E)
     assert host(err)[0] == 0
     np.testing.assert_array_equal(host(p.row_of), ref["row_of"])
     rows = np.nonzero(ref["src_of"] >= 0)[0]
@@ -370,6 +404,41 @@ def test_empty_batch_every_stage():
     assert tuple(out.shape) == (0, H)
     torch.cuda.synchronize()
     assert host(err)[0] == 0
+
+
+@pytest.mark.parametrize("T,K,E,El,begin", [
+    (64, 2, 8, 8, 0),          # one launch
+    (300, 8, 64, 32, 16),      # one launch, an expert-parallel share
+    (700, 8, 64, 64, 0),       # the multi-launch path, scan fused into the scatter
+    (4096, 8, 256, 256, 0),    # the multi-launch path with the scan kernel
+])
+def test_permute_expert_id_out_of_range_fails_closed(T, K, E, El, begin):
+    """Router ids at or past the layer's expert count raise
+    MOE_DEVERR_EXPERT_RANGE and are not routed; every map and row still
+    matches the oracle (which drops them the same way); ids of other ranks'
+    experts and negative ids of any value are not errors."""
+    rng = np.random.default_rng(T + E)
+    idx = rng.integers(-3, E, size=(T, K)).astype(np.int32)
+    w = rng.random((T, K)).astype(np.float32)
+    hid = rng.integers(0, 2 ** 16, size=(T, 128), dtype=np.uint64).astype(np.uint16)
+    for bad in (False, True):
+        if bad:
+            idx[rng.integers(0, T, 3), rng.integers(0, K, 3)] = [E, E + 7, 2 ** 30]
+        ref = oracle.permute(idx, w, hid, El, begin, False, num_experts=E)
+        assert ref["expert_range_error"] == bad
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        p = ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), El, begin, False, dev_error=err,
+                            num_experts=E)
+        torch.cuda.synchronize()
+        assert host(err)[0] == (ops.MOE_DEVERR_EXPERT_RANGE if bad else 0)
+        for key in ("counts", "cu_seqlens", "row_of"):
+            np.testing.assert_array_equal(host(getattr(p, key)), ref[key])
+        used = int(ref["cu_seqlens"][-1])
+        np.testing.assert_array_equal(host(p.src_of)[:used], ref["src_of"])
+        rows = np.nonzero(ref["src_of"] >= 0)[0]
+        np.testing.assert_array_equal(host_bits(p.x_perm)[rows], ref["x_perm"][rows])
+    with pytest.raises(RuntimeError):                 # a share past the layer's experts
+        ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), El, E - El + 1, num_experts=E)
 
 
 def test_permute_capacity_overflow_is_flagged_not_written():
@@ -559,9 +628,8 @@ def _ffn_case(cfg, idx, w, hid, host_w, w13, w2, pow2=False, experts=None, tol=F
         x = oracle.bf16_bits_to_f64(ref["x_perm"][r0:r0 + n])
         want = oracle.expert_ffn(x, *host_w[e]) * ref["w_perm"][r0:r0 + n, None].astype(np.float64)
         got = bf16_bits_to_f32(host_bits(y[r0:r0 + n]))
-        err_e = rel_err(got, want)
-        worst = max(worst, err_e)
-        assert err_e <= tol, (e, n, err_e)
+        st = check_rows(got, want, tol, what=f"expert {e} ({n} rows)")
+        worst = max(worst, st["worst_row"])
         seg_end = int(cu[e + 1])
         if seg_end > r0 + n:                          # pow2 padding rows are never written
             assert np.all(host_bits(y[r0 + n:seg_end]) == 0)
@@ -587,7 +655,7 @@ def test_ffn_workloads(name):
     hid = workloads.hidden(cfg)
     w13, w2, host_w = stacked_weights(cfg)
     worst = _ffn_case(cfg, idx, w, hid, host_w, w13, w2)
-    print(f"{name}: worst per-expert rel err {worst:.3e}")
+    print(f"{name}: worst row rel err {worst:.3e}")
 
 
 def test_ffn_one_big_segment_many_tiles():
@@ -662,7 +730,7 @@ def test_ffn_packed_weights(H, I, T):
             continue
         x = oracle.bf16_bits_to_f64(ref["x_perm"][r0:r0 + n])
         want_y = oracle.expert_ffn(x, *host_w[e]) * ref["w_perm"][r0:r0 + n, None].astype(np.float64)
-        assert rel_err(bf16_bits_to_f32(host_bits(y[r0:r0 + n])), want_y) <= FFN_TOL, e
+        check_rows(bf16_bits_to_f32(host_bits(y[r0:r0 + n])), want_y, FFN_TOL, what=f"expert {e}")
     # and it agrees closely with the row-major kernel (different summation order)
     y2 = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13, w2, p.w_perm)
     used = int(ref["cu_seqlens"][-1])

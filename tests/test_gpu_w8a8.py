@@ -6,10 +6,17 @@
 * moe_pack_ffn_weights_fp8 with the K=128 layout: codes and scales
   bit-exact against oracle.quantize_weight_blocks through the documented
   order.
-* moe_grouped_ffn_w8a8 against oracle.grouped_ffn_w8a8 (float64, the same
-  quantization of rows, weights and intermediate): Frobenius relative error
-  <= 2e-2 per expert; pow2 padding rows never written; GATE_UP then DOWN
-  gives the same bits as ALL.
+* moe_grouped_ffn_w8a8 against the oracle's FP8 FFN (float64, the same
+  quantization of rows, weights and intermediate), in two steps, because one
+  intermediate code that lands on the neighbouring E4M3 value (when the GPU's
+  float32 SwiGLU and the oracle's float64 one round ``a`` to different bf16
+  neighbours) moves its whole output row by up to ~2 % at I = 128: the
+  intermediate codes and scales the gate/up stage leaves in the workspace
+  equal the oracle's except for such rare neighbouring-code flips; the down
+  stage, given the GPU's own intermediate, matches the oracle per row and
+  element within 2e-2; and end to end the Frobenius error per expert is
+  within 2e-2.  pow2 padding rows are never written; GATE_UP then DOWN gives
+  the same bits as ALL.
 """
 
 import numpy as np
@@ -20,7 +27,8 @@ import oracle
 import workloads
 from combine_top_route_moe_amd import ops
 from oracle.numerics import bf16_bits_to_f32
-from tests.gpu_util import need_gpu, dev_bf16, host_bits, dev, host, rel_err, stacked_weights
+from tests.gpu_util import (need_gpu, dev_bf16, host_bits, dev, host, stacked_weights, check_rows,
+                            rel_err, e4m3_decode, w8a8_intermediate, check_fp8_intermediate)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,16 +38,6 @@ FFN_TOL = 2e-2
 def setup_module(module):
     need_gpu()
     assert ops.moe_device_check(0) == 0, "not a gfx950 device"
-
-
-def e4m3_decode(codes: np.ndarray) -> np.ndarray:
-    """OCP E4M3FN bytes to values (sign, 4 exponent bits with bias 7, 3
-    mantissa bits; exponent 0 subnormal).  NaN codes must not appear."""
-    c = codes.astype(np.int64)
-    assert not np.any((c & 0x7F) == 0x7F), "NaN code"
-    e, m = (c >> 3) & 0xF, c & 7
-    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7))
-    return np.where(c & 0x80, -mag, mag)
 
 
 def test_quant_rows_fp8_matches_oracle():
@@ -157,18 +155,26 @@ def test_w8a8_ffn_matches_oracle(H, I, T, hot, pow2):
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
     ref = oracle.permute(idx, w, hid, G, 0, pow2)
     qx, sx = oracle.quantize_rows_fp8(ref["x_perm"], row_mask=ref["src_of"] >= 0)
-    want = oracle.grouped_ffn_w8a8(qx, sx, ref["cu_seqlens"], ref["counts"],
-                                   lambda e: host_w[e], ref["w_perm"])
     got = bf16_bits_to_f32(host_bits(y))
-    worst = 0.0
+    # the intermediate the gate/up stage left in the workspace, per row
+    qa_gpu, sa_gpu = w8a8_intermediate(ws, cap, G, I, ref["counts"], ref["cu_seqlens"])
+    worst, flips = 0.0, 0.0
     for e in range(G):
         n, r0 = int(ref["counts"][e]), int(ref["cu_seqlens"][e])
         if n == 0:
             continue
-        err_e = rel_err(got[r0:r0 + n], want[r0:r0 + n])
-        worst = max(worst, err_e)
-        assert err_e <= FFN_TOL, (e, n, err_e)
+        st = oracle.expert_ffn_w8a8_steps(qx[r0:r0 + n], sx[r0:r0 + n], *host_w[e])
+        rs = ref["w_perm"][r0:r0 + n, None].astype(np.float64)
+        # gate/up: the same codes and scales but for last-bit flips of bf16 a
+        flips = max(flips, check_fp8_intermediate(qa_gpu[r0:r0 + n], sa_gpu[r0:r0 + n],
+                                                  st["qa"], st["sa"], what=f"expert {e}"))
+        # down, on the GPU's own intermediate: per row and element
+        y_own = oracle.block_scaled_matmul(qa_gpu[r0:r0 + n], sa_gpu[r0:r0 + n], *st["w2q"]) * rs
+        c = check_rows(got[r0:r0 + n], y_own, FFN_TOL, what=f"expert {e} ({n} rows), down")
+        worst = max(worst, c["worst_row"])
+        # end to end against the oracle's own chain
+        assert rel_err(got[r0:r0 + n], st["y"] * rs) <= FFN_TOL, e
         seg_end = int(ref["cu_seqlens"][e + 1])
         if seg_end > r0 + n:
             assert np.all(host_bits(y[r0 + n:seg_end]) == 0)
-    print(f"H={H} I={I} T={T}: worst per-expert rel err vs the FP8 oracle {worst:.3e}")
+    print(f"H={H} I={I} T={T}: worst down row rel err {worst:.3e}, intermediate code flips {flips:.2e}")

@@ -102,3 +102,34 @@ def test_expert_ffn_w8a8_error_is_the_intermediate_rounding():
     # and the bound is not vacuous: a dropped block scale breaks it
     qa_bad = expert_ffn_w8a8(qx, sx * np.float32(2), w13b, w2b)
     assert not np.all(np.abs(qa_bad - want) <= bound)
+
+
+def test_grouped_ffn_w8a8_equals_row_by_row():
+    """The segment loop against each row computed on its own: hand-built
+    segments with an empty expert and pow2 padding rows (garbage codes that
+    must not be computed), a different router weight per row.  A wrong
+    segment start, a slice of the wrong expert's weights or router weights,
+    or padding rows that leak into the output fail it."""
+    rng = np.random.default_rng(21)
+    H, I = 256, 128
+    counts = np.array([3, 0, 5, 1], np.int32)
+    sizes = np.array([4, 0, 8, 1])                        # next powers of two
+    cu = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    cap = int(cu[-1])
+    xb = _rows(cap, H, 22)
+    qx, sx = quantize_rows_fp8(xb)
+    valid = np.zeros(cap, bool)
+    for e in range(4):
+        valid[cu[e]:cu[e] + counts[e]] = True
+    qx[~valid] = 448.0                                    # padding rows hold garbage
+    sx[~valid] = np.float32(1e3)
+    w = {e: (f32_to_bf16_bits((rng.standard_normal((2 * I, H)) * 0.05).astype(np.float32)),
+             f32_to_bf16_bits((rng.standard_normal((H, I)) * 0.05).astype(np.float32)))
+         for e in range(4)}
+    row_scale = rng.uniform(0.1, 1.0, cap).astype(np.float32)
+    got = oracle.grouped_ffn_w8a8(qx, sx, cu, counts, lambda e: w[e], row_scale)
+    assert np.all(got[~valid] == 0)
+    for e in range(4):
+        for r in range(cu[e], cu[e] + counts[e]):
+            want = expert_ffn_w8a8(qx[r:r + 1], sx[r:r + 1], *w[e])[0] * float(row_scale[r])
+            np.testing.assert_allclose(got[r], want, rtol=1e-9, atol=1e-12)

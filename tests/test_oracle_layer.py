@@ -73,3 +73,76 @@ def test_workload_shapes_and_recipe():
     assert counts2[hot].min() > 4 * counts2[cold].max()
     v = workloads.row_valid(c["prefill"])
     assert int((v == 0).sum()) == 1638
+
+
+def _f32_ordered_sum(rows, shared=None):
+    """float32 sum from +0 in the given order, the shared row last, then one
+    bfloat16 rounding (written out here with scalar float32 adds)."""
+    H = rows.shape[1] if len(rows) else shared.shape[0]
+    acc = np.zeros(H, np.float32)
+    for r in rows:
+        acc = (acc + oracle.bf16_bits_to_f32(r)).astype(np.float32)
+    if shared is not None:
+        acc = (acc + oracle.bf16_bits_to_f32(shared)).astype(np.float32)
+    return oracle.f32_to_bf16_bits(acc)
+
+
+def test_layer_fp8_gemm_equals_dense_per_token_sum():
+    """The FP8 path (``fp8_gemm=True``) through the grouped layer equals a
+    dense per-token loop: quantize the token's row, run each chosen expert's
+    FP8 FFN on that one row, weight it, round it to bfloat16, add the slots
+    in order and the shared expert (on the same codes) last.  Pins the
+    gather of codes and scales through ``src_of // K`` and the shared
+    expert's input in the layer's FP8 branch."""
+    cfg = workloads.CONFIGS["tiny"].with_(pad_rows=6, shared_I=128, T=24)
+    sw = workloads.shared_weights(cfg)
+    res, w = _tiny_layer(cfg, shared_weights=sw, fp8_gemm=True, pad_pow2=True)
+    hid = workloads.hidden(cfg)
+    for t in range(cfg.T):
+        qx, sx = oracle.quantize_rows_fp8(hid[t:t + 1])
+        rows = []
+        for k in range(cfg.K):
+            e = res["topk_idx"][t, k]
+            if e < 0:
+                continue
+            y = oracle.expert_ffn_w8a8(qx, sx, *w[e])[0] * float(res["topk_w"][t, k])
+            rows.append(oracle.f32_to_bf16_bits(y.astype(np.float32)))
+        rows = np.array(rows, np.uint16).reshape(-1, cfg.H)
+        shared = oracle.f32_to_bf16_bits(oracle.expert_ffn_w8a8(qx, sx, *sw)[0].astype(np.float32))
+        np.testing.assert_array_equal(res["out"][t], _f32_ordered_sum(rows, shared), err_msg=str(t))
+
+
+def test_layer_quantizer_wiring_equals_per_token_composition():
+    """Dispatch and combine FP8 quantizers in the layer, bit for bit against
+    a per-token composition: the token's row fake-quantized per 1 x 128
+    block -> each chosen expert's FFN -> router weight -> bfloat16 -> the
+    per-tensor combine QDQ -> the ordered sum, with the shared expert on the
+    unquantized row, added last and never quantized.  The calibrated scale
+    is fl32(max|row| / 448) over exactly the routed rows of the composition
+    (pow2 padding rows and the shared rows excluded)."""
+    cfg = workloads.CONFIGS["tiny"].with_(pad_rows=5, shared_I=128)
+    sw = workloads.shared_weights(cfg)
+    res, w = _tiny_layer(cfg, shared_weights=sw, dispatch_block=128, pad_pow2=True,
+                         combine_qdq=True)
+    hid = workloads.hidden(cfg)
+    per_tok = []
+    for t in range(cfg.T):
+        if res["topk_idx"][t, 0] < 0:
+            per_tok.append(np.zeros((0, cfg.H), np.uint16))
+            continue
+        hq, _ = oracle.fake_quant_block(hid[t:t + 1], 128)
+        x = bf16_bits_to_f64(hq)
+        rows = [oracle.f32_to_bf16_bits(
+                    (oracle.expert_ffn(x, *w[res["topk_idx"][t, k]])[0]
+                     * float(res["topk_w"][t, k])).astype(np.float32))
+                for k in range(cfg.K)]
+        per_tok.append(np.array(rows, np.uint16))
+    allrows = np.concatenate([r for r in per_tok if len(r)])
+    amax = np.float32(np.abs(oracle.bf16_bits_to_f32(allrows)).max())
+    scale = np.float32(amax / np.float32(448.0))
+    assert res["combine_scale"] == scale
+    x_all = bf16_bits_to_f64(hid)
+    for t in range(cfg.T):
+        rows_q = oracle.fake_quant_per_tensor(per_tok[t], scale) if len(per_tok[t]) else per_tok[t]
+        shared = oracle.f32_to_bf16_bits(oracle.expert_ffn(x_all[t:t + 1], *sw)[0].astype(np.float32))
+        np.testing.assert_array_equal(res["out"][t], _f32_ordered_sum(rows_q, shared), err_msg=str(t))

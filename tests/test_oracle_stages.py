@@ -90,6 +90,37 @@ def test_route_invariants_and_padding():
         assert np.all(np.diff(w[t]) <= 0)
 
 
+def test_route_nan_ranks_as_minus_infinity():
+    """A NaN logit ranks exactly like -inf (below every number, ties among
+    such entries to the lower index), checked against the brute-force
+    subset order on the row with -inf written in; weights against closed
+    forms: a chosen -inf below a finite maximum weighs 0, and a row whose
+    chosen logits are all -inf (or NaN) splits 1/k evenly."""
+    nan, inf = np.float32(np.nan), np.float32(np.inf)
+    logits = np.array([
+        [nan, 1.0, 0.5, nan, 2.0, -3.0],       # NaNs among finite values
+        [nan, nan, nan, nan, nan, nan],        # all NaN
+        [-inf, nan, 0.0, -inf, nan, -1.0],     # fewer than k finite
+        [inf, 1.0, inf, nan, -inf, 0.0],       # two +inf: they tie at the top
+    ], dtype=np.float32)
+    k = 3
+    idx, w = oracle.route(logits, None, k)
+    as_inf = np.where(np.isnan(logits), -inf, logits)
+    for t in range(len(logits)):
+        assert list(idx[t]) == _brute_topk(as_inf[t], k), t
+    np.testing.assert_allclose(w[0], scipy.special.softmax([2.0, 1.0, 0.5]), rtol=1e-6)
+    assert list(idx[1]) == [0, 1, 2] and np.all(w[1] == np.float32(1 / 3))
+    assert list(idx[2]) == [2, 5, 0]
+    np.testing.assert_allclose(w[2], [1 / (1 + math.exp(-1)), math.exp(-1) / (1 + math.exp(-1)), 0.0],
+                               rtol=1e-6)
+    assert list(idx[3]) == [0, 2, 1] and list(w[3]) == [0.5, 0.5, 0.0]
+    # without renormalisation the denominator runs over all E the same way
+    _, w_full = oracle.route(logits, None, k, renormalize=False)
+    np.testing.assert_allclose(w_full[0], scipy.special.softmax([2.0, 1.0, 0.5, -3.0])[:3],
+                               rtol=1e-6)
+    assert np.all(w_full[1] == np.float32(1 / 6))
+
+
 # ----------------------------------------------------------------- fake quant
 
 def test_block_fake_quant_blocks_are_independent():
@@ -132,6 +163,29 @@ def test_permute_hand_examples():
         p = oracle.permute(idx, w, hid, case["E"], case["expert_begin"], case["pad_pow2"])
         for key in ("counts", "cu_seqlens", "row_of", "src_of"):
             assert p[key].tolist() == case[key], key
+
+
+def test_permute_expert_ids_past_the_layer_are_reported_not_routed():
+    """An id at or past the layer's expert count is dropped and reported;
+    the other slots land exactly where they would without it; negative ids
+    of any value are padding slots (not reported)."""
+    idx = np.array([[0, 9], [3, -1], [-5, 2], [4, 1]], np.int32)   # E = 5: 9 is bad
+    w = np.arange(8, dtype=np.float32).reshape(4, 2) + 1
+    hid = np.arange(16, dtype=np.uint16).reshape(4, 4)
+    p = oracle.permute(idx, w, hid, 5, num_experts=5)
+    assert p["expert_range_error"]
+    assert p["row_of"].tolist() == [0, -1, 3, -1, -1, 2, 4, 1]
+    assert p["counts"].tolist() == [1, 1, 1, 1, 1]
+    clean = idx.copy()
+    clean[0, 1] = -1
+    q = oracle.permute(clean, w, hid, 5, num_experts=5)
+    assert not q["expert_range_error"]
+    for key in ("counts", "cu_seqlens", "row_of", "src_of", "w_perm", "x_perm"):
+        np.testing.assert_array_equal(p[key], q[key])
+    # an expert-parallel share of [2, 4) inside 5 experts: 4 belongs to
+    # another rank (not reported), 9 to none (reported)
+    r = oracle.permute(idx, w, hid, 2, expert_begin=2, num_experts=5)
+    assert r["expert_range_error"] and r["counts"].tolist() == [1, 1]
 
 
 def _permute_by_stable_argsort(idx, El, expert_begin):

@@ -110,13 +110,19 @@ def committed_traffic(stage: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, logits, hidden, row_valid, budget_s: float, fp8=None):
-    """Time the oracle layer (as it stands) on a bounded sample of tokens.
-    With FP8 weights the oracle's weight quantization runs once per expert
-    before timing (like weight generation): the timed layer is the oracle
-    on the dequantized weights, which is what its FP8-weight mode computes."""
+def cpu_baseline(cfg, logits, hidden, row_valid, budget_s: float, expert_weights, shared):
+    """Time the oracle layer (as it stands) on a bounded sample of the batch:
+    its first n tokens, n doubled from 8 until one run takes about a quarter
+    of the budget, then repeated (median kept) until about half of it.
+
+    ``expert_weights(e)`` returns expert e's bf16 weights as host arrays; the
+    bench hands over a copy from the device tensors it uploaded (a few ms per
+    expert, inside the timed oracle run), so no second copy of every
+    expert's weights is held in host memory.  The sample is a prefix of the
+    batch, so it pays the oracle's per-expert costs (converting each touched
+    expert's weights to float64) for fewer tokens than the full batch would:
+    the rate is a lower bound for the full batch, labelled as a sample."""
     import oracle
-    import workloads
 
     cores = len(os.sched_getaffinity(0))
     try:
@@ -126,53 +132,34 @@ def cpu_baseline(cfg, logits, hidden, row_valid, budget_s: float, fp8=None):
             cores = min(cores, max(blas))
     except Exception:
         pass
-    # a contiguous prefix of the batch, sized so the run stays within budget:
-    # probe with a small sample, then scale
-    weights_cache = {}
-
-    def prep(ws):
-        if fp8 != "weights":
-            return ws
-        return tuple(oracle.quantize_weight_blocks(w)[2] for w in ws)
-
-    def weights(e):
-        if e not in weights_cache:
-            weights_cache[e] = prep(workloads.expert_weights(cfg, e))
-        return weights_cache[e]
-
-    shared = workloads.shared_weights(cfg)
-    if shared is not None:
-        shared = prep(shared)
 
     def run(n):
         rv = None if row_valid is None else row_valid[:n]
         t0 = time.perf_counter()
-        oracle.moe_layer(logits[:n], hidden[:n], weights, cfg.K, rv,
+        oracle.moe_layer(logits[:n], hidden[:n], expert_weights, cfg.K, rv,
                          dispatch_block=cfg.dispatch_block or None, pad_pow2=cfg.pad_pow2,
-                         shared_weights=shared, combine_qdq=cfg.combine_qdq,
-                         fp8_gemm=fp8 == "w8a8")
+                         shared_weights=shared, combine_qdq=cfg.combine_qdq)
         return time.perf_counter() - t0
 
-    n = min(cfg.T, 64)
-    for e in range(cfg.E):            # weight generation is not part of the timed oracle
-        weights(e)
+    n = min(cfg.T, 8)
     dt = run(n)
     while n < cfg.T and dt < budget_s / 4:
-        n = min(cfg.T, n * 4)
+        n = min(cfg.T, n * 2)
         dt = run(n)
     times = [dt]
-    # repeat the sample (the median is kept) until about half the budget of
-    # CPU work has been done, so that a small batch is still timed over
-    # seconds, not one short run
     while sum(times) < budget_s / 2 and len(times) < 50:
         times.append(run(n))
     dt = float(np.median(times))
     tv = n if row_valid is None else int(row_valid[:n].sum())
+    touched = len(set(int(e) for e in oracle.route(logits[:n], None if row_valid is None
+                                                   else row_valid[:n], cfg.K)[0].reshape(-1)
+                      if e >= 0))
     return {"value": tv / dt, "unit": "routed tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {n} of {cfg.T} tokens of the {cfg.name} batch ({tv} routed), "
-                      f"whole layer, float64 numpy, median of {len(times)} runs: {dt:.2f} s"
-                      + ("; FP8 weights dequantized once before timing" if fp8 == "weights"
-                         else "; the oracle's FP8 path" if fp8 == "w8a8" else "")}
+            "sample": f"first {n} of {cfg.T} tokens of the {cfg.name} batch ({tv} routed, "
+                      f"{touched} of {cfg.E} experts touched), whole layer, float64 numpy, "
+                      f"median of {len(times)} runs: {dt:.2f} s; a prefix pays each touched "
+                      "expert's weight conversion for fewer tokens than the whole batch, so "
+                      "this sampled rate is a lower bound for the full batch"}
 
 
 def calibrate_spin(stream, target_ms: float = 1.0) -> int:
@@ -187,6 +174,27 @@ def calibrate_spin(stream, target_ms: float = 1.0) -> int:
     torch.cuda.synchronize()
     ms = max(a.elapsed_time(b), 1e-3)
     return int(cycles * target_ms / ms)
+
+
+def copy_gbps(steps: int = 5, nbytes: int = 1 << 30) -> float:
+    """Bandwidth of moe_copy_bytes (read + write) over 1 GiB: the plain
+    16-byte streaming copy, timed with events on the launch stream."""
+    import torch
+    from combine_top_route_moe_amd import ops
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    ops.moe_copy_bytes(src, dst)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        ops.moe_copy_bytes(src, dst)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
 def copy_calibration(steps: int, warmup: int) -> None:
@@ -214,17 +222,22 @@ def copy_calibration(steps: int, warmup: int) -> None:
                       "GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
+def pct(v, q):
+    return round(float(np.percentile(np.asarray(v, dtype=np.float64), q)), 5)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="balanced",
-                    help="tiny | balanced | skewed | deepseek | prefill")
+    ap.add_argument("--config", default="deepseek",
+                    help="deepseek (default: the largest workload) | prefill | balanced | "
+                         "skewed | tiny")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-stages", action="store_true",
-                    help="also time the stages with 1 GiB written before every step (cold "
-                         "caches) and report them as stages_cold")
+    ap.add_argument("--no-cold-stages", action="store_true",
+                    help="skip the stage timing with 1 GiB written before every step (cold "
+                         "caches), reported as stages_cold")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the steps as eager launches instead of HIP-graph replays")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
@@ -281,8 +294,8 @@ def main():
     sw = workloads.shared_weights(cfg)
     layer.set_weights(w13, w2, *(bf16(x) for x in sw) if sw else (None, None),
                       fp8={None: False, "weights": True, "w8a8": "w8a8"}[args.fp8])
-    if args.fp8:
-        del w13, w2                   # only the packed FP8 codes stay resident
+    if args.fp8 or args.no_cpu_baseline:
+        del w13, w2                   # only the packed weights stay resident
     if cfg.combine_qdq:
         layer.calibrate_combine_scale(logits, hidden, row_valid)
     torch.cuda.synchronize()
@@ -320,6 +333,24 @@ def main():
     elapsed = time.perf_counter() - t0
     assert layer.dev_error.item() == 0, "device error word set during the timed run"
 
+    # Per-step layer times (after the timed region, not instead of it): each
+    # graph replay and each eager step bracketed by events on the launch
+    # stream, for the median and the p10 / p90 spread.
+    def per_step(fn):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for i in range(args.steps):
+            fn()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+
+    layer_ms = {}
+    if graph is not None:
+        layer_ms["graph"] = per_step(graph.replay)
+    layer_ms["eager"] = per_step(lambda: layer.forward(logits, hidden, row_valid))
+
     # Timed region 2 (stages, roofline): K eager steps with HIP events between
     # the stages on the launch stream.  Each step is preceded by a short GPU
     # spin kernel, so the host has enqueued the whole step (and its events)
@@ -342,30 +373,33 @@ def main():
             torch.cuda.synchronize()
             for i, (name, _) in enumerate(stages):
                 per_stage[name].append(evs[i].elapsed_time(evs[i + 1]))
-        return {k: float(np.median(v)) for k, v in per_stage.items()}
+        return per_stage
 
-    stage_ms = time_stages()
-    # Timed region 3 (--cold-stages, stages_cold): the same with 1 GiB
-    # written before every step, so each stage starts from cold caches (a
-    # replayed layer otherwise finds part of its weights, and the small
-    # workloads part of their rows, in the infinity cache); reported beside
-    # the in-context figures, not instead of them.  Off by default, so that
-    # the default run's kernels are the in-context ones only.
-    stage_ms_cold = None
-    if args.cold_stages:
+    stage_samples = time_stages()
+    # Timed region 3 (stages_cold): the same with 1 GiB written before every
+    # step, so each stage starts from cold L2 and infinity cache (a replayed
+    # layer otherwise finds part of its weights, and the small workloads part
+    # of their rows, in the infinity cache); reported beside the in-context
+    # figures, not instead of them.  --no-cold-stages skips it (the profiled
+    # runs do, so that their kernel averages are the in-context launches).
+    stage_samples_cold = None
+    if not args.no_cold_stages:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        stage_ms_cold = time_stages(flush)
+        stage_samples_cold = time_stages(flush)
         del flush
     assert layer.dev_error.item() == 0, "device error word set during the stage timing"
+    copy_bw = copy_gbps()
 
     counts = layer.perm.counts.cpu().numpy()
     alg = algorithmic(cfg, counts, args.fp8)
     peak_mfma = PEAK_FP8_TFLOPS if args.fp8 == "w8a8" else PEAK_BF16_TFLOPS
-    def stage_report(times):
+
+    def stage_report(samples):
         out = {}
-        for name, ms in times.items():
+        for name, v in samples.items():
+            ms = float(np.median(v))
             a = alg.get(name, {})
-            d = {"ms": round(ms, 5)}
+            d = {"ms": round(ms, 5), "ms_p10": pct(v, 10), "ms_p90": pct(v, 90)}
             if "bytes" in a:
                 d["alg_bytes"] = a["bytes"]
                 d["GBps"] = round(a["bytes"] / (ms * 1e-3) / 1e9, 1)
@@ -376,8 +410,9 @@ def main():
             out[name] = d
         return out
 
-    stages = stage_report(stage_ms)
-    stages_cold = stage_report(stage_ms_cold) if stage_ms_cold else None
+    stage_ms = {k: float(np.median(v)) for k, v in stage_samples.items()}
+    stages = stage_report(stage_samples)
+    stages_cold = stage_report(stage_samples_cold) if stage_samples_cold else None
 
     dom = max(stage_ms, key=stage_ms.get)
     a = alg[dom]
@@ -424,22 +459,38 @@ def main():
         "grouped_gemm_mfma_util": round(gemm_flops / (gemm_ms * 1e-3) / (peak_mfma * 1e12), 4),
         "permute_GBps": stages["permute"]["GBps"],
         "combine_GBps": stages["combine"]["GBps"],
+        "copy_GBps": round(copy_bw, 1),
+        "layer_ms": {k: {"median": round(float(np.median(v)), 5), "p10": pct(v, 10),
+                         "p90": pct(v, 90)} for k, v in layer_ms.items()},
         "stages": stages,
         **({"stages_cold": stages_cold} if stages_cold else {}),
         "roofline": roof,
         "timing": {"value": ("HIP-graph replay of the whole layer" if graph is not None
                              else "eager launches of the whole layer"),
+                   "layer_ms": "each graph replay and each eager whole-layer step between HIP "
+                               "events on the launch stream (after the timed region)",
                    "stages": "eager steps queued behind a GPU spin kernel, HIP events between "
-                             "stages on the launch stream, median over steps; stages run "
-                             "one after another (the layer itself runs the shared expert "
+                             "stages on the launch stream, median (p10, p90) over steps; stages "
+                             "run one after another (the layer itself runs the shared expert "
                              "concurrently with the routed path)",
+                   "copy_GBps": "moe_copy_bytes, 1 GiB read + 1 GiB written per launch",
                    **({"stages_cold": "the same, with 1 GiB written before every step "
                                       "(cold L2 and infinity cache)"} if stages_cold else {})},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, logits_h, hidden_h, valid_h, args.cpu_budget,
-                                              args.fp8)
+        if args.fp8:
+            result["cpu_baseline_note"] = (
+                "not timed in the FP8 modes: the oracle quantizes each expert's weights to "
+                "128 x 128 tiles in numpy (seconds per expert), which a bounded sample cannot "
+                "separate from the layer; the BF16 line carries the oracle baseline")
+        else:
+            def expert_weights(e):
+                return (w13[e].view(torch.int16).cpu().numpy().view(np.uint16),
+                        w2[e].view(torch.int16).cpu().numpy().view(np.uint16))
+
+            result["cpu_baseline"] = cpu_baseline(cfg, logits_h, hidden_h, valid_h,
+                                                  args.cpu_budget, expert_weights, sw)
     print(json.dumps(result), flush=True)
 
 

@@ -22,6 +22,10 @@ SIGNATURES = {
     "moe_permute_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "moe_permute": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                              _c_int, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp, _vp]),
+    "moe_permute_noalloc_scratch_bytes": (_c_size, []),
+    "moe_permute_noalloc": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                     _c_int, _c_int, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _vp]),
     "moe_grouped_ffn_workspace_bytes": (_c_size, [_c_i64, _c_int, _c_int, _c_int]),
     "moe_grouped_ffn": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp,
                                  _c_i64, _c_int, _vp, _c_size, _vp, _vp]),

@@ -19,6 +19,10 @@ size_t permute_workspace_bytes(int64_t, int);
 int launch_permute(const int32_t*, const float*, const uint16_t*, int, int, int, int, int, int, int,
                    int, int64_t, int32_t*, int32_t*, uint16_t*, int32_t*, int32_t*, float*, void*,
                    int32_t*, hipStream_t);
+size_t permute_noalloc_scratch_bytes();
+int launch_permute_noalloc(const int32_t*, const float*, const uint16_t*, int, int, int, int, int,
+                           int, int, int, int64_t, int32_t*, int32_t*, uint16_t*, int32_t*,
+                           int32_t*, float*, int32_t*, hipStream_t);
 size_t grouped_ffn_workspace_bytes(int64_t, int, int);
 int launch_grouped_ffn(const uint16_t*, const int32_t*, const int32_t*, int, int, int,
                        const void*, const float*, const void*, const float*, const float*,
@@ -58,6 +62,9 @@ const char* moe_status_string(int status) {
     case MOE_ERR_WORKSPACE: return "workspace smaller than the size query requires";
     case MOE_ERR_HIP: return "HIP runtime error or kernel launch failure";
     case MOE_ERR_DEVICE: return "the current device is not a gfx950 (MI355X-class) GPU";
+    case MOE_ERR_SCRATCH:
+      return "the call needs more than moe_permute_noalloc's fixed device scratch (4 MiB); "
+             "use moe_permute with a caller workspace";
     default: return "unknown status";
   }
 }
@@ -99,7 +106,7 @@ size_t moe_permute_workspace_bytes(int T, int K, int num_local_experts, int flag
   return permute_workspace_bytes((int64_t)T * K, num_local_experts);
 }
 
-// Argument checks of moe_permute (scalars and
+// Argument checks shared by moe_permute and moe_permute_noalloc (scalars and
 // pointers only).
 static int check_permute_args(const int32_t* topk_idx, const float* topk_w, const uint16_t* hidden,
                               int T, int K, int H, int num_experts, int expert_begin,
@@ -135,6 +142,24 @@ int moe_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t* hi
                         num_local_experts, (flags & MOE_PERMUTE_PAD_POW2) ? 1 : 0,
                         (flags & MOE_PERMUTE_DISPATCH_FP8) ? 1 : 0, capacity, counts, cu_seqlens,
                         x_perm, row_of, src_of, w_perm, workspace, dev_error, as_stream(stream));
+}
+
+size_t moe_permute_noalloc_scratch_bytes(void) { return permute_noalloc_scratch_bytes(); }
+
+int moe_permute_noalloc(const int32_t* topk_idx, const float* topk_w, const uint16_t* hidden,
+                        int T, int K, int H, int num_experts, int expert_begin,
+                        int num_local_experts, int flags, int64_t capacity, int32_t* counts,
+                        int32_t* cu_seqlens, uint16_t* x_perm, int32_t* row_of, int32_t* src_of,
+                        float* w_perm, int32_t* dev_error, void* stream) {
+  const int st = check_permute_args(topk_idx, topk_w, hidden, T, K, H, num_experts, expert_begin,
+                                    num_local_experts, flags, capacity, counts, cu_seqlens,
+                                    x_perm, row_of, src_of, w_perm);
+  if (st != MOE_OK) return st;
+  return launch_permute_noalloc(topk_idx, topk_w, hidden, T, K, H, num_experts, expert_begin,
+                                num_local_experts, (flags & MOE_PERMUTE_PAD_POW2) ? 1 : 0,
+                                (flags & MOE_PERMUTE_DISPATCH_FP8) ? 1 : 0, capacity, counts,
+                                cu_seqlens, x_perm, row_of, src_of, w_perm, dev_error,
+                                as_stream(stream));
 }
 
 size_t moe_grouped_ffn_workspace_bytes(int64_t capacity, int num_groups, int H, int I) {

@@ -39,6 +39,8 @@
 // DeepGEMM Mega-MoE", PR summary and "How it works"; 1 x 128 blocks as in
 // "[Kernel] DeepEP dispatch-combine kernel integration", review thread on
 // the low-latency dispatch) to each row vector on its way.
+#include <atomic>
+
 #include "common.h"
 
 namespace moe {
@@ -663,6 +665,61 @@ int launch_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t*
   }
 #undef MOE_PERMUTE_SCATTER
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// The permute without a caller workspace (moe_permute_noalloc): the chunk
+// table and the ranks live in a fixed device array instead.  Each GPU the
+// library runs on holds its own copy of `scratch` until the process ends;
+// its device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and kept here.  In host code the array's name is
+// only a host-side stand-in, never a device address, so nothing but the
+// looked-up pointer is ever handed to a kernel.  The kernels write every
+// table entry and rank they later read, so nothing needs clearing between
+// calls; calls that overlap on one GPU share the array and race.
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+size_t permute_noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+// The current device's copy of `scratch`, or nullptr with *status set.
+static void* current_device_scratch(int* status) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    *status = MOE_ERR_HIP;
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *status = MOE_ERR_UNSUPPORTED;
+    return nullptr;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) {
+    *status = MOE_ERR_HIP;
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(q, std::memory_order_release);   // racing threads store the same
+  return q;
+}
+
+int launch_permute_noalloc(const int32_t* topk_idx, const float* topk_w, const uint16_t* hidden,
+                           int T, int K, int H, int num_experts, int expert_begin, int El,
+                           int pad_pow2, int dispatch_fp8, int64_t capacity, int32_t* counts,
+                           int32_t* cu_seqlens, uint16_t* x_perm, int32_t* row_of,
+                           int32_t* src_of, float* w_perm, int32_t* dev_error,
+                           hipStream_t stream) {
+  if (permute_workspace_bytes((int64_t)T * K, El) > kNoAllocScratchBytes) return MOE_ERR_SCRATCH;
+  int status = MOE_OK;
+  void* ws = current_device_scratch(&status);
+  if (!ws) return status;
+  return launch_permute(topk_idx, topk_w, hidden, T, K, H, num_experts, expert_begin, El,
+                        pad_pow2, dispatch_fp8, capacity, counts, cu_seqlens, x_perm, row_of,
+                        src_of, w_perm, ws, dev_error, stream);
 }
 
 }  // namespace moe

@@ -21,6 +21,7 @@ MOE_PERMUTE_DISPATCH_FP8 = 2
 MOE_FFN_GATE_UP, MOE_FFN_DOWN, MOE_FFN_ALL, MOE_FFN_PACKED_WEIGHTS = 1, 2, 3, 4
 MOE_FQ_PER_TENSOR, MOE_FQ_BLOCK, MOE_FQ_NVFP4, MOE_FQ_MXFP4 = 0, 1, 2, 3
 MOE_DEVERR_ROW_RANGE, MOE_DEVERR_CAPACITY, MOE_DEVERR_LAYOUT, MOE_DEVERR_EXPERT_RANGE = 1, 2, 3, 4
+MOE_ERR_SCRATCH = -6
 MOE_FP8_LAYOUT_K128 = 1
 
 
@@ -128,6 +129,34 @@ def moe_permute(topk_idx: torch.Tensor, topk_w: torch.Tensor, hidden: torch.Tens
         flags, capacity, _ptr(out.counts), _ptr(out.cu_seqlens), _ptr(out.x_perm),
         _ptr(out.row_of), _ptr(out.src_of), _ptr(out.w_perm), _ptr(workspace),
         workspace.numel(), _ptr(dev_error), _stream(stream)))
+    return out
+
+
+def moe_permute_noalloc_scratch_bytes() -> int:
+    return load().moe_permute_noalloc_scratch_bytes()
+
+
+def moe_permute_noalloc(topk_idx: torch.Tensor, topk_w: torch.Tensor, hidden: torch.Tensor,
+                        num_local_experts: int, out: Permuted, expert_begin: int = 0,
+                        pad_pow2: bool = False, dev_error: Optional[torch.Tensor] = None,
+                        stream=None, dispatch_fp8: bool = False,
+                        num_experts: Optional[int] = None) -> Permuted:
+    """``moe_permute`` with the library's fixed device scratch instead of a
+    workspace: the caller passes the output buffers (``out``, whose
+    ``x_perm`` rows are the capacity); nothing is allocated here either."""
+    _want(topk_idx, torch.int32, "topk_idx")
+    _want(topk_w, torch.float32, "topk_w")
+    _want(hidden, torch.bfloat16, "hidden")
+    T, K = topk_idx.shape
+    H = hidden.shape[1]
+    flags = (MOE_PERMUTE_PAD_POW2 if pad_pow2 else 0) | (MOE_PERMUTE_DISPATCH_FP8 if dispatch_fp8 else 0)
+    if num_experts is None:
+        num_experts = expert_begin + num_local_experts
+    check("moe_permute_noalloc", load().moe_permute_noalloc(
+        _ptr(topk_idx), _ptr(topk_w), _ptr(hidden), T, K, H, num_experts, expert_begin,
+        num_local_experts, flags, out.x_perm.shape[0], _ptr(out.counts), _ptr(out.cu_seqlens),
+        _ptr(out.x_perm), _ptr(out.row_of), _ptr(out.src_of), _ptr(out.w_perm), _ptr(dev_error),
+        _stream(stream)))
     return out
 
 

@@ -52,7 +52,9 @@ enum {
                                H or I not a multiple of 128, E > 1024)     */
   MOE_ERR_WORKSPACE = -3,   /* workspace smaller than the size query says */
   MOE_ERR_HIP = -4,         /* a HIP runtime call or launch failed        */
-  MOE_ERR_DEVICE = -5       /* the current device is not a gfx950 GPU     */
+  MOE_ERR_DEVICE = -5,      /* the current device is not a gfx950 GPU     */
+  MOE_ERR_SCRATCH = -6      /* moe_permute_noalloc: the call needs more than
+                               its fixed device scratch                   */
 };
 
 /* ---- device error word codes (first error wins) ----------------------- */
@@ -173,6 +175,28 @@ int moe_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t* hi
                 int64_t capacity, int32_t* counts, int32_t* cu_seqlens, uint16_t* x_perm,
                 int32_t* row_of, int32_t* src_of, float* w_perm, void* workspace,
                 size_t workspace_bytes, int32_t* dev_error, void* stream);
+
+/* moe_permute without a workspace argument, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same operation, arguments, outputs, flags
+ * and errors as moe_permute, with the chunk table and ranks kept in a
+ * fixed array of moe_permute_noalloc_scratch_bytes() (4 MiB) in device
+ * memory that the library owns (one copy per GPU, held until the process
+ * ends; its address is looked up once per device on the first call there).
+ * Nothing is allocated or freed, by this call or any library routine it
+ * uses.  A call whose moe_permute_workspace_bytes() exceeds the scratch
+ * returns MOE_ERR_SCRATCH and enqueues nothing (about T*K <= 900 000 slots
+ * with 128 local experts).  The kernels overwrite every scratch entry they
+ * read, so no state carries over between calls; but every call on one GPU
+ * shares the array, so calls that may overlap on that GPU (concurrent
+ * streams, or graphs replayed concurrently) race and must be serialized by
+ * the caller. */
+size_t moe_permute_noalloc_scratch_bytes(void);
+int moe_permute_noalloc(const int32_t* topk_idx, const float* topk_w, const uint16_t* hidden,
+                        int T, int K, int H, int num_experts, int expert_begin,
+                        int num_local_experts, int flags, int64_t capacity, int32_t* counts,
+                        int32_t* cu_seqlens, uint16_t* x_perm, int32_t* row_of, int32_t* src_of,
+                        float* w_perm, int32_t* dev_error, void* stream);
 
 /* ---- grouped SwiGLU FFN -------------------------------------------------
  * For every group g with n = counts[g] rows starting at row c = cu_seqlens[g]

@@ -218,15 +218,31 @@ __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
 // Neither the DMA nor the chunk barrier may wait for the weight prefetches
 // (lds_barrier and dma16 below say how), or the weight pipeline would drain
 // at every chunk.
+constexpr int kTallMin = 96;     // mean segment rows from which the tall tiles are used
 constexpr int kPrefetch = 4;     // weight K-steps in flight per wave
 constexpr int kChunkSteps = 2;   // activation K-steps per LDS stage
 constexpr int kStages = 3;       // activation LDS ring: DMA runs kStages-1 chunks ahead
 constexpr int kMsub = 8;         // 16-row m-subtiles per workgroup (128 rows)
 constexpr int kFrags = 4;        // B fragments per wave (one column tile)
-constexpr int kStageBlocks = kMsub * kChunkSteps;  // 1 KB blocks per LDS stage
 // Waves (= column tiles) per workgroup, NW: 8 when segments are long (the
 // activation tile is then shared by more columns), 4 when they are short (more,
 // smaller workgroups balance skewed segment sizes better).
+//
+// Tall tiles (TALL): for segments of about one to two m-tiles (129..256 rows
+// would otherwise take two 128-row m-tiles, the second reading the whole
+// weight panel again for a handful of rows), a workgroup covers 256 rows and
+// each wave half a column tile: 16 m-subtiles x 2 fragments (w13: the 16
+// gate rows and the 16 matching up rows; w2: 32 consecutive rows).  The
+// accumulators stay at 16 x 2 x 4 = 128 registers, each weight byte streams
+// into the CU once per segment, and a CU still runs 8 weight streams; the
+// cost is twice the LDS activation reads per MFMA, which the weight-streaming
+// workloads this is used for have to spare.
+template <bool TALL> struct FragShape {
+  static constexpr int kMs = TALL ? 16 : kMsub;        // 16-row m-subtiles per workgroup
+  static constexpr int kFr = TALL ? 2 : kFrags;        // B fragments per wave
+  static constexpr int kRows = 16 * kMs;               // rows per tile
+  static constexpr int kSB = kMs * kChunkSteps;        // 1 KB blocks per LDS stage
+};
 
 
 // FP8 weights: a lane's 8 E4M3 codes (a B-fragment row piece) to the bf16
@@ -260,15 +276,23 @@ __device__ __forceinline__ void epi_store(u32x4_t* p, const u32x4_t& v) {
 template <bool F8>
 using WFrag = typename std::conditional<F8, u32x2_t, u32x4_t>::type;
 
-template <bool GATE_UP, bool NT, int NW, bool F8>
+template <bool GATE_UP, bool NT, int NW, bool F8, bool TALL>
 __device__ __forceinline__ void frag_gemm_body(
-    u32x4_t (*As)[kStageBlocks][kWave], const WFrag<F8>* __restrict__ wp, int kstride,
+    u32x4_t (*As)[FragShape<TALL>::kSB][kWave], const WFrag<F8>* __restrict__ wp, int kstride,
     const float* __restrict__ sc_g, const float* __restrict__ sc_u,
     const uint16_t* a_base, const int64_t* a_uoff, const uint32_t* a_voff, int a_chunk_stride,
     int w, int lane, int nks, int nlive,
-    int valid, int ct, bool ct_ok, int64_t row_base, int64_t mt_glob, int Nout,
+    int valid, int ct, int hsel, bool ct_ok, int64_t row_base, int64_t mt_glob, int Nout,
     const float* tile_scale, uint16_t* __restrict__ Out, int crot, bool prio, uint16_t* epi) {
-  constexpr int kDmaPerWave = kStageBlocks / NW;
+  constexpr int MS = FragShape<TALL>::kMs, FR = FragShape<TALL>::kFr;
+  constexpr int kDmaPerWave = FragShape<TALL>::kSB / NW;
+  // the packed fragment this wave's f-th B operand is: all four of its
+  // column tile, or (tall) the half hsel — w13: gate fragment hsel and up
+  // fragment hsel + 2; w2: fragments 2 hsel, 2 hsel + 1
+  auto frag_of = [&](int f) {
+    if (!TALL) return f;
+    return GATE_UP ? (f == 0 ? hsel : hsel + 2) : 2 * hsel + f;
+  };
   // every workgroup walks K from its own starting chunk (crot) and wraps
   // around, so the many weight streams do not all hit the same offsets —
   // and so the same HBM channels — at the same time
@@ -287,7 +311,7 @@ __device__ __forceinline__ void frag_gemm_body(
     }
     asm volatile("" ::: "memory");
   };
-  WFrag<F8> bq[kPrefetch][kFrags];
+  WFrag<F8> bq[kPrefetch][FR];
   // weights read exactly once stream past the caches (non-temporal)
   auto load_w = [&](int idx) -> WFrag<F8> {
     if (NT) return __builtin_nontemporal_load(&wp[idx]);
@@ -304,16 +328,16 @@ __device__ __forceinline__ void frag_gemm_body(
   };
   auto bfrag = [&](int s, int f) -> bf16x8_t {
     if constexpr (F8)
-      return dequant8(bq[s][f], f >= 2 ? bsu[s] : bsg[s]);
+      return dequant8(bq[s][f], f >= FR / 2 ? bsu[s] : bsg[s]);   // w13: gate, then up
     else
       return __builtin_bit_cast(bf16x8_t, bq[s][f]);
   };
 
-  f32x4_t acc[kMsub][kFrags];
+  f32x4_t acc[MS][FR];
 #pragma unroll
-  for (int i = 0; i < kMsub; ++i)
+  for (int i = 0; i < MS; ++i)
 #pragma unroll
-    for (int f = 0; f < kFrags; ++f) acc[i][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int f = 0; f < FR; ++f) acc[i][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nchunks = nks / kChunkSteps;
 #pragma unroll
@@ -321,7 +345,8 @@ __device__ __forceinline__ void frag_gemm_body(
 #pragma unroll
   for (int s = 0; s < kPrefetch; ++s) {
 #pragma unroll
-    for (int f = 0; f < kFrags; ++f) bq[s][f] = load_w(wrap(s + krot, nks) * kstride + f * kWave);
+    for (int f = 0; f < FR; ++f)
+      bq[s][f] = load_w(wrap(s + krot, nks) * kstride + frag_of(f) * kWave);
     load_scales(s, wrap(s + krot, nks));
   }
   asm volatile("" ::: "memory");
@@ -334,9 +359,9 @@ __device__ __forceinline__ void frag_gemm_body(
   // prologue's DMAs are followed by its kPrologue weight loads and the
   // refills of the chunks before c: fewer than that only for chunk 0, which
   // then waits for kPrologue.
-  constexpr int kAfterDma = (kStages - 1) * kChunkSteps * kFrags;
-  constexpr int kPrologue = kPrefetch * kFrags;
-  static_assert(kAfterDma <= kPrologue + kChunkSteps * kFrags, "prologue count");
+  constexpr int kAfterDma = (kStages - 1) * kChunkSteps * FR;
+  constexpr int kPrologue = kPrefetch * FR;
+  static_assert(kAfterDma <= kPrologue + kChunkSteps * FR, "prologue count");
   static_assert(kPrefetch % kChunkSteps == 0, "chunk boundaries fall on prefetch slots");
   // nks is a multiple of kPrefetch = 4 (K is a multiple of 128)
   int stage = 0;  // ring slot of the current chunk
@@ -373,33 +398,44 @@ __device__ __forceinline__ void frag_gemm_body(
         issue_chunk(min(chunk + kStages - 1, nchunks - 1), ahead);
       }
       const int sub = ks % kChunkSteps;
-      bf16x8_t bfr[kFrags];
+      bf16x8_t bfr[FR];
 #pragma unroll
-      for (int f = 0; f < kFrags; ++f) bfr[f] = bfrag(s, f);
-      // all of the step's activation fragments are read before the MFMAs
-      // (in two halves, so a segment of at most 64 rows reads only the
-      // first): one LDS latency per step instead of one per m-subtile
-      u32x4_t a[kMsub];
+      for (int f = 0; f < FR; ++f) bfr[f] = bfrag(s, f);
+      // the step's activation fragments are read before the MFMAs, 8
+      // m-subtiles at a time (each 8 in two halves, so a segment of at most
+      // 64 rows reads only the first): one LDS latency per 8 m-subtiles
+      // instead of one per m-subtile
 #pragma unroll
-      for (int i = 0; i < kMsub / 2; ++i) a[i] = As[stage][i * kChunkSteps + sub][lane];
-      if (nlive > kMsub / 2) {
+      for (int g8 = 0; g8 < MS; g8 += 8) {
+        // (tall: a constant trip count with skipped iterations, so that the
+        // loops unroll and the 16 x 2 accumulators stay in registers)
+        if (TALL ? g8 >= nlive : false) continue;
+        if (!TALL && g8 >= nlive) break;
+        u32x4_t a[8];
 #pragma unroll
-        for (int i = kMsub / 2; i < kMsub; ++i) a[i] = As[stage][i * kChunkSteps + sub][lane];
-      }
+        for (int i = 0; i < 4; ++i) a[i] = As[stage][(g8 + i) * kChunkSteps + sub][lane];
+        if (nlive > g8 + 4) {
 #pragma unroll
-      for (int i = 0; i < kMsub; ++i) {
-        if (i >= nlive) break;
-        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, a[i]);
+          for (int i = 4; i < 8; ++i) a[i] = As[stage][(g8 + i) * kChunkSteps + sub][lane];
+        }
 #pragma unroll
-        for (int f = 0; f < kFrags; ++f)
-          acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[f], acc[i][f], 0, 0, 0);
+        for (int i = 0; i < 8; ++i) {
+          if (TALL ? g8 + i >= nlive : false) continue;
+          if (!TALL && g8 + i >= nlive) break;
+          const bf16x8_t af = __builtin_bit_cast(bf16x8_t, a[i]);
+#pragma unroll
+          for (int f = 0; f < FR; ++f)
+            acc[g8 + i][f] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[f], acc[g8 + i][f], 0, 0, 0);
+        }
       }
       // refill this slot kPrefetch steps ahead (past the end: the last step
       // again, which keeps the outstanding-load count constant)
       const int nxt = min(ks + kPrefetch, nks - 1);
       asm volatile("" ::: "memory");
 #pragma unroll
-      for (int f = 0; f < kFrags; ++f) bq[s][f] = load_w(wrap(nxt + krot, nks) * kstride + f * kWave);
+      for (int f = 0; f < FR; ++f)
+        bq[s][f] = load_w(wrap(nxt + krot, nks) * kstride + frag_of(f) * kWave);
       load_scales(s, wrap(nxt + krot, nks));
       asm volatile("" ::: "memory");
     }
@@ -412,10 +448,13 @@ __device__ __forceinline__ void frag_gemm_body(
   // so the 2-byte writes are conflict-free), and is stored back as 16-byte
   // vectors: whole 128-byte row pieces instead of 2-byte scattered stores.
   // Rows past the segment end are neither staged nor stored.
-  constexpr int kEpiStride = GATE_UP ? 40 : 72;  // bf16 per staged row (32 or 64 + 8)
+  // bf16 per staged row: the wave's output columns (gate/up: 32, or 16 when
+  // tall; down: 64, or 32 when tall) + 8
+  constexpr int kEpiStride = (GATE_UP ? 8 * FR : 16 * FR) + 8;
 #pragma unroll
-  for (int i = 0; i < kMsub; ++i) {
-    if (i >= nlive) break;
+  for (int i = 0; i < MS; ++i) {
+    if (TALL ? i >= nlive : false) continue;
+    if (!TALL && i >= nlive) break;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int rr = 4 * (lane >> 4) + q;
@@ -423,13 +462,13 @@ __device__ __forceinline__ void frag_gemm_body(
       if (r >= valid) continue;
       if (GATE_UP) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+        for (int f = 0; f < FR / 2; ++f)
           epi[rr * kEpiStride + f * 16 + (lane & 15)] =
-              (uint16_t)f32_to_bf16(silu_f(acc[i][f][q]) * acc[i][f + 2][q]);
+              (uint16_t)f32_to_bf16(silu_f(acc[i][f][q]) * acc[i][f + FR / 2][q]);
       } else {
         const float sc = tile_scale ? tile_scale[r] : 1.0f;
 #pragma unroll
-        for (int f = 0; f < kFrags; ++f)
+        for (int f = 0; f < FR; ++f)
           epi[rr * kEpiStride + f * 16 + (lane & 15)] = (uint16_t)f32_to_bf16(sc * acc[i][f][q]);
       }
     }
@@ -438,15 +477,23 @@ __device__ __forceinline__ void frag_gemm_body(
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     if (GATE_UP) {
       // a is written in the down GEMM's activation fragment order: block
-      // (m-tile, m-subtile i, K-step ct) of 64 lanes x 8 values, where lane
-      // L = row%16 + 16*(col%32 / 8) holds columns 8*(col%32 / 8) .. +8
+      // (128-row m-tile, m-subtile, K-step ct) of 64 lanes x 8 values, where
+      // lane L = row%16 + 16*(col%32 / 8) holds columns 8*(col%32 / 8) .. +8
+      // (a tall tile's m-subtiles 8..15 are those of the next m-tile, and
+      // its wave fills lanes 32 hsel .. 32 hsel + 31 of the block)
       const int row = lane & 15;
-      if (i * 16 + row < valid) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&epi[row * kEpiStride + 8 * (lane >> 4)]);
-        uint16_t* blk = Out + ((mt_glob * kMsub + i) * (int64_t)(Nout / 32) + ct) * (kWave * 8);
-        epi_store<true>(reinterpret_cast<u32x4_t*>(blk) + lane, v);
+      uint16_t* blk = Out + ((mt_glob * kMsub + i) * (int64_t)(Nout / 32) + ct) * (kWave * 8);
+      if (!TALL) {
+        if (i * 16 + row < valid) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&epi[row * kEpiStride + 8 * (lane >> 4)]);
+          epi_store<true>(reinterpret_cast<u32x4_t*>(blk) + lane, v);
+        }
+      } else if (lane < 32 && i * 16 + row < valid) {
+        const int c8 = lane >> 4;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&epi[row * kEpiStride + 8 * c8]);
+        epi_store<true>(reinterpret_cast<u32x4_t*>(blk) + row + 16 * (2 * hsel + c8), v);
       }
-    } else {
+    } else if (!TALL) {
       // 16 rows x 64 columns = 128 pieces of 8 columns, two per lane
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -456,6 +503,14 @@ __device__ __forceinline__ void frag_gemm_body(
           epi_store<false>(reinterpret_cast<u32x4_t*>(Out + (row_base + i * 16 + row) * Nout + ct * 64) + c8, v);
         }
       }
+    } else {
+      // tall: 16 rows x 32 columns (64 ct + 32 hsel ..) = 64 pieces, one per lane
+      const int row = lane >> 2, c8 = lane & 3;
+      if (i * 16 + row < valid) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&epi[row * kEpiStride + 8 * c8]);
+        epi_store<false>(reinterpret_cast<u32x4_t*>(Out + (row_base + i * 16 + row) * Nout +
+                                                    ct * 64 + 32 * hsel) + c8, v);
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   }
@@ -463,20 +518,23 @@ __device__ __forceinline__ void frag_gemm_body(
 
 // Two waves per SIMD: an 8-wave workgroup needs them, a 4-wave one gets two
 // workgroups per CU; the register budget is 256 per lane either way.
-template <bool GATE_UP, int NW, bool F8>
+template <bool GATE_UP, int NW, bool F8, bool TALL>
 __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
     const uint16_t* __restrict__ A, const void* __restrict__ Wf, const float* __restrict__ Wsc,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ counts, int G,
     int Kdim, int Nw /* weight rows per group */, int Nout, const float* __restrict__ row_scale,
     uint16_t* __restrict__ Out, int64_t capacity, int32_t* __restrict__ dev_error) {
-  __shared__ __attribute__((aligned(16))) u32x4_t As[kStages][kStageBlocks][kWave];
+  using Shape = FragShape<TALL>;
+  constexpr int BMR = Shape::kRows;
+  __shared__ __attribute__((aligned(16))) u32x4_t As[kStages][Shape::kSB][kWave];
   __shared__ __attribute__((aligned(16))) uint16_t Epi[NW][16 * 72];  // per-wave output staging
 
-  const int n_ct = Nw / 64;              // column tiles per group
-  const int n_cb = (n_ct + NW - 1) / NW;  // workgroups per m-tile
+  const int n_ct = Nw / 64;               // column tiles per group
+  const int n_wt = TALL ? 2 * n_ct : n_ct;  // wave tiles per group (a tall wave: half a tile)
+  const int n_cb = (n_wt + NW - 1) / NW;  // workgroups per m-tile
   const int pid = xcd_remap(blockIdx.x);
   int g, mt, cb, mt_base;
-  if (!decode_tile(pid, counts, G, n_cb, g, mt, cb, &mt_base)) return;
+  if (!decode_tile<BMR>(pid, counts, G, n_cb, g, mt, cb, &mt_base)) return;
   // the same in every lane: say so, so that addresses built from them stay scalar
   g = __builtin_amdgcn_readfirstlane(g);
   mt = __builtin_amdgcn_readfirstlane(mt);
@@ -488,18 +546,20 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
     if ((threadIdx.x & 63) == 0) raise_error(dev_error, MOE_DEVERR_ROW_RANGE);
     return;
   }
-  const int m0 = mt * kBM;
-  const int valid = min(kBM, nrows - m0);
+  const int m0 = mt * BMR;
+  const int valid = min(BMR, nrows - m0);
   if (valid <= 0) return;
   const int64_t row_base = (int64_t)seg0 + m0;
   const int nlive = (valid + 15) >> 4;   // m-subtiles holding real rows
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // the last column block may hold fewer than NW tiles: the spare
+  // the last column block may hold fewer than NW wave tiles: the spare
   // waves stream a real tile and store nothing
-  const bool ct_ok = cb * NW + w < n_ct;
-  const int ct = ct_ok ? cb * NW + w : n_ct - 1;
+  const bool ct_ok = cb * NW + w < n_wt;
+  const int wt = ct_ok ? cb * NW + w : n_wt - 1;
+  const int ct = TALL ? wt >> 1 : wt;
+  const int hsel = TALL ? wt & 1 : 0;
   const int nks = Kdim / 32;
 
   // this wave's weight stream: step ks, fragment f at wp[ks * kstride + f * 64]
@@ -508,7 +568,8 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
   const WFrag<F8>* wp = reinterpret_cast<const WFrag<F8>*>(Wf) +
                         ((int64_t)g * nks * n_ct + ct) * (kFrags * kWave) + lane;
   // FP8: the scale rows ([G][Nw/128][Kdim/128]) of this tile's gate and up
-  // rows (w13: gate rows 32 ct.., up rows Nw/2 + 32 ct..; w2: rows 64 ct..)
+  // rows (w13: gate rows 32 ct.., up rows Nw/2 + 32 ct..; w2: rows 64 ct..);
+  // half a tile lies in the same 128-row scale block as the whole
   const int nkb = Kdim / 128, nrb = Nw / 128;
   const float* sc_g = nullptr;
   const float* sc_u = nullptr;
@@ -520,12 +581,13 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
   }
   // the activation DMA: this wave fills LDS blocks kDmaPerWave*w .. of a
   // stage; block b is m-subtile b / kChunkSteps, K-step b % kChunkSteps
-  constexpr int kDmaPerWave = kStageBlocks / NW;
+  constexpr int kDmaPerWave = Shape::kSB / NW;
   // gate/up reads the permuted rows (row-major); down reads the gate/up
-  // output, which that kernel wrote in fragment order per m-tile.  Source of
-  // block q: a_base + a_uoff[q] (+ the chunk's offset) in elements, uniform,
-  // plus a_voff[q] bytes per lane
-  const int64_t mt_glob = (int64_t)mt_base + mt;
+  // output, which that kernel wrote in fragment order per 128-row m-tile
+  // (a tall tile's second half is the next m-tile).  Source of block q:
+  // a_base + a_uoff[q] (+ the chunk's offset) in elements, uniform, plus
+  // a_voff[q] bytes per lane
+  const int64_t mt_glob = (int64_t)mt_base + (int64_t)mt * (BMR / kBM);
   const uint16_t* a_base =
       GATE_UP ? A + row_base * Kdim : A + mt_glob * kMsub * (int64_t)nks * (kWave * 8);
   int64_t a_uoff[kDmaPerWave];
@@ -545,8 +607,8 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
   }
   const int a_chunk_stride = GATE_UP ? kChunkSteps * 32 : kChunkSteps * kWave * 8;
 
-  // down: the m-tile's row scales, staged in LDS once for the epilogue
-  __shared__ float rs[kBM];
+  // down: the tile's row scales, staged in LDS once for the epilogue
+  __shared__ float rs[BMR];
   const float* tile_scale = nullptr;
   if (!GATE_UP && row_scale) {
     for (int r = threadIdx.x; r < valid; r += NW * kWave) rs[r] = row_scale[row_base + r];
@@ -554,8 +616,8 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
     tile_scale = rs;
   }
 
-  // an expert whose rows fit in one m-tile reads each weight byte once
-  const bool once = nrows <= kBM;
+  // an expert whose rows fit in one tile reads each weight byte once
+  const bool once = nrows <= BMR;
   // K rotation for experts read once, so that the experts in flight do not
   // all read the same K offsets (the same HBM channels) at the same time:
   // per expert with 8-wave workgroups (the expert's workgroups stay in step
@@ -576,17 +638,19 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
   bool prio = false;
   if (NW == 4 && once) {
     bool fits = true;
-    for (int e = lane; e < G; e += kWave) fits = fits && counts[e] <= kBM;
+    for (int e = lane; e < G; e += kWave) fits = fits && counts[e] <= BMR;
     prio = __ballot(!fits) == 0;
   }
   if (once)
-    frag_gemm_body<GATE_UP, true, NW, F8>(As, wp, kstride, sc_g, sc_u, a_base, a_uoff, a_voff, a_chunk_stride, w, lane, nks, nlive, valid,
-                                      ct, ct_ok, row_base, mt_glob, Nout, tile_scale, Out, crot, prio,
-                                      Epi[w]);
+    frag_gemm_body<GATE_UP, true, NW, F8, TALL>(As, wp, kstride, sc_g, sc_u, a_base, a_uoff, a_voff,
+                                                a_chunk_stride, w, lane, nks, nlive, valid, ct, hsel,
+                                                ct_ok, row_base, mt_glob, Nout, tile_scale, Out,
+                                                crot, prio, Epi[w]);
   else
-    frag_gemm_body<GATE_UP, false, NW, F8>(As, wp, kstride, sc_g, sc_u, a_base, a_uoff, a_voff, a_chunk_stride, w, lane, nks, nlive, valid,
-                                       ct, ct_ok, row_base, mt_glob, Nout, tile_scale, Out, crot, false,
-                                       Epi[w]);
+    frag_gemm_body<GATE_UP, false, NW, F8, TALL>(As, wp, kstride, sc_g, sc_u, a_base, a_uoff,
+                                                 a_voff, a_chunk_stride, w, lane, nks, nlive, valid,
+                                                 ct, hsel, ct_ok, row_base, mt_glob, Nout,
+                                                 tile_scale, Out, crot, false, Epi[w]);
 }
 
 // Packing: one thread per 16-byte vector of the source (coalesced reads),
@@ -765,17 +829,35 @@ int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32
   // fills an m-tile (each activation tile then serves 8 column tiles), else
   // 4 (smaller workgroups balance uneven segments).  The down projection
   // uses 8 only for means between one and two m-tiles; with many m-tiles per
-  // expert the smaller workgroups balance better there.
+  // expert the smaller workgroups balance better there.  With bf16 weights,
+  // segments averaging kTallMin..2*kBM-1 rows (about half of them one m-tile
+  // long, half two) use the 8-wave tall tiles in both stages instead, so that
+  // no expert streams its weights twice (same-box A/B on the deepseek-shape
+  // layer, T=4096, H=7168, 256 experts, I=2048: gate/up 2.75 -> 2.58 ms, down
+  // unchanged, the layer 4.86 -> 4.71 ms).  With FP8 weights a tall wave's
+  // half-size fragments keep too few bytes in flight (the same A/B: gate/up
+  // 2.34 -> 2.58 ms), so they keep the 128-row tiles.
   const int64_t mean_x = capacity / G;  // mean rows per group, rounded down
   const bool wide = mean_x >= kBM;
   const bool wide_down = wide && mean_x < 2 * kBM;
-  if (flags & MOE_FFN_GATE_UP) {
+  const bool tall = packed && !f8 && mean_x >= kTallMin && mean_x < 2 * kBM;
+  const int64_t m_tiles_tall = (capacity + 2 * kBM - 1) / (2 * kBM) + G;
+  auto grid_tall = [&](int64_t n_tiles) {
+    return (m_tiles_tall * n_tiles + grid_unit - 1) / grid_unit * grid_unit;
+  };
+  if ((flags & MOE_FFN_GATE_UP) && tall) {
+    const int64_t blocks = grid_tall((2 * (2 * I / 64) + 7) / 8);
+    if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((frag_gemm_kernel<true, 8, false, true>), dim3((unsigned)blocks),
+                       dim3(8 * kWave), 0, stream, x, w13, w13s, cu_seqlens, counts, G, H, 2 * I, I,
+                       nullptr, act, capacity, dev_error);
+  } else if (flags & MOE_FFN_GATE_UP) {
     if (packed) {
       const int nw = wide ? 8 : 4;
       const int64_t blocks = grid_for((2 * I / 64 + nw - 1) / nw);
       if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
 #define MOE_FRAG_GU(NW, F8)                                                                  \
-  hipLaunchKernelGGL((frag_gemm_kernel<true, NW, F8>), dim3((unsigned)blocks), dim3(NW * kWave), \
+  hipLaunchKernelGGL((frag_gemm_kernel<true, NW, F8, false>), dim3((unsigned)blocks), dim3(NW * kWave), \
                      0, stream, x, w13, w13s, cu_seqlens, counts, G, H, 2 * I, I, nullptr, act,  \
                      capacity, dev_error)
       if (f8) {
@@ -792,13 +874,19 @@ int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32
                          capacity, dev_error);
     }
   }
-  if (flags & MOE_FFN_DOWN) {
+  if ((flags & MOE_FFN_DOWN) && tall) {
+    const int64_t blocks = grid_tall((2 * (H / 64) + 7) / 8);
+    if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((frag_gemm_kernel<false, 8, false, true>), dim3((unsigned)blocks),
+                       dim3(8 * kWave), 0, stream, act, w2, w2s, cu_seqlens, counts, G, I, H, H,
+                       row_scale, y, capacity, dev_error);
+  } else if (flags & MOE_FFN_DOWN) {
     if (packed) {
       const int nw = wide_down ? 8 : 4;
       const int64_t blocks = grid_for((H / 64 + nw - 1) / nw);
       if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
 #define MOE_FRAG_DN(NW, F8)                                                                   \
-  hipLaunchKernelGGL((frag_gemm_kernel<false, NW, F8>), dim3((unsigned)blocks), dim3(NW * kWave), \
+  hipLaunchKernelGGL((frag_gemm_kernel<false, NW, F8, false>), dim3((unsigned)blocks), dim3(NW * kWave), \
                      0, stream, act, w2, w2s, cu_seqlens, counts, G, I, H, H, row_scale, y,       \
                      capacity, dev_error)
       if (f8) {

@@ -735,3 +735,40 @@ def test_ffn_packed_weights(H, I, T):
     y2 = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13, w2, p.w_perm)
     used = int(ref["cu_seqlens"][-1])
     assert rel_err(bf16_bits_to_f32(host_bits(y[:used])), bf16_bits_to_f32(host_bits(y2[:used]))) < 1e-2
+
+
+def test_ffn_tall_tiles_edges():
+    """Segments averaging 96..255 rows take the tall tiles (256 rows per
+    workgroup, half a column tile per wave): segments of exactly 128, 129,
+    255, 256 and 257 rows (the last spills into a second tall tile), a
+    single row, an empty expert, and a down projection whose wave tiles do
+    not fill the last workgroup (H / 32 = 12 of 16); every expert against
+    the oracle per row and element, with BF16 and with FP8 weights."""
+    sizes = [128, 129, 255, 256, 257, 1, 0]
+    G, H, I = len(sizes), 384, 256
+    cfg = workloads.MoEConfig("t", 41, T=sum(sizes), H=H, E=G, K=1, I=I)
+    assert 96 <= sum(sizes) // G < 256
+    idx = np.concatenate([np.full(n, e, np.int32) for e, n in enumerate(sizes)])[:, None]
+    idx = np.random.default_rng(3).permutation(idx)
+    w = np.random.default_rng(4).uniform(0.5, 1.5, idx.shape).astype(np.float32)
+    hid = workloads.hidden(cfg)
+    w13, w2, host_w = stacked_weights(cfg)
+    ref = oracle.permute(idx, w, hid, G, 0, False)
+    p = ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), G)
+    w13p, w2p = ops.moe_pack_ffn_weights(w13, w2)
+    y = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13p, w2p, p.w_perm,
+                            flags=ops.MOE_FFN_ALL | ops.MOE_FFN_PACKED_WEIGHTS)
+    q13, s13, q2, s2 = ops.moe_pack_ffn_weights_fp8(w13, w2)
+    y8 = ops.moe_grouped_ffn_fp8(p.x_perm, p.cu_seqlens, p.counts, q13, s13, q2, s2, p.w_perm)
+    torch.cuda.synchronize()
+    for e in range(G):
+        n, r0 = int(ref["counts"][e]), int(ref["cu_seqlens"][e])
+        if n == 0:
+            continue
+        x = oracle.bf16_bits_to_f64(ref["x_perm"][r0:r0 + n])
+        rs = ref["w_perm"][r0:r0 + n, None].astype(np.float64)
+        check_rows(bf16_bits_to_f32(host_bits(y[r0:r0 + n])),
+                   oracle.expert_ffn(x, *host_w[e]) * rs, FFN_TOL, what=f"bf16 expert {e} ({n} rows)")
+        deq = [oracle.quantize_weight_blocks(m)[2] for m in host_w[e]]
+        check_rows(bf16_bits_to_f32(host_bits(y8[r0:r0 + n])),
+                   oracle.expert_ffn(x, *deq) * rs, FFN_TOL, what=f"fp8w expert {e} ({n} rows)")

@@ -120,25 +120,35 @@ __device__ __forceinline__ void lds_barrier() {
 // across lds_barrier(), whose empty asm statements clobber memory.
 // The source address is a wave-uniform base (SGPRs) plus a 32-bit per-lane
 // byte offset, which keeps the per-lane state of the DMA small.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const void* l) {
-  const uint32_t lds =
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)l;
+// (dma16_at takes the LDS byte address itself.)
+__device__ __forceinline__ void dma16_at(const void* sbase, uint32_t voff, uint32_t lds) {
   // one wait state between the SALU write of M0 and the DMA that reads it
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "m0");
 }
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const void* l) {
+  dma16_at(sbase, voff, (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)l);
+}
 
 // The same for 4 bytes per lane (global_load_lds_dword: 64 lanes x 4 bytes
 // to LDS at M0 + 4 * lane), for small per-row tables such as row scales.
-__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, const void* l) {
-  const uint32_t lds =
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)l;
+__device__ __forceinline__ void dma4_at(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "m0");
+}
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, const void* l) {
+  dma4_at(sbase, voff, (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)l);
+}
+
+// The LDS byte address of a __shared__ object (its generic address cast back
+// once, outside any loop, so that no per-use null check is generated).
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 }  // namespace moe

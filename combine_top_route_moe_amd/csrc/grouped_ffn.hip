@@ -38,6 +38,7 @@
 // Workgroups past the last tile exit at once.  MFMA sub-tiles lying wholly
 // past the segment's last row are skipped.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -653,6 +654,380 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
                                                  tile_scale, Out, crot, false, Epi[w]);
 }
 
+// ---------------------------------------------------------------------------
+// The tall tiles, streamed.  In the one-tile-per-workgroup form every tile
+// boundary stalls the CU's memory streams: the waves wait for all their
+// loads (the weight prefetch runs kPrefetch steps past the end), decode the
+// next tile from the counts in memory, store their outputs, and only then
+// start the next tile's weight and activation streams, whose first bytes
+// land a memory latency later.  With weight-streaming tiles of about 50 us
+// that is several per cent of the time.
+//
+// Here a persistent workgroup walks its tiles (virtual blocks b, b + grid,
+// ..., in increasing tile order) and its streams run on across each
+// boundary: in a tile's last kPrefetch K-steps the weight refills fetch the
+// next tile's first steps, and the DMAs of its last kStages-1 chunks fill the
+// ring with the next tile's first chunks (the ring carries on slot after
+// slot), so the next tile's data is in flight while this tile's epilogue
+// runs.  The tile table (per group: tiles up to and including it, 128-row
+// m-tiles before it, segment start, row count) is built once per workgroup
+// in LDS, so a decode issues no memory load.  The down projection's row
+// scales arrive by DMA with each tile's first chunk, in a double buffer.
+//
+// Wait accounting, per wave (loads complete in issue order; stores count in
+// vmcnt too):
+//  - within a tile as in the one-tile kernel: at a chunk's barrier at least
+//    kAfterDma weight loads were issued after that chunk's DMA;
+//  - the next tile's chunk 0 goes out with this tile's chunk L-1 (L the
+//    last), followed by kAfterDma weight refills and then the epilogue's
+//    stores: exactly kStreamStores of them, since every m-subtile issues one
+//    buffer store whatever it holds (lanes with nothing to write aim it
+//    past the buffer's range, where the hardware drops it).  So the next
+//    tile's first chunk waits for vmcnt(kAfterDma + kStreamStores) and does
+//    not wait for the stores just issued;
+//  - its chunk 1 goes out with chunk L, followed by refills, the stores and
+//    the next tile's own refills: more than kAfterDma.
+// After the workgroup's last tile the refills and DMAs re-read its last step
+// and chunk, as the one-tile kernel does, which keeps these counts.
+constexpr int kStreamMaxG = 1024;                     // groups the LDS tile table holds
+constexpr int kStreamStores = FragShape<true>::kMs;   // epilogue stores per wave and tile
+constexpr uint32_t kBufferOob = 0x80000000u;          // a buffer offset past every range
+
+// A raw buffer (stride 0) over `bytes` bytes at p, p wave-uniform: offsets
+// at or past `bytes` are dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_buffer(uint16_t* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, bytes, 0x00020000);
+}
+
+// One tall tile as a wave of the streamed kernel sees it: wave-uniform but
+// for a_voff.
+struct TallTile {
+  int ok;                   // a tile is assigned
+  int nlive, valid;         // m-subtiles holding rows, rows
+  int ct, hsel, ct_ok;      // column tile, its half, whether this wave's half exists
+  int nt, crot;             // weights read once (streamed past the caches), K rotation
+  int64_t row_base, mt_glob;
+  const u32x4_t* wp;        // the wave's weight stream at lane 0, K-step 0
+  const uint16_t* a_base;   // the activation DMA's base
+  uint32_t a_voff[FragShape<true>::kSB / 8];  // gate/up: per-lane byte offsets of the DMA blocks
+};
+
+// Decode virtual block vb into t (t.ok = 0 past the last tile) from the LDS
+// tile table.
+template <bool GATE_UP>
+__device__ __forceinline__ void tall_decode(TallTile& t, int vb, int nvirt, const int* t_incl,
+                                            const int* t_m128, const int* t_seg, const int* t_cnt,
+                                            int G, int n_cb, int n_wt, int n_ct, int nks, int Kdim,
+                                            const uint16_t* A, const u32x4_t* Wf, int w, int lane) {
+  t.ok = 0;
+  if (vb >= nvirt) return;
+  const int pid = xcd_remap(vb);
+  int g = -1;
+  for (int base = 0; base < G; base += kWave) {
+    const int e = base + lane;
+    const uint64_t hit = __ballot(e < G && pid < t_incl[e]);
+    if (hit) {
+      g = base + __ffsll((unsigned long long)hit) - 1;
+      break;
+    }
+  }
+  if (g < 0) return;
+  g = __builtin_amdgcn_readfirstlane(g);
+  const int excl = __builtin_amdgcn_readfirstlane(g > 0 ? t_incl[g - 1] : 0);
+  const int nrows = __builtin_amdgcn_readfirstlane(t_cnt[g]);
+  const int seg0 = __builtin_amdgcn_readfirstlane(t_seg[g]);
+  const int m128 = __builtin_amdgcn_readfirstlane(t_m128[g]);
+  constexpr int BMR = FragShape<true>::kRows;
+  const int mtiles = (nrows + BMR - 1) / BMR;
+  const int local = pid - excl;
+  const int cb = local / mtiles, mt = local - cb * mtiles;
+  t.ok = 1;
+  t.valid = min(BMR, nrows - mt * BMR);
+  t.nlive = (t.valid + 15) >> 4;
+  t.row_base = (int64_t)seg0 + mt * BMR;
+  t.mt_glob = (int64_t)m128 + (int64_t)mt * (BMR / kBM);
+  int wt = cb * 8 + w;
+  t.ct_ok = wt < n_wt;
+  if (!t.ct_ok) wt = n_wt - 1;   // a spare wave streams a real half tile and stores nothing
+  t.ct = wt >> 1;
+  t.hsel = wt & 1;
+  t.nt = nrows <= BMR;
+  // the one-tile kernel's K rotation for experts read once (per expert)
+  t.crot = t.nt ? (int)((((uint32_t)g * 977u) * 2654435761u) >> 8) % (nks / kChunkSteps) : 0;
+  t.wp = Wf + ((int64_t)g * nks * n_ct + t.ct) * (kFrags * kWave);
+  t.a_base = GATE_UP ? A + t.row_base * Kdim : A + t.mt_glob * kMsub * (int64_t)nks * (kWave * 8);
+  if (GATE_UP) {
+#pragma unroll
+    for (int q = 0; q < FragShape<true>::kSB / 8; ++q) {
+      const int b = w * (FragShape<true>::kSB / 8) + q;
+      const int ms = b / kChunkSteps, sub = b % kChunkSteps;
+      const int r = min(ms * 16 + (lane & 15), t.valid - 1);   // rows past the end re-read the last
+      t.a_voff[q] = (uint32_t)(r * Kdim + sub * 32 + 8 * (lane >> 4)) * 2u;
+    }
+  }
+}
+
+template <bool GATE_UP>
+__global__ void __launch_bounds__(8 * kWave, 2) tall_stream_kernel(
+    const uint16_t* __restrict__ A, const void* __restrict__ Wf_,
+    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ counts, int G,
+    int Kdim, int Nw /* weight rows per group */, int Nout, const float* __restrict__ row_scale,
+    uint16_t* __restrict__ Out, int64_t capacity, int32_t* __restrict__ dev_error, int nvirt) {
+  using Shape = FragShape<true>;
+  constexpr int NW = 8, MS = Shape::kMs, FR = Shape::kFr, BMR = Shape::kRows;
+  constexpr int kDmaPerWave = Shape::kSB / NW;
+  __shared__ __attribute__((aligned(16))) u32x4_t As[kStages][Shape::kSB][kWave];
+  __shared__ __attribute__((aligned(16))) uint16_t Epi[NW][16 * 72];   // per-wave output staging
+  __shared__ float rs[2][BMR];
+  __shared__ int t_incl[kStreamMaxG], t_m128[kStreamMaxG], t_seg[kStreamMaxG], t_cnt[kStreamMaxG];
+
+  const u32x4_t* Wf = static_cast<const u32x4_t*>(Wf_);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_ct = Nw / 64, n_wt = 2 * n_ct, n_cb = (n_wt + NW - 1) / NW;
+  const int nks = Kdim / 32, nch = nks / kChunkSteps;
+  const int kstride = n_ct * kFrags * kWave;
+
+  // the tile table: a group whose segment leaves [0, capacity) gets no tile
+  // (and raises the error); the 128-row m-tile count, which places the
+  // activation rows, counts every group as the one-tile kernel does
+  if (w == 0) {
+    int carry = 0, carry128 = 0;
+    for (int base = 0; base < G; base += kWave) {
+      const int e = base + lane;
+      int c = 0, s0 = 0;
+      if (e < G) {
+        c = max(counts[e], 0);
+        s0 = cu_seqlens[e];
+      }
+      const int m128 = (c + kBM - 1) / kBM;
+      if (c > 0 && ((int64_t)s0 + c > capacity || s0 < 0)) {
+        raise_error(dev_error, MOE_DEVERR_ROW_RANGE);
+        c = 0;
+      }
+      int incl = ((c + BMR - 1) / BMR) * n_cb, incl128 = m128;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, kWave), y128 = __shfl_up(incl128, off, kWave);
+        if (lane >= off) {
+          incl += y;
+          incl128 += y128;
+        }
+      }
+      incl += carry;
+      incl128 += carry128;
+      if (e < G) {
+        t_incl[e] = incl;
+        t_m128[e] = incl128 - m128;
+        t_seg[e] = s0;
+        t_cnt[e] = c;
+      }
+      carry = __shfl(incl, 63, kWave);
+      carry128 = __shfl(incl128, 63, kWave);
+    }
+  }
+  __syncthreads();
+
+  TallTile cur, nxt;
+  int vb = blockIdx.x;
+  tall_decode<GATE_UP>(cur, vb, nvirt, t_incl, t_m128, t_seg, t_cnt, G, n_cb, n_wt, n_ct, nks,
+                       Kdim, A, Wf, w, lane);
+  if (!cur.ok) return;   // the whole workgroup
+
+  const uint32_t as_lds = lds_addr(&As[0][0][0]), rs_lds = lds_addr(&rs[0][0]);
+  auto wrap = [](int x, int n) { return x >= n ? x - n : x; };
+  // the packed fragment of this wave's f-th B operand (see frag_gemm_body)
+  auto frag_of = [](const TallTile& t, int f) {
+    return GATE_UP ? (f == 0 ? t.hsel : t.hsel + 2) : 2 * t.hsel + f;
+  };
+  // LDS blocks of m-subtiles past the segment end are never read: skip them
+  auto issue_chunk = [&](const TallTile& t, int chunk, int slot) {
+    const int64_t coff = (int64_t)wrap(chunk + t.crot, nch) *
+                         (GATE_UP ? kChunkSteps * 32 : kChunkSteps * kWave * 8);
+#pragma unroll
+    for (int q = 0; q < kDmaPerWave; ++q) {
+      const int b = w * kDmaPerWave + q;
+      if (b / kChunkSteps >= t.nlive) break;
+      const int64_t uoff =
+          GATE_UP ? 0 : ((int64_t)(b / kChunkSteps) * nks + b % kChunkSteps) * (kWave * 8);
+      const uint32_t voff = GATE_UP ? t.a_voff[q] : (uint32_t)lane * 16u;
+      dma16_at(t.a_base + uoff + coff, voff, as_lds + (uint32_t)((slot * Shape::kSB + b) * kWave * 16));
+    }
+  };
+  // down: the tile's row scales into rs[buf], rows past the end re-reading the last
+  auto issue_scales = [&](const TallTile& t, int buf) {
+    if (!GATE_UP && row_scale && w < BMR / kWave) {
+      const int r = min(w * kWave + lane, t.valid - 1);
+      dma4_at(row_scale + t.row_base, (uint32_t)r * 4u, rs_lds + (uint32_t)((buf * BMR + w * kWave) * 4));
+    }
+  };
+  u32x4_t bq[kPrefetch][FR];
+  auto load_step = [&](const TallTile& t, int step, int s) {
+    const u32x4_t* p = t.wp + (int64_t)wrap(step + t.crot * kChunkSteps, nks) * kstride + lane;
+    if (t.nt) {
+#pragma unroll
+      for (int f = 0; f < FR; ++f) bq[s][f] = __builtin_nontemporal_load(p + frag_of(t, f) * kWave);
+    } else {
+#pragma unroll
+      for (int f = 0; f < FR; ++f) bq[s][f] = p[frag_of(t, f) * kWave];
+    }
+  };
+
+  // the first tile's prologue: scales, kStages-1 chunks, kPrefetch weight steps
+  asm volatile("" ::: "memory");
+  issue_scales(cur, 0);
+#pragma unroll
+  for (int c = 0; c < kStages - 1; ++c) issue_chunk(cur, min(c, nch - 1), c);
+#pragma unroll
+  for (int s = 0; s < kPrefetch; ++s) load_step(cur, s, s);
+  asm volatile("" ::: "memory");
+
+  constexpr int kAfterDma = (kStages - 1) * kChunkSteps * FR;
+  static_assert(kAfterDma <= kPrefetch * FR, "prologue count");
+  static_assert(kPrefetch == (kStages - 1) * kChunkSteps, "the last block's chunks are the ring's lookahead");
+  static_assert(kAfterDma + kStreamStores < 64, "vmcnt range");
+  int stage = kStages - 1;   // ring slot of the current chunk (the prologue filled 0 ..)
+  int par = 0;               // row-scale buffer of the current tile
+  bool first = true;
+  f32x4_t acc[MS][FR];
+
+  // one K-step of the current tile; `tail`: the last kPrefetch steps, whose
+  // lookahead loads belong to the next tile (or, after the last, re-read)
+  auto step = [&](int ks, int s, bool tail) {
+    if (s % kChunkSteps == 0) {
+      const int chunk = ks / kChunkSteps;
+      stage = stage + 1 == kStages ? 0 : stage + 1;
+      if (chunk == 0 && !first)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAfterDma + kStreamStores));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAfterDma));
+      lds_barrier();
+      // the slot kStages-1 ahead was last read in the previous chunk
+      const int slot = stage + kStages - 1 >= kStages ? stage - 1 : stage + kStages - 1;
+      const int ahead = chunk + kStages - 1;
+      asm volatile("" ::: "memory");
+      if (!tail) {
+        issue_chunk(cur, ahead, slot);
+      } else if (nxt.ok) {
+        if (ahead == nch) issue_scales(nxt, par ^ 1);
+        issue_chunk(nxt, ahead - nch, slot);
+      } else {
+        issue_chunk(cur, nch - 1, slot);
+      }
+      asm volatile("" ::: "memory");
+    }
+    const int sub = ks % kChunkSteps;
+    bf16x8_t bfr[FR];
+#pragma unroll
+    for (int f = 0; f < FR; ++f) bfr[f] = __builtin_bit_cast(bf16x8_t, bq[s][f]);
+#pragma unroll
+    for (int g8 = 0; g8 < MS; g8 += 8) {
+      if (g8 >= cur.nlive) continue;
+      u32x4_t a[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[stage][(g8 + i) * kChunkSteps + sub][lane];
+      if (cur.nlive > g8 + 4) {
+#pragma unroll
+        for (int i = 4; i < 8; ++i) a[i] = As[stage][(g8 + i) * kChunkSteps + sub][lane];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (g8 + i >= cur.nlive) continue;
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, a[i]);
+#pragma unroll
+        for (int f = 0; f < FR; ++f)
+          acc[g8 + i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[f], acc[g8 + i][f], 0, 0, 0);
+      }
+    }
+    asm volatile("" ::: "memory");
+    if (!tail)
+      load_step(cur, ks + kPrefetch, s);
+    else if (nxt.ok)
+      load_step(nxt, ks + kPrefetch - nks, s);
+    else
+      load_step(cur, nks - 1, s);
+    asm volatile("" ::: "memory");
+  };
+
+  constexpr int kEpiStride = (GATE_UP ? 8 * FR : 16 * FR) + 8;
+  uint16_t* epi = Epi[w];
+  for (;;) {
+    tall_decode<GATE_UP>(nxt, vb + (int)gridDim.x, nvirt, t_incl, t_m128, t_seg, t_cnt, G, n_cb,
+                         n_wt, n_ct, nks, Kdim, A, Wf, w, lane);
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+      for (int f = 0; f < FR; ++f) acc[i][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int ks0 = 0; ks0 < nks - kPrefetch; ks0 += kPrefetch) {
+#pragma unroll
+      for (int s = 0; s < kPrefetch; ++s) step(ks0 + s, s, false);
+    }
+#pragma unroll
+    for (int s = 0; s < kPrefetch; ++s) step(nks - kPrefetch + s, s, true);
+
+    // epilogue, as in the one-tile kernel, but every m-subtile issues
+    // exactly one 16-byte buffer store (see the wait accounting above)
+    const bool use_scale = !GATE_UP && row_scale != nullptr;
+    // gate/up: the tile's 16 m-subtile blocks of the activation layout;
+    // down: the tile's rows of the output (rows past the end are out of range)
+    const int nblk = Nout / 32;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        GATE_UP ? wave_buffer(Out + cur.mt_glob * kMsub * (int64_t)nblk * (kWave * 8),
+                              MS * nblk * kWave * 8 * 2)
+                : wave_buffer(Out + cur.row_base * Nout, cur.valid * Nout * 2);
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      uint32_t off = kBufferOob;
+      if (i < cur.nlive && cur.ct_ok) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int rr = 4 * (lane >> 4) + q;
+          const int r = i * 16 + rr;
+          if (r >= cur.valid) continue;
+          if (GATE_UP) {
+            epi[rr * kEpiStride + (lane & 15)] =
+                (uint16_t)f32_to_bf16(silu_f(acc[i][0][q]) * acc[i][1][q]);
+          } else {
+            const float sc = use_scale ? rs[par][r] : 1.0f;
+#pragma unroll
+            for (int f = 0; f < FR; ++f)
+              epi[rr * kEpiStride + f * 16 + (lane & 15)] = (uint16_t)f32_to_bf16(sc * acc[i][f][q]);
+          }
+        }
+        // the staging area is the wave's own: its LDS operations run in
+        // order, and the fences keep the compiler from moving them across
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        if (GATE_UP) {
+          // fragment order of the down GEMM's activations: block (m-subtile i,
+          // K-step ct), lane L = row + 16 (2 hsel + c8) holding 8 columns
+          const int row = lane & 15, c8 = lane >> 4;
+          if (lane < 32 && i * 16 + row < cur.valid) {
+            v = *reinterpret_cast<const u32x4_t*>(&epi[row * kEpiStride + 8 * c8]);
+            off = (uint32_t)(((i * nblk + cur.ct) * kWave + row + 16 * (2 * cur.hsel + c8)) * 16);
+          }
+        } else {
+          // 16 rows x 32 columns (64 ct + 32 hsel ..) = 64 pieces, one per lane
+          const int row = lane >> 2, c8 = lane & 3;
+          if (i * 16 + row < cur.valid) {
+            v = *reinterpret_cast<const u32x4_t*>(&epi[row * kEpiStride + 8 * c8]);
+            off = (uint32_t)(((i * 16 + row) * Nout + cur.ct * 64 + 32 * cur.hsel + 8 * c8) * 2);
+          }
+        }
+      }
+      // gate/up's activations are read once, by the down GEMM: non-temporal
+      __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, (int)off, 0, GATE_UP ? 2 : 0);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    }
+    if (!nxt.ok) break;
+    cur = nxt;
+    par ^= 1;
+    first = false;
+    vb += gridDim.x;
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA may outlive the workgroup
+}
+
 // Packing: one thread per 16-byte vector of the source (coalesced reads),
 // each written to its place in the packed layout.
 __global__ void __launch_bounds__(256) pack_weights_kernel(const uint16_t* __restrict__ W,
@@ -812,6 +1187,28 @@ size_t grouped_ffn_workspace_bytes(int64_t capacity, int G, int I) {
   return (((size_t)rows * I * sizeof(uint16_t)) + 255) & ~(size_t)255;
 }
 
+// CUs of the current device (cached per device).
+static int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Grid of the streamed tall kernel for `nvirt` virtual blocks: one 8-wave
+// workgroup per CU (the register budget allows no second), a multiple of 8
+// so that each workgroup's virtual blocks stay on its XCD, at most nvirt.
+static int64_t stream_grid(int64_t nvirt) {
+  const int64_t p = ((int64_t)device_cu_count() / kNumXcd) * kNumXcd;
+  return p > 0 && p < nvirt ? p : nvirt;
+}
+
 int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32_t* counts, int G,
                        int H, int I, const void* w13, const float* w13s, const void* w2,
                        const float* w2s, const float* row_scale, uint16_t* y, int64_t capacity,
@@ -845,7 +1242,15 @@ int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32
   auto grid_tall = [&](int64_t n_tiles) {
     return (m_tiles_tall * n_tiles + grid_unit - 1) / grid_unit * grid_unit;
   };
-  if ((flags & MOE_FFN_GATE_UP) && tall) {
+  // the streamed form when the tile table fits its LDS
+  const bool streamed = tall && G <= kStreamMaxG;
+  if ((flags & MOE_FFN_GATE_UP) && streamed) {
+    const int64_t blocks = grid_tall((2 * (2 * I / 64) + 7) / 8);
+    if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(tall_stream_kernel<true>, dim3((unsigned)stream_grid(blocks)),
+                       dim3(8 * kWave), 0, stream, x, w13, cu_seqlens, counts, G, H, 2 * I, I,
+                       nullptr, act, capacity, dev_error, (int)blocks);
+  } else if ((flags & MOE_FFN_GATE_UP) && tall) {
     const int64_t blocks = grid_tall((2 * (2 * I / 64) + 7) / 8);
     if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
     hipLaunchKernelGGL((frag_gemm_kernel<true, 8, false, true>), dim3((unsigned)blocks),
@@ -874,7 +1279,13 @@ int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32
                          capacity, dev_error);
     }
   }
-  if ((flags & MOE_FFN_DOWN) && tall) {
+  if ((flags & MOE_FFN_DOWN) && streamed) {
+    const int64_t blocks = grid_tall((2 * (H / 64) + 7) / 8);
+    if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(tall_stream_kernel<false>, dim3((unsigned)stream_grid(blocks)),
+                       dim3(8 * kWave), 0, stream, act, w2, cu_seqlens, counts, G, I, H, H,
+                       row_scale, y, capacity, dev_error, (int)blocks);
+  } else if ((flags & MOE_FFN_DOWN) && tall) {
     const int64_t blocks = grid_tall((2 * (H / 64) + 7) / 8);
     if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
     hipLaunchKernelGGL((frag_gemm_kernel<false, 8, false, true>), dim3((unsigned)blocks),

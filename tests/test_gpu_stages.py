@@ -737,6 +737,43 @@ def test_ffn_packed_weights(H, I, T):
     assert rel_err(bf16_bits_to_f32(host_bits(y[:used])), bf16_bits_to_f32(host_bits(y2[:used]))) < 1e-2
 
 
+def test_ffn_tall_tiles_streamed_across_tiles():
+    """The tall tiles run persistently, each workgroup taking several tiles
+    in turn, with the next tile's weights and activation chunks fetched
+    during the current tile's last steps and its epilogue.  Enough tiles for
+    about three per workgroup, tile to tile changes of segment length (a
+    single row, 16 and 17 rows, full 256-row tiles, experts spanning two
+    tall tiles, empty experts between), every expert against the oracle per
+    row and element."""
+    rng = np.random.default_rng(11)
+    G, H, I = 200, 1024, 512
+    sizes = rng.integers(90, 220, G)
+    sizes[:14] = [0, 1, 16, 17, 255, 256, 257, 300, 511, 512, 128, 129, 0, 2]
+    sizes = [int(n) for n in rng.permutation(sizes)]
+    assert 96 <= sum(sizes) // G < 256
+    cfg = workloads.MoEConfig("t", 43, T=sum(sizes), H=H, E=G, K=1, I=I)
+    idx = np.concatenate([np.full(n, e, np.int32) for e, n in enumerate(sizes)])[:, None]
+    idx = rng.permutation(idx)
+    w = rng.uniform(0.5, 1.5, idx.shape).astype(np.float32)
+    hid = workloads.hidden(cfg)
+    w13, w2, host_w = stacked_weights(cfg)
+    ref = oracle.permute(idx, w, hid, G, 0, False)
+    p = ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), G)
+    w13p, w2p = ops.moe_pack_ffn_weights(w13, w2)
+    y = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13p, w2p, p.w_perm,
+                            flags=ops.MOE_FFN_ALL | ops.MOE_FFN_PACKED_WEIGHTS)
+    torch.cuda.synchronize()
+    got = bf16_bits_to_f32(host_bits(y))
+    for e in range(G):
+        n, r0 = int(ref["counts"][e]), int(ref["cu_seqlens"][e])
+        if n == 0:
+            continue
+        x = oracle.bf16_bits_to_f64(ref["x_perm"][r0:r0 + n])
+        rs = ref["w_perm"][r0:r0 + n, None].astype(np.float64)
+        check_rows(got[r0:r0 + n], oracle.expert_ffn(x, *host_w[e]) * rs, FFN_TOL,
+                   what=f"expert {e} ({n} rows)")
+
+
 def test_ffn_tall_tiles_edges():
     """Segments averaging 96..255 rows take the tall tiles (256 rows per
     workgroup, half a column tile per wave): segments of exactly 128, 129,

@@ -94,6 +94,20 @@ def kernel_source_hash(stage: str, fp8=None) -> str:
     return h.hexdigest()[:16]
 
 
+def gemm_kernel_name(layer, fp8, gate_up: bool) -> str:
+    """The grouped-GEMM kernel a routed projection launches: the FP8 path's,
+    or, with BF16 weights whose segments average 96..255 rows (and at most
+    1024 local experts), the streamed tall-tile kernel, else the
+    fragment-streaming one.  The same rule as the library's launcher."""
+    t = "true" if gate_up else "false"
+    if fp8 == "w8a8":
+        return f"w8a8_gemm_kernel<{t}>"
+    mean = layer.capacity // layer.El
+    if fp8 is None and 96 <= mean < 256 and layer.El <= 1024:
+        return f"tall_stream_kernel<{t}>"
+    return f"frag_gemm_kernel<{t}>"
+
+
 def committed_traffic(stage: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
     taken on the kernel as it is now (same source hash); else None.
@@ -425,8 +439,8 @@ def main():
         roof = {"bound": "hbm", "achieved": stages[dom]["GBps"], "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    gemm = "w8a8_gemm_kernel" if args.fp8 == "w8a8" else "frag_gemm_kernel"
-    roof["kernel"] = {"ffn_gate_up": f"{gemm}<true>", "ffn_down": f"{gemm}<false>"}.get(dom, dom)
+    roof["kernel"] = {"ffn_gate_up": gemm_kernel_name(layer, args.fp8, True),
+                      "ffn_down": gemm_kernel_name(layer, args.fp8, False)}.get(dom, dom)
     roof["alg_bytes_per_launch"] = a["bytes"]
     roof["traffic"] = committed_traffic(
         dom, cfg.name + {None: "", "weights": "_fp8w", "w8a8": "_w8a8"}[args.fp8])

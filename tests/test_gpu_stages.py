@@ -809,3 +809,15 @@ def test_ffn_tall_tiles_edges():
         deq = [oracle.quantize_weight_blocks(m)[2] for m in host_w[e]]
         check_rows(bf16_bits_to_f32(host_bits(y8[r0:r0 + n])),
                    oracle.expert_ffn(x, *deq) * rs, FFN_TOL, what=f"fp8w expert {e} ({n} rows)")
+
+
+@pytest.mark.parametrize("nvec", [1, 255, 1024, 4097, 300001])
+def test_copy_bytes(nvec):
+    """The streaming copy behind the copy-bandwidth figure: exact, including
+    sizes that end part-way through a workgroup's run of 4 x 256 vectors."""
+    src = torch.randint(-2**31, 2**31 - 1, (nvec * 4,), dtype=torch.int32, device="cuda")
+    dst = torch.zeros(nvec * 4 + 4, dtype=torch.int32, device="cuda")
+    ops.moe_copy_bytes(src, dst[:nvec * 4])
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nvec * 4], src)
+    assert int(dst[nvec * 4:].abs().sum()) == 0   # nothing written past the end

@@ -514,6 +514,39 @@ def test_combine_random_rows(T, K, H):
     _combine_case(rows, (k_idx * T + t_idx).astype(np.int32), T, K, shared)
 
 
+@pytest.mark.parametrize("scale", [3.0 / 448, 0.0123, 1e-30])
+def test_combine_qdq_table_form(scale):
+    """Combines of at least 2^20 16-byte vectors take the table form of the
+    FP8 QDQ (each workgroup tabulates the quantizer over the 32768
+    magnitudes, the sign is copied).  Every bf16 bit pattern as a routed row:
+    the table form bit-identical to the arithmetic form that smaller combines
+    take, for every pattern (NaNs and infinities too), and both bit-exact
+    against the oracle for the finite ones; then random K=2 rows with a
+    shared slot at table-form size against the oracle."""
+    s = float(np.float32(scale))
+    sc = torch.tensor([s], dtype=torch.float32, device="cuda")
+    T, H = 2048, 4096                     # T * H / 8 = 2^20 vectors
+    pat = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    rows = np.tile(pat, T * H // 65536).reshape(T, H)
+    row_of = np.arange(T, dtype=np.int32)
+    big = host_bits(ops.moe_combine(dev_bf16(rows), dev(row_of), T, 1, None, sc))
+    small = host_bits(ops.moe_combine(dev_bf16(rows[:16]), dev(row_of[:16]), 16, 1, None, sc))
+    np.testing.assert_array_equal(big[:16], small)
+    np.testing.assert_array_equal(big[16:32], small)
+    finite = ((pat & 0x7F80) != 0x7F80).reshape(16, H)
+    fin_rows = np.where(finite, rows[:16], 0).astype(np.uint16)   # the oracle takes finite values
+    ref = oracle.combine(oracle.fake_quant_per_tensor(fin_rows, np.float32(s)), row_of[:16], 16, 1)
+    np.testing.assert_array_equal(small[finite], ref[finite])
+    rng = np.random.default_rng(21)
+    K = 2
+    R = T * K + 3
+    vals = rng.standard_normal((R, H)).astype(np.float32) * rng.choice([1e-3, 1.0, 1e3], (R, 1)).astype(np.float32)
+    perm = rng.permutation(R)[: T * K].astype(np.int32)
+    row_of = np.where(rng.random(T * K) < 0.2, -1, perm).astype(np.int32)
+    shared = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    _combine_case(f32_to_bf16_bits(vals), row_of, T, K, shared, scale=s)
+
+
 def _check_case(seed=7, T=37, K=4, H=256):
     rng = np.random.default_rng(seed)
     rows = f32_to_bf16_bits(rng.standard_normal((T * K, H)).astype(np.float32))

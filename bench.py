@@ -211,6 +211,27 @@ def copy_gbps(steps: int = 5, nbytes: int = 1 << 30) -> float:
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def read_gbps(steps: int = 5, nbytes: int = 1 << 30) -> float:
+    """Bandwidth of moe_read_bytes over 1 GiB of random bytes: the plain
+    non-temporal read stream (the practical ceiling of the weight-streaming
+    GEMMs), timed with events on the launch stream."""
+    import torch
+    from combine_top_route_moe_amd import ops
+
+    src = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
+    ops.moe_read_bytes(src, sink)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        ops.moe_read_bytes(src, sink)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    del src, sink
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def copy_calibration(steps: int, warmup: int) -> None:
     """Time moe_copy_bytes over 1 GiB: the plain streaming kernel whose
     measured bandwidth and FETCH_SIZE / WRITE_SIZE counters calibrate the
@@ -403,6 +424,7 @@ def main():
         del flush
     assert layer.dev_error.item() == 0, "device error word set during the stage timing"
     copy_bw = copy_gbps()
+    read_bw = read_gbps()
 
     counts = layer.perm.counts.cpu().numpy()
     alg = algorithmic(cfg, counts, args.fp8)
@@ -474,6 +496,7 @@ def main():
         "permute_GBps": stages["permute"]["GBps"],
         "combine_GBps": stages["combine"]["GBps"],
         "copy_GBps": round(copy_bw, 1),
+        "read_GBps": round(read_bw, 1),
         "layer_ms": {k: {"median": round(float(np.median(v)), 5), "p10": pct(v, 10),
                          "p90": pct(v, 90)} for k, v in layer_ms.items()},
         "stages": stages,
@@ -488,6 +511,7 @@ def main():
                              "run one after another (the layer itself runs the shared expert "
                              "concurrently with the routed path)",
                    "copy_GBps": "moe_copy_bytes, 1 GiB read + 1 GiB written per launch",
+                   "read_GBps": "moe_read_bytes, 1 GiB of random bytes read per launch",
                    **({"stages_cold": "the same, with 1 GiB written before every step "
                                       "(cold L2 and infinity cache)"} if stages_cold else {})},
         "cpu_baseline": None,

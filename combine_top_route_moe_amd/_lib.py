@@ -47,6 +47,7 @@ SIGNATURES = {
     "moe_combine_check": (_c_int, [_vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp,
                                    _vp]),
     "moe_copy_bytes": (_c_int, [_vp, _vp, _c_size, _vp]),
+    "moe_read_bytes": (_c_int, [_vp, _c_size, _vp, _vp]),
 }
 
 _lib = None

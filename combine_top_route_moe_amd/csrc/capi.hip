@@ -62,6 +62,23 @@ __global__ void __launch_bounds__(256) copy_kernel(const copy_vec_t* __restrict_
     }
   }
 }
+// The read-only stream: runs of 8 x 256 vectors per workgroup, all eight
+// loads of a thread in flight together, non-temporal; the xor of what a
+// thread read is written only if it equals a marker, which keeps the loads.
+__global__ void __launch_bounds__(256) read_kernel(const copy_vec_t* __restrict__ src,
+                                                   copy_vec_t* __restrict__ sink, int64_t n) {
+  constexpr int kUnroll = 8;
+  copy_vec_t acc = {0u, 0u, 0u, 0u};
+  for (int64_t base = (int64_t)blockIdx.x * 256 * kUnroll; base < n;
+       base += (int64_t)gridDim.x * 256 * kUnroll) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = base + u * 256 + threadIdx.x;
+      if (i < n) acc ^= __builtin_nontemporal_load(src + i);
+    }
+  }
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x5ca1ab1eu) sink[(blockIdx.x * 256 + threadIdx.x) & 4095] = acc;
+}
 }  // namespace moe
 
 using namespace moe;
@@ -370,6 +387,18 @@ int moe_copy_bytes(const void* src, void* dst, size_t bytes, void* stream) {
   if (blocks > 256 * 64) blocks = 256 * 64;
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
                      static_cast<const copy_vec_t*>(src), static_cast<copy_vec_t*>(dst), n);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_read_bytes(const void* src, size_t bytes, void* sink, void* stream) {
+  if (bytes % 16) return MOE_ERR_INVALID_ARG;
+  if (bytes == 0) return MOE_OK;
+  if (!src || !sink || !aligned16(src) || !aligned16(sink)) return MOE_ERR_INVALID_ARG;
+  const int64_t n = (int64_t)(bytes / 16);
+  int64_t blocks = (n + 2047) / 2048;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  hipLaunchKernelGGL(read_kernel, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
+                     static_cast<const copy_vec_t*>(src), static_cast<copy_vec_t*>(sink), n);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

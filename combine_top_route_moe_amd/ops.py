@@ -413,6 +413,13 @@ def moe_combine_check(rows: torch.Tensor, row_of: torch.Tensor, T: int, K: int,
         _ptr(dev_error), _stream(stream)))
 
 
+def moe_read_bytes(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    n = src.numel() * src.element_size()
+    if sink.numel() * sink.element_size() < 65536:
+        raise ValueError("sink must hold at least 64 KiB")
+    check("moe_read_bytes", load().moe_read_bytes(_ptr(src), n, _ptr(sink), _stream(stream)))
+
+
 def moe_copy_bytes(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     n = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() < n:

@@ -436,6 +436,16 @@ int moe_combine_check(const uint16_t* rows, int64_t num_rows, const int32_t* row
  * multiple of 16 and both pointers 16-byte aligned. */
 int moe_copy_bytes(const void* src, void* dst, size_t bytes, void* stream);
 
+/* ---- streaming read -----------------------------------------------------
+ * Reads src[0:bytes) once with 16-byte non-temporal vector loads and folds
+ * it into a 32-bit checksum per thread; `sink` (at least 64 KiB, 16-byte
+ * aligned, device) receives only checksums equal to 0x5ca1ab1e, so in
+ * practice nothing is written.  The read-only counterpart of
+ * moe_copy_bytes: its measured rate is the practical ceiling of the
+ * weight-streaming kernels.  `bytes` must be a multiple of 16, `src`
+ * 16-byte aligned. */
+int moe_read_bytes(const void* src, size_t bytes, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,3 +64,6 @@ def test_host_only_entry_points():
                                     None, None, None, None, 16, 3, None, 0, None, None) == -1
     assert lib.moe_combine(None, 0, None, None, 0, 1, 128, None, None, None, None) == 0  # T = 0
     assert lib.moe_copy_bytes(None, None, 15, None) == -1
+    assert lib.moe_read_bytes(None, 15, None, None) == -1        # not a multiple of 16
+    assert lib.moe_read_bytes(None, 0, None, None) == 0          # nothing to read
+    assert lib.moe_read_bytes(None, 16, None, None) == -1        # null pointers

@@ -854,3 +854,16 @@ def test_copy_bytes(nvec):
     torch.cuda.synchronize()
     assert torch.equal(dst[:nvec * 4], src)
     assert int(dst[nvec * 4:].abs().sum()) == 0   # nothing written past the end
+
+
+def test_read_bytes():
+    """The read-only stream behind the read-bandwidth figure: it reads its
+    whole input (a ragged size included) without error and writes nothing
+    to the sink unless a thread's checksum equals the marker, which these
+    inputs never produce."""
+    sink = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
+    for nvec in (1, 2047, 300001):
+        src = torch.zeros(nvec * 4, dtype=torch.int32, device="cuda")
+        ops.moe_read_bytes(src, sink)
+    torch.cuda.synchronize()
+    assert int(sink.sum()) == 0

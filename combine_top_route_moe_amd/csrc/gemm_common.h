@@ -30,35 +30,26 @@ __device__ __forceinline__ int xcd_remap(int bid) {
   return (chunk * kNumXcd + xcd) * kXcdChunk + off;
 }
 
-// Decode tile number `pid` into (group, m-tile, n-tile), with tiles of BMR
-// rows (128, or 256 for the tall tiles).  Every lane of the calling wave
-// returns the same answer; returns false past the last tile.  mt_base (if
-// asked for) is the number of 128-row m-tiles of the groups before g — the
-// unit in which the gate/up output is laid out for the down projection,
-// whatever the tile height.
-template <int BMR = kBM>
+// Decode tile number `pid` into (group, m-tile, n-tile).  Every lane of
+// the calling wave returns the same answer; returns false past the last
+// tile.  mt_base (if asked for) is the number of m-tiles of the groups
+// before g.
 __device__ __forceinline__ bool decode_tile(int pid, const int32_t* __restrict__ counts, int G,
                                             int n_tiles, int& g, int& mt, int& nt,
                                             int* mt_base = nullptr) {
   const int lane = threadIdx.x & 63;
-  int carry = 0, carry128 = 0;
+  int carry = 0;
   for (int base = 0; base < G; base += kWave) {
     const int e = base + lane;
     const int c = e < G ? max(counts[e], 0) : 0;
-    const int tiles = ((c + BMR - 1) / BMR) * n_tiles;
-    const int m128 = (c + kBM - 1) / kBM;
-    int incl = tiles, incl128 = m128;
+    const int tiles = ((c + kBM - 1) / kBM) * n_tiles;
+    int incl = tiles;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(incl, off, kWave);
       if (lane >= off) incl += y;
-      if (BMR != kBM) {
-        const int y128 = __shfl_up(incl128, off, kWave);
-        if (lane >= off) incl128 += y128;
-      }
     }
     incl += carry;
-    incl128 += carry128;
     const int excl = incl - tiles;
     const uint64_t hit = __ballot(e < G && pid >= excl && pid < incl);
     if (hit) {
@@ -66,19 +57,13 @@ __device__ __forceinline__ bool decode_tile(int pid, const int32_t* __restrict__
       g = base + src;
       const int ex = __shfl(excl, src, kWave);
       const int local = pid - ex;
-      const int mtiles = (__shfl(c, src, kWave) + BMR - 1) / BMR;
+      const int mtiles = (__shfl(c, src, kWave) + kBM - 1) / kBM;
       nt = local / mtiles;
       mt = local - nt * mtiles;
-      if (mt_base) {
-        if (BMR == kBM)
-          *mt_base = ex / n_tiles;                                  // m-tiles before g
-        else
-          *mt_base = __shfl(incl128 - m128, src, kWave);
-      }
+      if (mt_base) *mt_base = ex / n_tiles;                   // m-tiles before g
       return true;
     }
     carry = __shfl(incl, 63, kWave);
-    if (BMR != kBM) carry128 = __shfl(incl128, 63, kWave);
   }
   return false;
 }

@@ -229,15 +229,16 @@ constexpr int kFrags = 4;        // B fragments per wave (one column tile)
 // activation tile is then shared by more columns), 4 when they are short (more,
 // smaller workgroups balance skewed segment sizes better).
 //
-// Tall tiles (TALL): for segments of about one to two m-tiles (129..256 rows
-// would otherwise take two 128-row m-tiles, the second reading the whole
-// weight panel again for a handful of rows), a workgroup covers 256 rows and
-// each wave half a column tile: 16 m-subtiles x 2 fragments (w13: the 16
-// gate rows and the 16 matching up rows; w2: 32 consecutive rows).  The
-// accumulators stay at 16 x 2 x 4 = 128 registers, each weight byte streams
-// into the CU once per segment, and a CU still runs 8 weight streams; the
-// cost is twice the LDS activation reads per MFMA, which the weight-streaming
-// workloads this is used for have to spare.
+// Tall tiles (FragShape<true>, the streamed kernel further down): for
+// segments of about one to two m-tiles (129..256 rows would otherwise take
+// two 128-row m-tiles, the second reading the whole weight panel again for a
+// handful of rows), a workgroup covers 256 rows and each wave half a column
+// tile: 16 m-subtiles x 2 fragments (w13: the 16 gate rows and the 16
+// matching up rows; w2: 32 consecutive rows).  The accumulators stay at
+// 16 x 2 x 4 = 128 registers, each weight byte streams into the CU once per
+// segment, and a CU still runs 8 weight streams; the cost is twice the LDS
+// activation reads per MFMA, which the weight-streaming workloads this is
+// used for have to spare.
 template <bool TALL> struct FragShape {
   static constexpr int kMs = TALL ? 16 : kMsub;        // 16-row m-subtiles per workgroup
   static constexpr int kFr = TALL ? 2 : kFrags;        // B fragments per wave
@@ -277,23 +278,16 @@ __device__ __forceinline__ void epi_store(u32x4_t* p, const u32x4_t& v) {
 template <bool F8>
 using WFrag = typename std::conditional<F8, u32x2_t, u32x4_t>::type;
 
-template <bool GATE_UP, bool NT, int NW, bool F8, bool TALL>
+template <bool GATE_UP, bool NT, int NW, bool F8>
 __device__ __forceinline__ void frag_gemm_body(
-    u32x4_t (*As)[FragShape<TALL>::kSB][kWave], const WFrag<F8>* __restrict__ wp, int kstride,
+    u32x4_t (*As)[FragShape<false>::kSB][kWave], const WFrag<F8>* __restrict__ wp, int kstride,
     const float* __restrict__ sc_g, const float* __restrict__ sc_u,
     const uint16_t* a_base, const int64_t* a_uoff, const uint32_t* a_voff, int a_chunk_stride,
     int w, int lane, int nks, int nlive,
-    int valid, int ct, int hsel, bool ct_ok, int64_t row_base, int64_t mt_glob, int Nout,
+    int valid, int ct, bool ct_ok, int64_t row_base, int64_t mt_glob, int Nout,
     const float* tile_scale, uint16_t* __restrict__ Out, int crot, bool prio, uint16_t* epi) {
-  constexpr int MS = FragShape<TALL>::kMs, FR = FragShape<TALL>::kFr;
-  constexpr int kDmaPerWave = FragShape<TALL>::kSB / NW;
-  // the packed fragment this wave's f-th B operand is: all four of its
-  // column tile, or (tall) the half hsel — w13: gate fragment hsel and up
-  // fragment hsel + 2; w2: fragments 2 hsel, 2 hsel + 1
-  auto frag_of = [&](int f) {
-    if (!TALL) return f;
-    return GATE_UP ? (f == 0 ? hsel : hsel + 2) : 2 * hsel + f;
-  };
+  constexpr int MS = FragShape<false>::kMs, FR = FragShape<false>::kFr;
+  constexpr int kDmaPerWave = FragShape<false>::kSB / NW;
   // every workgroup walks K from its own starting chunk (crot) and wraps
   // around, so the many weight streams do not all hit the same offsets —
   // and so the same HBM channels — at the same time
@@ -347,7 +341,7 @@ __device__ __forceinline__ void frag_gemm_body(
   for (int s = 0; s < kPrefetch; ++s) {
 #pragma unroll
     for (int f = 0; f < FR; ++f)
-      bq[s][f] = load_w(wrap(s + krot, nks) * kstride + frag_of(f) * kWave);
+      bq[s][f] = load_w(wrap(s + krot, nks) * kstride + f * kWave);
     load_scales(s, wrap(s + krot, nks));
   }
   asm volatile("" ::: "memory");
@@ -408,10 +402,7 @@ __device__ __forceinline__ void frag_gemm_body(
       // instead of one per m-subtile
 #pragma unroll
       for (int g8 = 0; g8 < MS; g8 += 8) {
-        // (tall: a constant trip count with skipped iterations, so that the
-        // loops unroll and the 16 x 2 accumulators stay in registers)
-        if (TALL ? g8 >= nlive : false) continue;
-        if (!TALL && g8 >= nlive) break;
+        if (g8 >= nlive) break;
         u32x4_t a[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) a[i] = As[stage][(g8 + i) * kChunkSteps + sub][lane];
@@ -421,8 +412,7 @@ __device__ __forceinline__ void frag_gemm_body(
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          if (TALL ? g8 + i >= nlive : false) continue;
-          if (!TALL && g8 + i >= nlive) break;
+          if (g8 + i >= nlive) break;
           const bf16x8_t af = __builtin_bit_cast(bf16x8_t, a[i]);
 #pragma unroll
           for (int f = 0; f < FR; ++f)
@@ -436,7 +426,7 @@ __device__ __forceinline__ void frag_gemm_body(
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int f = 0; f < FR; ++f)
-        bq[s][f] = load_w(wrap(nxt + krot, nks) * kstride + frag_of(f) * kWave);
+        bq[s][f] = load_w(wrap(nxt + krot, nks) * kstride + f * kWave);
       load_scales(s, wrap(nxt + krot, nks));
       asm volatile("" ::: "memory");
     }
@@ -449,13 +439,11 @@ __device__ __forceinline__ void frag_gemm_body(
   // so the 2-byte writes are conflict-free), and is stored back as 16-byte
   // vectors: whole 128-byte row pieces instead of 2-byte scattered stores.
   // Rows past the segment end are neither staged nor stored.
-  // bf16 per staged row: the wave's output columns (gate/up: 32, or 16 when
-  // tall; down: 64, or 32 when tall) + 8
+  // bf16 per staged row: the wave's output columns (gate/up: 32; down: 64) + 8
   constexpr int kEpiStride = (GATE_UP ? 8 * FR : 16 * FR) + 8;
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
-    if (TALL ? i >= nlive : false) continue;
-    if (!TALL && i >= nlive) break;
+    if (i >= nlive) break;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int rr = 4 * (lane >> 4) + q;
@@ -480,21 +468,13 @@ __device__ __forceinline__ void frag_gemm_body(
       // a is written in the down GEMM's activation fragment order: block
       // (128-row m-tile, m-subtile, K-step ct) of 64 lanes x 8 values, where
       // lane L = row%16 + 16*(col%32 / 8) holds columns 8*(col%32 / 8) .. +8
-      // (a tall tile's m-subtiles 8..15 are those of the next m-tile, and
-      // its wave fills lanes 32 hsel .. 32 hsel + 31 of the block)
       const int row = lane & 15;
       uint16_t* blk = Out + ((mt_glob * kMsub + i) * (int64_t)(Nout / 32) + ct) * (kWave * 8);
-      if (!TALL) {
-        if (i * 16 + row < valid) {
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&epi[row * kEpiStride + 8 * (lane >> 4)]);
-          epi_store<true>(reinterpret_cast<u32x4_t*>(blk) + lane, v);
-        }
-      } else if (lane < 32 && i * 16 + row < valid) {
-        const int c8 = lane >> 4;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&epi[row * kEpiStride + 8 * c8]);
-        epi_store<true>(reinterpret_cast<u32x4_t*>(blk) + row + 16 * (2 * hsel + c8), v);
+      if (i * 16 + row < valid) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&epi[row * kEpiStride + 8 * (lane >> 4)]);
+        epi_store<true>(reinterpret_cast<u32x4_t*>(blk) + lane, v);
       }
-    } else if (!TALL) {
+    } else {
       // 16 rows x 64 columns = 128 pieces of 8 columns, two per lane
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -504,14 +484,6 @@ __device__ __forceinline__ void frag_gemm_body(
           epi_store<false>(reinterpret_cast<u32x4_t*>(Out + (row_base + i * 16 + row) * Nout + ct * 64) + c8, v);
         }
       }
-    } else {
-      // tall: 16 rows x 32 columns (64 ct + 32 hsel ..) = 64 pieces, one per lane
-      const int row = lane >> 2, c8 = lane & 3;
-      if (i * 16 + row < valid) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&epi[row * kEpiStride + 8 * c8]);
-        epi_store<false>(reinterpret_cast<u32x4_t*>(Out + (row_base + i * 16 + row) * Nout +
-                                                    ct * 64 + 32 * hsel) + c8, v);
-      }
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   }
@@ -519,23 +491,23 @@ __device__ __forceinline__ void frag_gemm_body(
 
 // Two waves per SIMD: an 8-wave workgroup needs them, a 4-wave one gets two
 // workgroups per CU; the register budget is 256 per lane either way.
-template <bool GATE_UP, int NW, bool F8, bool TALL>
+template <bool GATE_UP, int NW, bool F8>
 __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
     const uint16_t* __restrict__ A, const void* __restrict__ Wf, const float* __restrict__ Wsc,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ counts, int G,
     int Kdim, int Nw /* weight rows per group */, int Nout, const float* __restrict__ row_scale,
     uint16_t* __restrict__ Out, int64_t capacity, int32_t* __restrict__ dev_error) {
-  using Shape = FragShape<TALL>;
+  using Shape = FragShape<false>;
   constexpr int BMR = Shape::kRows;
   __shared__ __attribute__((aligned(16))) u32x4_t As[kStages][Shape::kSB][kWave];
   __shared__ __attribute__((aligned(16))) uint16_t Epi[NW][16 * 72];  // per-wave output staging
 
   const int n_ct = Nw / 64;               // column tiles per group
-  const int n_wt = TALL ? 2 * n_ct : n_ct;  // wave tiles per group (a tall wave: half a tile)
+  const int n_wt = n_ct;                  // wave tiles per group
   const int n_cb = (n_wt + NW - 1) / NW;  // workgroups per m-tile
   const int pid = xcd_remap(blockIdx.x);
   int g, mt, cb, mt_base;
-  if (!decode_tile<BMR>(pid, counts, G, n_cb, g, mt, cb, &mt_base)) return;
+  if (!decode_tile(pid, counts, G, n_cb, g, mt, cb, &mt_base)) return;
   // the same in every lane: say so, so that addresses built from them stay scalar
   g = __builtin_amdgcn_readfirstlane(g);
   mt = __builtin_amdgcn_readfirstlane(mt);
@@ -559,8 +531,7 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
   // waves stream a real tile and store nothing
   const bool ct_ok = cb * NW + w < n_wt;
   const int wt = ct_ok ? cb * NW + w : n_wt - 1;
-  const int ct = TALL ? wt >> 1 : wt;
-  const int hsel = TALL ? wt & 1 : 0;
+  const int ct = wt;
   const int nks = Kdim / 32;
 
   // this wave's weight stream: step ks, fragment f at wp[ks * kstride + f * 64]
@@ -569,8 +540,7 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
   const WFrag<F8>* wp = reinterpret_cast<const WFrag<F8>*>(Wf) +
                         ((int64_t)g * nks * n_ct + ct) * (kFrags * kWave) + lane;
   // FP8: the scale rows ([G][Nw/128][Kdim/128]) of this tile's gate and up
-  // rows (w13: gate rows 32 ct.., up rows Nw/2 + 32 ct..; w2: rows 64 ct..);
-  // half a tile lies in the same 128-row scale block as the whole
+  // rows (w13: gate rows 32 ct.., up rows Nw/2 + 32 ct..; w2: rows 64 ct..)
   const int nkb = Kdim / 128, nrb = Nw / 128;
   const float* sc_g = nullptr;
   const float* sc_u = nullptr;
@@ -584,11 +554,10 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
   // stage; block b is m-subtile b / kChunkSteps, K-step b % kChunkSteps
   constexpr int kDmaPerWave = Shape::kSB / NW;
   // gate/up reads the permuted rows (row-major); down reads the gate/up
-  // output, which that kernel wrote in fragment order per 128-row m-tile
-  // (a tall tile's second half is the next m-tile).  Source of block q:
-  // a_base + a_uoff[q] (+ the chunk's offset) in elements, uniform, plus
-  // a_voff[q] bytes per lane
-  const int64_t mt_glob = (int64_t)mt_base + (int64_t)mt * (BMR / kBM);
+  // output, which that kernel wrote in fragment order per 128-row m-tile.
+  // Source of block q: a_base + a_uoff[q] (+ the chunk's offset) in
+  // elements, uniform, plus a_voff[q] bytes per lane
+  const int64_t mt_glob = (int64_t)mt_base + mt;
   const uint16_t* a_base =
       GATE_UP ? A + row_base * Kdim : A + mt_glob * kMsub * (int64_t)nks * (kWave * 8);
   int64_t a_uoff[kDmaPerWave];
@@ -643,20 +612,20 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
     prio = __ballot(!fits) == 0;
   }
   if (once)
-    frag_gemm_body<GATE_UP, true, NW, F8, TALL>(As, wp, kstride, sc_g, sc_u, a_base, a_uoff, a_voff,
-                                                a_chunk_stride, w, lane, nks, nlive, valid, ct, hsel,
-                                                ct_ok, row_base, mt_glob, Nout, tile_scale, Out,
-                                                crot, prio, Epi[w]);
+    frag_gemm_body<GATE_UP, true, NW, F8>(As, wp, kstride, sc_g, sc_u, a_base, a_uoff, a_voff,
+                                          a_chunk_stride, w, lane, nks, nlive, valid, ct, ct_ok,
+                                          row_base, mt_glob, Nout, tile_scale, Out, crot, prio,
+                                          Epi[w]);
   else
-    frag_gemm_body<GATE_UP, false, NW, F8, TALL>(As, wp, kstride, sc_g, sc_u, a_base, a_uoff,
-                                                 a_voff, a_chunk_stride, w, lane, nks, nlive, valid,
-                                                 ct, hsel, ct_ok, row_base, mt_glob, Nout,
-                                                 tile_scale, Out, crot, false, Epi[w]);
+    frag_gemm_body<GATE_UP, false, NW, F8>(As, wp, kstride, sc_g, sc_u, a_base, a_uoff, a_voff,
+                                           a_chunk_stride, w, lane, nks, nlive, valid, ct, ct_ok,
+                                           row_base, mt_glob, Nout, tile_scale, Out, crot, false,
+                                           Epi[w]);
 }
 
 // ---------------------------------------------------------------------------
-// The tall tiles, streamed.  In the one-tile-per-workgroup form every tile
-// boundary stalls the CU's memory streams: the waves wait for all their
+// The tall tiles, streamed.  With one tile per workgroup every tile boundary
+// would stall the CU's memory streams: the waves wait for all their
 // loads (the weight prefetch runs kPrefetch steps past the end), decode the
 // next tile from the counts in memory, store their outputs, and only then
 // start the next tile's weight and activation streams, whose first bytes
@@ -836,7 +805,9 @@ __global__ void __launch_bounds__(8 * kWave, 2) tall_stream_kernel(
 
   const uint32_t as_lds = lds_addr(&As[0][0][0]), rs_lds = lds_addr(&rs[0][0]);
   auto wrap = [](int x, int n) { return x >= n ? x - n : x; };
-  // the packed fragment of this wave's f-th B operand (see frag_gemm_body)
+  // the packed fragment of this wave's f-th B operand, the half hsel of its
+  // column tile: w13 gate fragment hsel and up fragment hsel + 2; w2
+  // fragments 2 hsel and 2 hsel + 1
   auto frag_of = [](const TallTile& t, int f) {
     return GATE_UP ? (f == 0 ? t.hsel : t.hsel + 2) : 2 * t.hsel + f;
   };
@@ -1231,9 +1202,11 @@ int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32
   // long, half two) use the 8-wave tall tiles in both stages instead, so that
   // no expert streams its weights twice (same-box A/B on the deepseek-shape
   // layer, T=4096, H=7168, 256 experts, I=2048: gate/up 2.75 -> 2.58 ms, down
-  // unchanged, the layer 4.86 -> 4.71 ms).  With FP8 weights a tall wave's
-  // half-size fragments keep too few bytes in flight (the same A/B: gate/up
-  // 2.34 -> 2.58 ms), so they keep the 128-row tiles.
+  // unchanged, the layer 4.86 -> 4.71 ms), in the streamed kernel (down
+  // 1.65 -> 1.48 ms more); its LDS tile table holds every group the ABI
+  // accepts.  With FP8 weights a tall wave's half-size fragments keep too few
+  // bytes in flight (the same A/B: gate/up 2.34 -> 2.58 ms), so they keep the
+  // 128-row tiles.
   const int64_t mean_x = capacity / G;  // mean rows per group, rounded down
   const bool wide = mean_x >= kBM;
   const bool wide_down = wide && mean_x < 2 * kBM;
@@ -1242,27 +1215,20 @@ int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32
   auto grid_tall = [&](int64_t n_tiles) {
     return (m_tiles_tall * n_tiles + grid_unit - 1) / grid_unit * grid_unit;
   };
-  // the streamed form when the tile table fits its LDS
-  const bool streamed = tall && G <= kStreamMaxG;
-  if ((flags & MOE_FFN_GATE_UP) && streamed) {
+  if (tall && G > kStreamMaxG) return MOE_ERR_UNSUPPORTED;   // the ABI admits at most 1024
+  if ((flags & MOE_FFN_GATE_UP) && tall) {
     const int64_t blocks = grid_tall((2 * (2 * I / 64) + 7) / 8);
     if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(tall_stream_kernel<true>, dim3((unsigned)stream_grid(blocks)),
                        dim3(8 * kWave), 0, stream, x, w13, cu_seqlens, counts, G, H, 2 * I, I,
                        nullptr, act, capacity, dev_error, (int)blocks);
-  } else if ((flags & MOE_FFN_GATE_UP) && tall) {
-    const int64_t blocks = grid_tall((2 * (2 * I / 64) + 7) / 8);
-    if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((frag_gemm_kernel<true, 8, false, true>), dim3((unsigned)blocks),
-                       dim3(8 * kWave), 0, stream, x, w13, w13s, cu_seqlens, counts, G, H, 2 * I, I,
-                       nullptr, act, capacity, dev_error);
   } else if (flags & MOE_FFN_GATE_UP) {
     if (packed) {
       const int nw = wide ? 8 : 4;
       const int64_t blocks = grid_for((2 * I / 64 + nw - 1) / nw);
       if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
 #define MOE_FRAG_GU(NW, F8)                                                                  \
-  hipLaunchKernelGGL((frag_gemm_kernel<true, NW, F8, false>), dim3((unsigned)blocks), dim3(NW * kWave), \
+  hipLaunchKernelGGL((frag_gemm_kernel<true, NW, F8>), dim3((unsigned)blocks), dim3(NW * kWave),        \
                      0, stream, x, w13, w13s, cu_seqlens, counts, G, H, 2 * I, I, nullptr, act,  \
                      capacity, dev_error)
       if (f8) {
@@ -1279,25 +1245,19 @@ int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32
                          capacity, dev_error);
     }
   }
-  if ((flags & MOE_FFN_DOWN) && streamed) {
+  if ((flags & MOE_FFN_DOWN) && tall) {
     const int64_t blocks = grid_tall((2 * (H / 64) + 7) / 8);
     if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(tall_stream_kernel<false>, dim3((unsigned)stream_grid(blocks)),
                        dim3(8 * kWave), 0, stream, act, w2, cu_seqlens, counts, G, I, H, H,
                        row_scale, y, capacity, dev_error, (int)blocks);
-  } else if ((flags & MOE_FFN_DOWN) && tall) {
-    const int64_t blocks = grid_tall((2 * (H / 64) + 7) / 8);
-    if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((frag_gemm_kernel<false, 8, false, true>), dim3((unsigned)blocks),
-                       dim3(8 * kWave), 0, stream, act, w2, w2s, cu_seqlens, counts, G, I, H, H,
-                       row_scale, y, capacity, dev_error);
   } else if (flags & MOE_FFN_DOWN) {
     if (packed) {
       const int nw = wide_down ? 8 : 4;
       const int64_t blocks = grid_for((H / 64 + nw - 1) / nw);
       if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
 #define MOE_FRAG_DN(NW, F8)                                                                   \
-  hipLaunchKernelGGL((frag_gemm_kernel<false, NW, F8, false>), dim3((unsigned)blocks), dim3(NW * kWave), \
+  hipLaunchKernelGGL((frag_gemm_kernel<false, NW, F8>), dim3((unsigned)blocks), dim3(NW * kWave),       \
                      0, stream, act, w2, w2s, cu_seqlens, counts, G, I, H, H, row_scale, y,       \
                      capacity, dev_error)
       if (f8) {

@@ -807,6 +807,40 @@ def test_ffn_tall_tiles_streamed_across_tiles():
                    what=f"expert {e} ({n} rows)")
 
 
+def test_ffn_tall_tiles_streamed_at_the_limits():
+    """The streamed tall kernel at its limits: 1024 groups (its LDS tile
+    table full) and H = I = 128, so each K loop has two chunks and the next
+    tile's first chunk goes out with the current tile's first one; many
+    tiles per workgroup, empty groups among them."""
+    rng = np.random.default_rng(12)
+    G, H, I = 1024, 128, 128
+    sizes = [int(n) for n in rng.integers(90, 230, G)]
+    for e in rng.choice(G, 40, replace=False):
+        sizes[e] = 0
+    sizes[3], sizes[500] = 257, 1
+    assert 96 <= sum(sizes) // G < 256
+    cfg = workloads.MoEConfig("t", 44, T=sum(sizes), H=H, E=G, K=1, I=I)
+    idx = rng.permutation(np.concatenate([np.full(n, e, np.int32) for e, n in enumerate(sizes)])[:, None])
+    w = rng.uniform(0.5, 1.5, idx.shape).astype(np.float32)
+    hid = workloads.hidden(cfg)
+    w13, w2, host_w = stacked_weights(cfg)
+    ref = oracle.permute(idx, w, hid, G, 0, False)
+    p = ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), G)
+    w13p, w2p = ops.moe_pack_ffn_weights(w13, w2)
+    y = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13p, w2p, p.w_perm,
+                            flags=ops.MOE_FFN_ALL | ops.MOE_FFN_PACKED_WEIGHTS)
+    torch.cuda.synchronize()
+    got = bf16_bits_to_f32(host_bits(y))
+    for e in range(G):
+        n, r0 = int(ref["counts"][e]), int(ref["cu_seqlens"][e])
+        if n == 0:
+            continue
+        x = oracle.bf16_bits_to_f64(ref["x_perm"][r0:r0 + n])
+        rs = ref["w_perm"][r0:r0 + n, None].astype(np.float64)
+        check_rows(got[r0:r0 + n], oracle.expert_ffn(x, *host_w[e]) * rs, FFN_TOL,
+                   what=f"expert {e} ({n} rows)")
+
+
 def test_ffn_tall_tiles_edges():
     """Segments averaging 96..255 rows take the tall tiles (256 rows per
     workgroup, half a column tile per wave): segments of exactly 128, 129,

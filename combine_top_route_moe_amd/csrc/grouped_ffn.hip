@@ -986,8 +986,11 @@ __global__ void __launch_bounds__(8 * kWave, 2) tall_stream_kernel(
           }
         }
       }
-      // gate/up's activations are read once, by the down GEMM: non-temporal
-      __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, (int)off, 0, GATE_UP ? 2 : 0);
+      // non-temporal (aux bit 1, nt): gate/up's activations are read once, by
+      // the down GEMM; the down rows once, by the combine (same-box A/B on
+      // the deepseek-shape layer: down 1.475 -> 1.425 ms, the combine
+      // unchanged; the 128-row kernel keeps ordinary stores for its down rows)
+      __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, (int)off, 0, 2);
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     }
     if (!nxt.ok) break;

@@ -833,9 +833,13 @@ __global__ void __launch_bounds__(8 * kWave, 2) tall_stream_kernel(
     }
   };
   u32x4_t bq[kPrefetch][FR];
+  // weights read once stream past the caches (non-temporal); gate/up always
+  // does, without the per-tile branch (same-box A/B on the deepseek-shape
+  // layer, every expert read once: gate/up 2.58 -> 2.50 ms; for down the
+  // branch-free form was slower)
   auto load_step = [&](const TallTile& t, int step, int s) {
     const u32x4_t* p = t.wp + (int64_t)wrap(step + t.crot * kChunkSteps, nks) * kstride + lane;
-    if (t.nt) {
+    if (GATE_UP || t.nt) {
 #pragma unroll
       for (int f = 0; f < FR; ++f) bq[s][f] = __builtin_nontemporal_load(p + frag_of(t, f) * kWave);
     } else {

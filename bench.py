@@ -96,14 +96,14 @@ def kernel_source_hash(stage: str, fp8=None) -> str:
 
 def gemm_kernel_name(layer, fp8, gate_up: bool) -> str:
     """The grouped-GEMM kernel a routed projection launches: the FP8 path's,
-    or, with BF16 weights whose segments average 96..255 rows (and at most
-    1024 local experts), the streamed tall-tile kernel, else the
-    fragment-streaming one.  The same rule as the library's launcher."""
+    or, for segments averaging 96..255 rows (BF16 or FP8 weights), the
+    streamed tall-tile kernel, else the fragment-streaming one.  The same
+    rule as the library's launcher."""
     t = "true" if gate_up else "false"
     if fp8 == "w8a8":
         return f"w8a8_gemm_kernel<{t}>"
     mean = layer.capacity // layer.El
-    if fp8 is None and 96 <= mean < 256 and layer.El <= 1024:
+    if 96 <= mean < 256:
         return f"tall_stream_kernel<{t}>"
     return f"frag_gemm_kernel<{t}>"
 

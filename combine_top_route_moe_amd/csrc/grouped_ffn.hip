@@ -676,18 +676,21 @@ struct TallTile {
   int ct, hsel, ct_ok;      // column tile, its half, whether this wave's half exists
   int nt, crot;             // weights read once (streamed past the caches), K rotation
   int64_t row_base, mt_glob;
-  const u32x4_t* wp;        // the wave's weight stream at lane 0, K-step 0
+  const void* wp;           // the wave's weight stream at lane 0, K-step 0
+  const float* sc_g;        // FP8 weights: the tile scales of the wave's gate (or w2) rows
+  const float* sc_u;        // ... and of its up rows, per 128 K
   const uint16_t* a_base;   // the activation DMA's base
   uint32_t a_voff[FragShape<true>::kSB / 8];  // gate/up: per-lane byte offsets of the DMA blocks
 };
 
 // Decode virtual block vb into t (t.ok = 0 past the last tile) from the LDS
 // tile table.
-template <bool GATE_UP>
+template <bool GATE_UP, bool F8>
 __device__ __forceinline__ void tall_decode(TallTile& t, int vb, int nvirt, const int* t_incl,
                                             const int* t_m128, const int* t_seg, const int* t_cnt,
                                             int G, int n_cb, int n_wt, int n_ct, int nks, int Kdim,
-                                            const uint16_t* A, const u32x4_t* Wf, int w, int lane) {
+                                            int Nw, const uint16_t* A, const void* Wf,
+                                            const float* Wsc, int w, int lane) {
   t.ok = 0;
   if (vb >= nvirt) return;
   const int pid = xcd_remap(vb);
@@ -723,7 +726,17 @@ __device__ __forceinline__ void tall_decode(TallTile& t, int vb, int nvirt, cons
   t.nt = nrows <= BMR;
   // the one-tile kernel's K rotation for experts read once (per expert)
   t.crot = t.nt ? (int)((((uint32_t)g * 977u) * 2654435761u) >> 8) % (nks / kChunkSteps) : 0;
-  t.wp = Wf + ((int64_t)g * nks * n_ct + t.ct) * (kFrags * kWave);
+  t.wp = static_cast<const WFrag<F8>*>(Wf) + ((int64_t)g * nks * n_ct + t.ct) * (kFrags * kWave);
+  if (F8) {
+    // scale rows ([G][Nw/128][Kdim/128]): w13 gate rows 32 ct + 16 hsel ..,
+    // up rows Nw/2 + the same; w2 rows 64 ct + 32 hsel ..; each half tile
+    // lies in one 128-row scale block, that of its column tile
+    const int nkb = Kdim / 128, nrb = Nw / 128;
+    const int rb_g = GATE_UP ? (32 * t.ct) / 128 : (64 * t.ct) / 128;
+    const int rb_u = GATE_UP ? (Nw / 2 + 32 * t.ct) / 128 : rb_g;
+    t.sc_g = Wsc + ((int64_t)g * nrb + rb_g) * nkb;
+    t.sc_u = Wsc + ((int64_t)g * nrb + rb_u) * nkb;
+  }
   t.a_base = GATE_UP ? A + t.row_base * Kdim : A + t.mt_glob * kMsub * (int64_t)nks * (kWave * 8);
   if (GATE_UP) {
 #pragma unroll
@@ -736,9 +749,9 @@ __device__ __forceinline__ void tall_decode(TallTile& t, int vb, int nvirt, cons
   }
 }
 
-template <bool GATE_UP>
+template <bool GATE_UP, bool F8>
 __global__ void __launch_bounds__(8 * kWave, 2) tall_stream_kernel(
-    const uint16_t* __restrict__ A, const void* __restrict__ Wf_,
+    const uint16_t* __restrict__ A, const void* __restrict__ Wf, const float* __restrict__ Wsc,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ counts, int G,
     int Kdim, int Nw /* weight rows per group */, int Nout, const float* __restrict__ row_scale,
     uint16_t* __restrict__ Out, int64_t capacity, int32_t* __restrict__ dev_error, int nvirt) {
@@ -750,7 +763,6 @@ __global__ void __launch_bounds__(8 * kWave, 2) tall_stream_kernel(
   __shared__ float rs[2][BMR];
   __shared__ int t_incl[kStreamMaxG], t_m128[kStreamMaxG], t_seg[kStreamMaxG], t_cnt[kStreamMaxG];
 
-  const u32x4_t* Wf = static_cast<const u32x4_t*>(Wf_);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_ct = Nw / 64, n_wt = 2 * n_ct, n_cb = (n_wt + NW - 1) / NW;
@@ -799,8 +811,8 @@ __global__ void __launch_bounds__(8 * kWave, 2) tall_stream_kernel(
 
   TallTile cur, nxt;
   int vb = blockIdx.x;
-  tall_decode<GATE_UP>(cur, vb, nvirt, t_incl, t_m128, t_seg, t_cnt, G, n_cb, n_wt, n_ct, nks,
-                       Kdim, A, Wf, w, lane);
+  tall_decode<GATE_UP, F8>(cur, vb, nvirt, t_incl, t_m128, t_seg, t_cnt, G, n_cb, n_wt, n_ct,
+                           nks, Kdim, Nw, A, Wf, Wsc, w, lane);
   if (!cur.ok) return;   // the whole workgroup
 
   const uint32_t as_lds = lds_addr(&As[0][0][0]), rs_lds = lds_addr(&rs[0][0]);
@@ -832,13 +844,19 @@ __global__ void __launch_bounds__(8 * kWave, 2) tall_stream_kernel(
       dma4_at(row_scale + t.row_base, (uint32_t)r * 4u, rs_lds + (uint32_t)((buf * BMR + w * kWave) * 4));
     }
   };
-  u32x4_t bq[kPrefetch][FR];
+  WFrag<F8> bq[kPrefetch][FR];
+  float bsg[kPrefetch], bsu[kPrefetch];   // FP8: the tile scales of each slot's K-step
   // weights read once stream past the caches (non-temporal); gate/up always
   // does, without the per-tile branch (same-box A/B on the deepseek-shape
   // layer, every expert read once: gate/up 2.58 -> 2.50 ms; for down the
   // branch-free form was slower)
   auto load_step = [&](const TallTile& t, int step, int s) {
-    const u32x4_t* p = t.wp + (int64_t)wrap(step + t.crot * kChunkSteps, nks) * kstride + lane;
+    const int kidx = wrap(step + t.crot * kChunkSteps, nks);
+    const WFrag<F8>* p = static_cast<const WFrag<F8>*>(t.wp) + (int64_t)kidx * kstride + lane;
+    if (F8) {   // 128 K-columns = 4 steps per scale
+      bsg[s] = t.sc_g[kidx >> 2];
+      bsu[s] = t.sc_u[kidx >> 2];
+    }
     if (GATE_UP || t.nt) {
 #pragma unroll
       for (int f = 0; f < FR; ++f) bq[s][f] = __builtin_nontemporal_load(p + frag_of(t, f) * kWave);
@@ -894,7 +912,12 @@ __global__ void __launch_bounds__(8 * kWave, 2) tall_stream_kernel(
     const int sub = ks % kChunkSteps;
     bf16x8_t bfr[FR];
 #pragma unroll
-    for (int f = 0; f < FR; ++f) bfr[f] = __builtin_bit_cast(bf16x8_t, bq[s][f]);
+    for (int f = 0; f < FR; ++f) {
+      if constexpr (F8)   // w13: fragment 0 gate rows, 1 up rows; w2: one scale block
+        bfr[f] = dequant8(bq[s][f], (GATE_UP && f == 1) ? bsu[s] : bsg[s]);
+      else
+        bfr[f] = __builtin_bit_cast(bf16x8_t, bq[s][f]);
+    }
 #pragma unroll
     for (int g8 = 0; g8 < MS; g8 += 8) {
       if (g8 >= cur.nlive) continue;
@@ -927,8 +950,8 @@ __global__ void __launch_bounds__(8 * kWave, 2) tall_stream_kernel(
   constexpr int kEpiStride = (GATE_UP ? 8 * FR : 16 * FR) + 8;
   uint16_t* epi = Epi[w];
   for (;;) {
-    tall_decode<GATE_UP>(nxt, vb + (int)gridDim.x, nvirt, t_incl, t_m128, t_seg, t_cnt, G, n_cb,
-                         n_wt, n_ct, nks, Kdim, A, Wf, w, lane);
+    tall_decode<GATE_UP, F8>(nxt, vb + (int)gridDim.x, nvirt, t_incl, t_m128, t_seg, t_cnt, G,
+                             n_cb, n_wt, n_ct, nks, Kdim, Nw, A, Wf, Wsc, w, lane);
 #pragma unroll
     for (int i = 0; i < MS; ++i)
 #pragma unroll
@@ -1211,13 +1234,14 @@ int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32
   // layer, T=4096, H=7168, 256 experts, I=2048: gate/up 2.75 -> 2.58 ms, down
   // unchanged, the layer 4.86 -> 4.71 ms), in the streamed kernel (down
   // 1.65 -> 1.48 ms more); its LDS tile table holds every group the ABI
-  // accepts.  With FP8 weights a tall wave's half-size fragments keep too few
-  // bytes in flight (the same A/B: gate/up 2.34 -> 2.58 ms), so they keep the
-  // 128-row tiles.
+  // accepts.  FP8 weights take the same tiles (each expert's weights read
+  // once: HBM traffic 1.40 -> 1.0 x on gate/up; the same A/B: gate/up
+  // unchanged at 2.38 ms, down 1.40 -> 1.37 ms: with FP8 weights the GEMM is
+  // bound by its conversion and issue, not by the bytes).
   const int64_t mean_x = capacity / G;  // mean rows per group, rounded down
   const bool wide = mean_x >= kBM;
   const bool wide_down = wide && mean_x < 2 * kBM;
-  const bool tall = packed && !f8 && mean_x >= kTallMin && mean_x < 2 * kBM;
+  const bool tall = packed && mean_x >= kTallMin && mean_x < 2 * kBM;
   const int64_t m_tiles_tall = (capacity + 2 * kBM - 1) / (2 * kBM) + G;
   auto grid_tall = [&](int64_t n_tiles) {
     return (m_tiles_tall * n_tiles + grid_unit - 1) / grid_unit * grid_unit;
@@ -1226,9 +1250,12 @@ int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32
   if ((flags & MOE_FFN_GATE_UP) && tall) {
     const int64_t blocks = grid_tall((2 * (2 * I / 64) + 7) / 8);
     if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(tall_stream_kernel<true>, dim3((unsigned)stream_grid(blocks)),
-                       dim3(8 * kWave), 0, stream, x, w13, cu_seqlens, counts, G, H, 2 * I, I,
-                       nullptr, act, capacity, dev_error, (int)blocks);
+#define MOE_TALL_GU(F8)                                                                         \
+  hipLaunchKernelGGL((tall_stream_kernel<true, F8>), dim3((unsigned)stream_grid(blocks)),          \
+                     dim3(8 * kWave), 0, stream, x, w13, w13s, cu_seqlens, counts, G, H, 2 * I, I, \
+                     nullptr, act, capacity, dev_error, (int)blocks)
+    if (f8) MOE_TALL_GU(true); else MOE_TALL_GU(false);
+#undef MOE_TALL_GU
   } else if (flags & MOE_FFN_GATE_UP) {
     if (packed) {
       const int nw = wide ? 8 : 4;
@@ -1255,9 +1282,12 @@ int launch_grouped_ffn(const uint16_t* x, const int32_t* cu_seqlens, const int32
   if ((flags & MOE_FFN_DOWN) && tall) {
     const int64_t blocks = grid_tall((2 * (H / 64) + 7) / 8);
     if (blocks > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(tall_stream_kernel<false>, dim3((unsigned)stream_grid(blocks)),
-                       dim3(8 * kWave), 0, stream, act, w2, cu_seqlens, counts, G, I, H, H,
-                       row_scale, y, capacity, dev_error, (int)blocks);
+#define MOE_TALL_DN(F8)                                                                         \
+  hipLaunchKernelGGL((tall_stream_kernel<false, F8>), dim3((unsigned)stream_grid(blocks)),         \
+                     dim3(8 * kWave), 0, stream, act, w2, w2s, cu_seqlens, counts, G, I, H, H,    \
+                     row_scale, y, capacity, dev_error, (int)blocks)
+    if (f8) MOE_TALL_DN(true); else MOE_TALL_DN(false);
+#undef MOE_TALL_DN
   } else if (flags & MOE_FFN_DOWN) {
     if (packed) {
       const int nw = wide_down ? 8 : 4;

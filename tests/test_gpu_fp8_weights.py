@@ -123,13 +123,10 @@ def test_ffn_fp8_weights_equal_bf16_on_dequantized(H, I, T, hot, pow2):
     ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, d13p, d2p, p.w_perm, yb,
                         flags=ops.MOE_FFN_ALL | ops.MOE_FFN_PACKED_WEIGHTS)
     assert host(err)[0] == 0
-    cap = p.x_perm.shape[0]
-    if not 96 <= cap // G < 256:
-        # the same tiles, the same summation order: the same bits
-        assert torch.equal(y8.view(torch.int16), yb.view(torch.int16))
-    # (segments averaging 96..255 rows: the bf16 kernel takes 256-row tiles
-    # whose K order differs, so there the two agree to rounding only; both
-    # are checked against the oracle below)
+    # the same tiles (128-row, or the streamed 256-row tiles for segments
+    # averaging 96..255 rows), the same summation order: the
+    # same bits
+    assert torch.equal(y8.view(torch.int16), yb.view(torch.int16))
     # the stages run separately give the same bits
     ws = torch.empty(ops.moe_grouped_ffn_workspace_bytes(p.x_perm.shape[0], G, H, I),
                      dtype=torch.uint8, device="cuda")

@@ -173,8 +173,17 @@ __global__ void __launch_bounds__(kQNW * kWave, 2) w8a8_gemm_kernel(
   const int n_ct = Nw / 64;
   const int n_cb = (n_ct + kQTiles - 1) / kQTiles;
   const int pid = xcd_remap(blockIdx.x);
-  int g, mt, cb, mt_base;
-  if (!decode_tile(pid, counts, G, n_cb, g, mt, cb, &mt_base)) return;
+  int g, mt, cb;
+  int64_t mt_before;
+  if (!decode_tile(pid, counts, G, n_cb, capacity, g, mt, cb, &mt_before)) return;
+  // the intermediate's m-tile must lie in the workspace (ceil(capacity/128)
+  // + G m-tiles): segments that overlap, each inside [0, capacity), could
+  // otherwise place later groups' m-tiles past its end
+  if (mt_before + mt >= (capacity + kBM - 1) / kBM + G) {
+    if ((threadIdx.x & 63) == 0) raise_error(dev_error, MOE_DEVERR_ROW_RANGE);
+    return;
+  }
+  int mt_base = (int)mt_before;
   g = __builtin_amdgcn_readfirstlane(g);
   mt = __builtin_amdgcn_readfirstlane(mt);
   cb = __builtin_amdgcn_readfirstlane(cb);

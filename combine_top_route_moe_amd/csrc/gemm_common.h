@@ -33,31 +33,33 @@ __device__ __forceinline__ int xcd_remap(int bid) {
 // Decode tile number `pid` into (group, m-tile, n-tile).  Every lane of
 // the calling wave returns the same answer; returns false past the last
 // tile.  mt_base (if asked for) is the number of m-tiles of the groups
-// before g.
+// before g.  Counts are clamped to [0, capacity] and summed in 64 bits, so
+// that corrupt counts give wrong tiles (which the kernels' range checks
+// reject) rather than wrapped sums.
 __device__ __forceinline__ bool decode_tile(int pid, const int32_t* __restrict__ counts, int G,
-                                            int n_tiles, int& g, int& mt, int& nt,
-                                            int* mt_base = nullptr) {
+                                            int n_tiles, int64_t capacity, int& g, int& mt,
+                                            int& nt, int64_t* mt_base = nullptr) {
   const int lane = threadIdx.x & 63;
-  int carry = 0;
+  long long carry = 0;
   for (int base = 0; base < G; base += kWave) {
     const int e = base + lane;
-    const int c = e < G ? max(counts[e], 0) : 0;
-    const int tiles = ((c + kBM - 1) / kBM) * n_tiles;
-    int incl = tiles;
+    const int c = e < G ? (int)min((int64_t)max(counts[e], 0), capacity) : 0;
+    const long long tiles = (((long long)c + kBM - 1) / kBM) * n_tiles;
+    long long incl = tiles;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, kWave);
+      const long long y = __shfl_up(incl, off, kWave);
       if (lane >= off) incl += y;
     }
     incl += carry;
-    const int excl = incl - tiles;
+    const long long excl = incl - tiles;
     const uint64_t hit = __ballot(e < G && pid >= excl && pid < incl);
     if (hit) {
       const int src = __ffsll((unsigned long long)hit) - 1;
       g = base + src;
-      const int ex = __shfl(excl, src, kWave);
-      const int local = pid - ex;
-      const int mtiles = (__shfl(c, src, kWave) + kBM - 1) / kBM;
+      const long long ex = __shfl(excl, src, kWave);
+      const int local = (int)(pid - ex);
+      const int mtiles = (int)(((long long)__shfl(c, src, kWave) + kBM - 1) / kBM);
       nt = local / mtiles;
       mt = local - nt * mtiles;
       if (mt_base) *mt_base = ex / n_tiles;                   // m-tiles before g

@@ -64,7 +64,7 @@ __global__ void __launch_bounds__(kThreads, 2) grouped_gemm_kernel(
   const int n_tiles = GATE_UP ? Nout / (kBN / 2) : Nout / kBN;
   const int pid = xcd_remap(blockIdx.x);
   int g, mt, nt;
-  if (!decode_tile(pid, counts, G, n_tiles, g, mt, nt)) return;
+  if (!decode_tile(pid, counts, G, n_tiles, capacity, g, mt, nt)) return;
 
   const int seg0 = cu_seqlens[g];
   const int nrows = counts[g];
@@ -506,8 +506,17 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
   const int n_wt = n_ct;                  // wave tiles per group
   const int n_cb = (n_wt + NW - 1) / NW;  // workgroups per m-tile
   const int pid = xcd_remap(blockIdx.x);
-  int g, mt, cb, mt_base;
-  if (!decode_tile(pid, counts, G, n_cb, g, mt, cb, &mt_base)) return;
+  int g, mt, cb;
+  int64_t mt_before;
+  if (!decode_tile(pid, counts, G, n_cb, capacity, g, mt, cb, &mt_before)) return;
+  // the intermediate's m-tile must lie in the workspace (ceil(capacity/128)
+  // + G m-tiles): segments that overlap, each inside [0, capacity), could
+  // otherwise place later groups' m-tiles past its end
+  if (mt_before + mt >= (capacity + kBM - 1) / kBM + G) {
+    if ((threadIdx.x & 63) == 0) raise_error(dev_error, MOE_DEVERR_ROW_RANGE);
+    return;
+  }
+  int mt_base = (int)mt_before;
   // the same in every lane: say so, so that addresses built from them stay scalar
   g = __builtin_amdgcn_readfirstlane(g);
   mt = __builtin_amdgcn_readfirstlane(mt);
@@ -769,37 +778,47 @@ __global__ void __launch_bounds__(8 * kWave, 2) tall_stream_kernel(
   const int nks = Kdim / 32, nch = nks / kChunkSteps;
   const int kstride = n_ct * kFrags * kWave;
 
-  // the tile table: a group whose segment leaves [0, capacity) gets no tile
-  // (and raises the error); the 128-row m-tile count, which places the
-  // activation rows, counts every group as the one-tile kernel does
+  // the tile table (the 128-row m-tile count, which places the activation
+  // rows, counts every group as the 128-row kernel does)
   if (w == 0) {
-    int carry = 0, carry128 = 0;
+    int carry = 0;
+    long long carry128 = 0;
+    const long long ws_mtiles = (capacity + kBM - 1) / kBM + G;
     for (int base = 0; base < G; base += kWave) {
       const int e = base + lane;
-      int c = 0, s0 = 0;
+      int craw = 0, s0 = 0;
       if (e < G) {
-        c = max(counts[e], 0);
+        craw = max(counts[e], 0);
         s0 = cu_seqlens[e];
       }
-      const int m128 = (c + kBM - 1) / kBM;
-      if (c > 0 && ((int64_t)s0 + c > capacity || s0 < 0)) {
+      // the 128-row m-tiles before each group (the activation layout) come
+      // from every group's count, clamped to the capacity and summed in 64
+      // bits; a group whose segment leaves [0, capacity), or whose m-tiles
+      // would end past the workspace's ceil(capacity/128) + G (overlapping
+      // segments), gets no tile
+      const int m128 = (int)((min((long long)craw, (long long)capacity) + kBM - 1) / kBM);
+      long long incl128 = m128;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const long long y128 = __shfl_up(incl128, off, kWave);
+        if (lane >= off) incl128 += y128;
+      }
+      incl128 += carry128;
+      int c = craw;
+      if (c > 0 && ((int64_t)s0 + c > capacity || s0 < 0 || incl128 > ws_mtiles)) {
         raise_error(dev_error, MOE_DEVERR_ROW_RANGE);
         c = 0;
       }
-      int incl = ((c + BMR - 1) / BMR) * n_cb, incl128 = m128;
+      int incl = ((c + BMR - 1) / BMR) * n_cb;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off, kWave), y128 = __shfl_up(incl128, off, kWave);
-        if (lane >= off) {
-          incl += y;
-          incl128 += y128;
-        }
+        const int y = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += y;
       }
       incl += carry;
-      incl128 += carry128;
       if (e < G) {
         t_incl[e] = incl;
-        t_m128[e] = incl128 - m128;
+        t_m128[e] = (int)min(incl128 - m128, ws_mtiles);   // used only by groups with tiles
         t_seg[e] = s0;
         t_cnt[e] = c;
       }

@@ -219,7 +219,12 @@ int moe_permute_noalloc(const int32_t* topk_idx, const float* topk_w, const uint
  * get the workspace a GATE_UP call with the same segments filled — and, with
  * MOE_FFN_PACKED_WEIGHTS, says that w13 and w2 are in the packed layout
  * moe_pack_ffn_weights() produces.  Segments that reach past `capacity` are
- * skipped and raise MOE_DEVERR_ROW_RANGE.  capacity 0 (an empty batch)
+ * skipped and raise MOE_DEVERR_ROW_RANGE.  Segments are meant to be
+ * disjoint (the permute's output is); with packed weights, tiles whose
+ * place in the workspace (counted from the counts, each clamped to
+ * `capacity`) would fall past its ceil(capacity/128) + G row tiles, which
+ * only overlapping segments or oversized counts produce, are skipped with
+ * the same error.  capacity 0 (an empty batch)
  * returns MOE_OK after the scalar checks, touching no pointer (the FP8 and
  * FP8-path variants below behave the same).
  * Requires H % 128 == 0, I % 128 == 0, 1 <= G <= 1024. */
@@ -322,7 +327,8 @@ int moe_quant_rows_fp8(const uint16_t* in, int64_t n_rows, int H, const int32_t*
  *     moe_grouped_ffn.
  * flags: MOE_FFN_GATE_UP (writes qa, sa into the workspace), MOE_FFN_DOWN
  * (reads them; needs the workspace of a GATE_UP call on the same segments)
- * or MOE_FFN_ALL.  Segments past capacity are skipped with
+ * or MOE_FFN_ALL.  Segments past capacity, and tiles past the workspace
+ * (as for moe_grouped_ffn with packed weights), are skipped with
  * MOE_DEVERR_ROW_RANGE.  Requires H % 128 == 0, I % 128 == 0, G <= 1024. */
 size_t moe_grouped_ffn_w8a8_workspace_bytes(int64_t capacity, int num_groups, int H, int I);
 int moe_grouped_ffn_w8a8(const uint8_t* xq, const float* x_scales, int64_t scale_stride,

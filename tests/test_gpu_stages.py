@@ -878,6 +878,58 @@ def test_ffn_tall_tiles_edges():
                    oracle.expert_ffn(x, *deq) * rs, FFN_TOL, what=f"fp8w expert {e} ({n} rows)")
 
 
+
+@pytest.mark.parametrize("pattern", ["overlap", "huge"])
+@pytest.mark.parametrize("path,capacity", [("bf16", 300), ("bf16", 600), ("fp8w", 300),
+                                           ("fp8w", 600), ("w8a8", 300)])
+def test_ffn_segments_past_the_workspace_fail_closed(path, capacity, pattern):
+    """Segments that each lie inside [0, capacity) but overlap (every group
+    starting at row 0), or counts far above the capacity, would place the
+    later groups' m-tiles of the intermediate past the workspace's
+    ceil(capacity / 128) + G m-tiles.  Every fragment-order kernel (the
+    128-row tiles at a mean under 96 rows per group, the streamed tall tiles
+    at 96..255, FP8 weights, FP8 rows) reports ROW_RANGE for them and
+    writes nothing past the workspace or the output."""
+    G, H, I = 4, 256, 256
+    cfg = workloads.MoEConfig("t", 45, T=capacity, H=H, E=G, K=1, I=I)
+    w13, w2, _ = stacked_weights(cfg)
+    x = dev_bf16(workloads.hidden(cfg))
+    if pattern == "overlap":
+        counts = np.full(G, capacity, np.int32)
+        seg = np.zeros(G + 1, np.int32)
+    else:
+        counts = np.array([2**31 - 1, 100, 2**31 - 1, 50], np.int32)
+        seg = np.array([0, 0, 0, 100, capacity], np.int32)
+    seg[G] = capacity
+    d_counts, d_seg = dev(counts), dev(seg)
+    y_all = torch.full((capacity + 8, H), 1.5, dtype=torch.bfloat16, device="cuda")
+    y = y_all[:capacity]
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    if path == "w8a8":
+        need = ops.moe_grouped_ffn_w8a8_workspace_bytes(capacity, G, H, I)
+    else:
+        need = ops.moe_grouped_ffn_workspace_bytes(capacity, G, H, I)
+    ws = torch.zeros(need + 4096, dtype=torch.uint8, device="cuda")
+    ws[need:] = 0xA5
+    if path == "bf16":
+        w13p, w2p = ops.moe_pack_ffn_weights(w13, w2)
+        ops.moe_grouped_ffn(x, d_seg, d_counts, w13p, w2p, None, y,
+                            ops.MOE_FFN_ALL | ops.MOE_FFN_PACKED_WEIGHTS, ws[:need], err)
+    elif path == "fp8w":
+        q13, s13, q2, s2 = ops.moe_pack_ffn_weights_fp8(w13, w2)
+        ops.moe_grouped_ffn_fp8(x, d_seg, d_counts, q13, s13, q2, s2, None, y,
+                                workspace=ws[:need], dev_error=err)
+    else:
+        q13, s13, q2, s2 = ops.moe_pack_ffn_weights_fp8(w13, w2, k128=True)
+        xq, xs = ops.moe_quant_rows_fp8(x)
+        ops.moe_grouped_ffn_w8a8(xq, xs, d_seg, d_counts, q13, s13, q2, s2, None, y,
+                                 workspace=ws[:need], dev_error=err)
+    torch.cuda.synchronize()
+    assert host(err)[0] == ops.MOE_DEVERR_ROW_RANGE
+    assert bool((ws[need:] == 0xA5).all())
+    assert bool((y_all[capacity:] == 1.5).all())
+
+
 @pytest.mark.parametrize("nvec", [1, 255, 1024, 4097, 300001])
 def test_copy_bytes(nvec):
     """The streaming copy behind the copy-bandwidth figure: exact, including

@@ -654,7 +654,7 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
 //
 // Wait accounting, per wave (loads complete in issue order; stores count in
 // vmcnt too):
-//  - within a tile as in the one-tile kernel: at a chunk's barrier at least
+//  - within a tile as in the 128-row kernel: at a chunk's barrier at least
 //    kAfterDma weight loads were issued after that chunk's DMA;
 //  - the next tile's chunk 0 goes out with this tile's chunk L-1 (L the
 //    last), followed by kAfterDma weight refills and then the epilogue's
@@ -666,7 +666,7 @@ __global__ void __launch_bounds__(NW * kWave, 2) frag_gemm_kernel(
 //  - its chunk 1 goes out with chunk L, followed by refills, the stores and
 //    the next tile's own refills: more than kAfterDma.
 // After the workgroup's last tile the refills and DMAs re-read its last step
-// and chunk, as the one-tile kernel does, which keeps these counts.
+// and chunk, as the 128-row kernel does, which keeps these counts.
 constexpr int kStreamMaxG = 1024;                     // groups the LDS tile table holds
 constexpr int kStreamStores = FragShape<true>::kMs;   // epilogue stores per wave and tile
 constexpr uint32_t kBufferOob = 0x80000000u;          // a buffer offset past every range
@@ -733,7 +733,7 @@ __device__ __forceinline__ void tall_decode(TallTile& t, int vb, int nvirt, cons
   t.ct = wt >> 1;
   t.hsel = wt & 1;
   t.nt = nrows <= BMR;
-  // the one-tile kernel's K rotation for experts read once (per expert)
+  // the 128-row kernel's K rotation for experts read once (per expert)
   t.crot = t.nt ? (int)((((uint32_t)g * 977u) * 2654435761u) >> 8) % (nks / kChunkSteps) : 0;
   t.wp = static_cast<const WFrag<F8>*>(Wf) + ((int64_t)g * nks * n_ct + t.ct) * (kFrags * kWave);
   if (F8) {
@@ -982,7 +982,7 @@ __global__ void __launch_bounds__(8 * kWave, 2) tall_stream_kernel(
 #pragma unroll
     for (int s = 0; s < kPrefetch; ++s) step(nks - kPrefetch + s, s, true);
 
-    // epilogue, as in the one-tile kernel, but every m-subtile issues
+    // epilogue, as in the 128-row kernel, but every m-subtile issues
     // exactly one 16-byte buffer store (see the wait accounting above)
     const bool use_scale = !GATE_UP && row_scale != nullptr;
     // gate/up: the tile's 16 m-subtile blocks of the activation layout;

@@ -241,10 +241,20 @@ __global__ void __launch_bounds__(kQNW * kWave, 2) w8a8_gemm_kernel(
   // by wave 0, gathered through smap for gate/up
   const float* s_base = GATE_UP ? Ascale : Ascale + mt_glob * nkb * kBM;
   const int64_t s_kstride = GATE_UP ? sstride : kBM;
+  // gate/up: row r's scales sit in column smap[row] / sdiv of Ascale (or the
+  // row's own column); a gathered column outside [0, sstride) — a corrupt
+  // map entry — is replaced by column 0 and raises the error, so the DMA
+  // never leaves the array
   auto scale_row = [&](int r) -> uint32_t {
     if (!GATE_UP) return (uint32_t)r;
     const int64_t pr = row_base + min(r, valid - 1);
-    return (uint32_t)(smap ? smap[pr] / sdiv : pr);
+    if (!smap) return (uint32_t)pr;
+    const int src = smap[pr];
+    if (src < 0 || src / sdiv >= sstride) {
+      raise_error(dev_error, MOE_DEVERR_ROW_RANGE);
+      return 0u;
+    }
+    return (uint32_t)(src / sdiv);
   };
   const uint32_t s_voff0 = scale_row(lane) * 4u;
   const uint32_t s_voff1 = scale_row(64 + lane) * 4u;

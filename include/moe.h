@@ -321,7 +321,9 @@ int moe_quant_rows_fp8(const uint16_t* in, int64_t n_rows, int H, const int32_t*
  *     (scale_div >= 1) — moe_permute's src_of and K, so that the scales of
  *     the unpermuted [T, H] rows serve the permuted codes, which moe_permute
  *     moves like any other row payload; scale_stride must then exceed every
- *     such row (>= T);
+ *     such row (>= T): a routed row whose scale_src entry is negative or
+ *     names a row at or past scale_stride raises MOE_DEVERR_ROW_RANGE (and
+ *     takes row 0's scales instead of reading outside x_scales);
  *   w13q / w2q and their tile scales from moe_pack_ffn_weights_fp8 with
  *     MOE_FP8_LAYOUT_K128; row_scale, y, cu_seqlens, counts, capacity as in
  *     moe_grouped_ffn.

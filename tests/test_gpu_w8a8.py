@@ -178,3 +178,37 @@ def test_w8a8_ffn_matches_oracle(H, I, T, hot, pow2):
         if seg_end > r0 + n:
             assert np.all(host_bits(y[r0 + n:seg_end]) == 0)
     print(f"H={H} I={I} T={T}: worst down row rel err {worst:.3e}, intermediate code flips {flips:.2e}")
+
+
+@pytest.mark.parametrize("bad", ["negative", "past_the_end"])
+def test_w8a8_scale_gather_out_of_range_fails_closed(bad):
+    """The FP8 path's gate/up gathers each row's activation scales through
+    scale_src[r] // scale_div (the permute's src_of and K): an entry that is
+    negative, or whose column lies past the scale array's stride, raises
+    ROW_RANGE instead of reading outside the array; the correct map raises
+    nothing."""
+    G, H, I, T, K = 2, 256, 256, 50, 2
+    cfg = workloads.MoEConfig("t", 46, T=T, H=H, E=G, K=K, I=I)
+    w13, w2, _ = stacked_weights(cfg)
+    w13q, w13s, w2q, w2s = ops.moe_pack_ffn_weights_fp8(w13, w2, k128=True)
+    xq_tok, xs = ops.moe_quant_rows_fp8(dev_bf16(workloads.hidden(cfg)))   # [T, H], [H/128, T]
+    cap = T * K
+    xq = xq_tok.repeat_interleave(K, dim=0).contiguous()   # row r holds token r // K
+    counts, cu = np.array([60, 40], np.int32), np.array([0, 60, cap], np.int32)
+    src = np.arange(cap, dtype=np.int32)
+
+    def run(src_map):
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        y = torch.zeros(cap, H, dtype=torch.bfloat16, device="cuda")
+        ops.moe_grouped_ffn_w8a8(xq, xs, dev(cu), dev(counts), w13q, w13s, w2q, w2s, None, y,
+                                 dev_error=err, scale_src=dev(src_map), scale_div=K)
+        torch.cuda.synchronize()
+        return int(host(err)[0])
+
+    assert run(src) == 0
+    corrupt = src.copy()
+    if bad == "negative":
+        corrupt[5] = -1
+    else:
+        corrupt[70] = T * K        # column T: one past the last token's
+    assert run(corrupt) == ops.MOE_DEVERR_ROW_RANGE

@@ -770,14 +770,16 @@ def test_ffn_packed_weights(H, I, T):
     assert rel_err(bf16_bits_to_f32(host_bits(y[:used])), bf16_bits_to_f32(host_bits(y2[:used]))) < 1e-2
 
 
-def test_ffn_tall_tiles_streamed_across_tiles():
+@pytest.mark.parametrize("fp8", [False, True])
+def test_ffn_tall_tiles_streamed_across_tiles(fp8):
     """The tall tiles run persistently, each workgroup taking several tiles
     in turn, with the next tile's weights and activation chunks fetched
     during the current tile's last steps and its epilogue.  Enough tiles for
     about three per workgroup, tile to tile changes of segment length (a
     single row, 16 and 17 rows, full 256-row tiles, experts spanning two
     tall tiles, empty experts between), every expert against the oracle per
-    row and element."""
+    row and element; with BF16 weights and with FP8 weights (against the
+    oracle on the dequantized weights)."""
     rng = np.random.default_rng(11)
     G, H, I = 200, 1024, 512
     sizes = rng.integers(90, 220, G)
@@ -792,9 +794,13 @@ def test_ffn_tall_tiles_streamed_across_tiles():
     w13, w2, host_w = stacked_weights(cfg)
     ref = oracle.permute(idx, w, hid, G, 0, False)
     p = ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), G)
-    w13p, w2p = ops.moe_pack_ffn_weights(w13, w2)
-    y = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13p, w2p, p.w_perm,
-                            flags=ops.MOE_FFN_ALL | ops.MOE_FFN_PACKED_WEIGHTS)
+    if fp8:
+        q13, s13, q2, s2 = ops.moe_pack_ffn_weights_fp8(w13, w2)
+        y = ops.moe_grouped_ffn_fp8(p.x_perm, p.cu_seqlens, p.counts, q13, s13, q2, s2, p.w_perm)
+    else:
+        w13p, w2p = ops.moe_pack_ffn_weights(w13, w2)
+        y = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13p, w2p, p.w_perm,
+                                flags=ops.MOE_FFN_ALL | ops.MOE_FFN_PACKED_WEIGHTS)
     torch.cuda.synchronize()
     got = bf16_bits_to_f32(host_bits(y))
     for e in range(G):
@@ -803,15 +809,17 @@ def test_ffn_tall_tiles_streamed_across_tiles():
             continue
         x = oracle.bf16_bits_to_f64(ref["x_perm"][r0:r0 + n])
         rs = ref["w_perm"][r0:r0 + n, None].astype(np.float64)
-        check_rows(got[r0:r0 + n], oracle.expert_ffn(x, *host_w[e]) * rs, FFN_TOL,
+        wts = [oracle.quantize_weight_blocks(m)[2] for m in host_w[e]] if fp8 else host_w[e]
+        check_rows(got[r0:r0 + n], oracle.expert_ffn(x, *wts) * rs, FFN_TOL,
                    what=f"expert {e} ({n} rows)")
 
 
-def test_ffn_tall_tiles_streamed_at_the_limits():
+@pytest.mark.parametrize("fp8", [False, True])
+def test_ffn_tall_tiles_streamed_at_the_limits(fp8):
     """The streamed tall kernel at its limits: 1024 groups (its LDS tile
     table full) and H = I = 128, so each K loop has two chunks and the next
     tile's first chunk goes out with the current tile's first one; many
-    tiles per workgroup, empty groups among them."""
+    tiles per workgroup, empty groups among them; BF16 and FP8 weights."""
     rng = np.random.default_rng(12)
     G, H, I = 1024, 128, 128
     sizes = [int(n) for n in rng.integers(90, 230, G)]
@@ -826,9 +834,13 @@ def test_ffn_tall_tiles_streamed_at_the_limits():
     w13, w2, host_w = stacked_weights(cfg)
     ref = oracle.permute(idx, w, hid, G, 0, False)
     p = ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), G)
-    w13p, w2p = ops.moe_pack_ffn_weights(w13, w2)
-    y = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13p, w2p, p.w_perm,
-                            flags=ops.MOE_FFN_ALL | ops.MOE_FFN_PACKED_WEIGHTS)
+    if fp8:
+        q13, s13, q2, s2 = ops.moe_pack_ffn_weights_fp8(w13, w2)
+        y = ops.moe_grouped_ffn_fp8(p.x_perm, p.cu_seqlens, p.counts, q13, s13, q2, s2, p.w_perm)
+    else:
+        w13p, w2p = ops.moe_pack_ffn_weights(w13, w2)
+        y = ops.moe_grouped_ffn(p.x_perm, p.cu_seqlens, p.counts, w13p, w2p, p.w_perm,
+                                flags=ops.MOE_FFN_ALL | ops.MOE_FFN_PACKED_WEIGHTS)
     torch.cuda.synchronize()
     got = bf16_bits_to_f32(host_bits(y))
     for e in range(G):
@@ -837,7 +849,8 @@ def test_ffn_tall_tiles_streamed_at_the_limits():
             continue
         x = oracle.bf16_bits_to_f64(ref["x_perm"][r0:r0 + n])
         rs = ref["w_perm"][r0:r0 + n, None].astype(np.float64)
-        check_rows(got[r0:r0 + n], oracle.expert_ffn(x, *host_w[e]) * rs, FFN_TOL,
+        wts = [oracle.quantize_weight_blocks(m)[2] for m in host_w[e]] if fp8 else host_w[e]
+        check_rows(got[r0:r0 + n], oracle.expert_ffn(x, *wts) * rs, FFN_TOL,
                    what=f"expert {e} ({n} rows)")
 
 

@@ -275,14 +275,23 @@ __global__ void __launch_bounds__(1024) permute_scan_kernel(
 }
 
 // FUSED: `table` holds the chunk_rank totals and the workgroup does the
-// scan's work itself (see the file comment); otherwise `table` holds the
-// absolute first row of every (chunk, expert) pair written by the scan.
+// scan's work itself from a copy of the table in LDS (see the file comment).
+// COLS: `table` holds the totals too (at most kColChunks chunks, at most 256
+// experts), and each workgroup reads only the table's columns: thread e sums
+// expert e's chunk counts (all of them, those before the workgroup's first
+// chunk, and those up to it; its slots span at most two chunks), then a
+// block-wide scan of the sizes gives the starts.  The loads of a column are
+// all in flight together and hit L2, so this costs each workgroup about one
+// memory round trip and saves the one-workgroup scan launch.
+// Otherwise `table` holds the absolute first row of every (chunk, expert)
+// pair written by the scan.
 // QDQ (both scatter kernels): each row vector is the dispatch FP8
 // fake-quant's output (fq_block128_vec).  The 16 vectors of a 1 x 128 block
 // are 16 consecutive indices of the copy loop, so 16 consecutive lanes of
 // one wave, which take every branch of the loop together (H / 8 and the
 // loop stride are multiples of 16).
-template <bool FUSED, bool QDQ>
+constexpr int kColChunks = 32;
+template <bool FUSED, bool COLS, bool QDQ>
 __global__ void __launch_bounds__(256) permute_scatter_kernel(
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
     const uint16_t* __restrict__ hidden, int T, int K, int H, int expert_begin, int El,
@@ -293,11 +302,26 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
     int32_t* __restrict__ cu_seqlens) {
   __shared__ int32_t dest[256];
   __shared__ int32_t s_tab[FUSED ? kFuseTable : 1];
-  __shared__ int32_t s_start[FUSED ? 1024 : 1];
-  __shared__ int32_t s_tot[FUSED ? 1024 : 1];
-  __shared__ int32_t s_size[FUSED ? 1024 : 1];
+  __shared__ int32_t s_start[FUSED ? 1024 : COLS ? 256 : 1];
+  __shared__ int32_t s_tot[FUSED ? 1024 : COLS ? 256 : 1];
+  __shared__ int32_t s_size[FUSED ? 1024 : COLS ? 256 : 1];
+  __shared__ int32_t s_pre[COLS ? 2 : 1][COLS ? 256 : 1];
   __shared__ int32_t s_wave[4];
   const int tid = threadIdx.x;
+  const int c0 = COLS ? (int)((int64_t)blockIdx.x * tok_per_block * K / kChunk) : 0;
+  // this workgroup's slots: their rank, id and weight, loaded before the
+  // start rows are worked out, so the two sets of loads overlap
+  const int t0 = blockIdx.x * tok_per_block;
+  const int nslots = tok_per_block * K;
+  const int64_t my_i = (int64_t)t0 * K + tid;
+  const bool my_slot = tid < nslots && t0 + tid / K < T;
+  int my_rank = -1, my_id = -1;
+  float my_w = 0.0f;
+  if (my_slot) {
+    my_rank = rank[my_i];
+    my_id = topk_idx[my_i];
+    my_w = topk_w[my_i];
+  }
   int64_t used_end;   // end of the last segment
   if (FUSED) {
     const int n = nchunks * El;
@@ -356,6 +380,60 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
           w_perm[r] = 0.0f;
         }
     used_end = grand;
+  } else if (COLS) {
+    int tot = 0, pre0 = 0, pre1 = 0;
+    if (tid < El && nchunks > 0) {
+      // every load unconditional (index clamped), so all are in flight
+      // before the first use; chunks past the end count 0
+      int vals[kColChunks];
+#pragma unroll
+      for (int c = 0; c < kColChunks; ++c) vals[c] = table[min(c, nchunks - 1) * El + tid];
+#pragma unroll
+      for (int c = 0; c < kColChunks; ++c) {
+        const int v = c < nchunks ? vals[c] : 0;
+        tot += v;
+        pre0 += c < c0 ? v : 0;
+        pre1 += c <= c0 ? v : 0;
+      }
+    }
+    const int sz = tid < El ? (pad_pow2 ? next_pow2_dev(tot) : tot) : 0;
+    const int lane = tid & 63, wid = tid >> 6;
+    int x = sz;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, kWave);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wave[wid] = x;
+    __syncthreads();
+    int before = x - sz;
+    for (int q = 0; q < wid; ++q) before += s_wave[q];
+    const int grand = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+    if (tid < El) {
+      s_start[tid] = before;
+      s_tot[tid] = tot;
+      s_size[tid] = sz;
+      s_pre[0][tid] = pre0;
+      s_pre[1][tid] = pre1;
+      if (blockIdx.x == 0) {
+        counts[tid] = tot;
+        cu_seqlens[tid] = before;
+      }
+    }
+    if (blockIdx.x == 0 && tid == 0) {
+      cu_seqlens[El] = grand;
+      if ((int64_t)grand > capacity) raise_error(dev_error, MOE_DEVERR_CAPACITY);
+    }
+    __syncthreads();
+    // pow2 padding rows: workgroup b marks those of experts b, b + grid, ...
+    if (pad_pow2)
+      for (int e = blockIdx.x; e < El; e += gridDim.x)
+        for (int r = s_start[e] + s_tot[e] + tid; r < s_start[e] + s_size[e] && (int64_t)r < capacity;
+             r += blockDim.x) {
+          src_of[r] = -1;
+          w_perm[r] = 0.0f;
+        }
+    used_end = grand;
   } else {
     used_end = cu_seqlens[El];
     // pow2 padding rows: workgroup b marks those of experts b, b + grid, ...
@@ -376,20 +454,19 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
     src_of[r] = -1;
     w_perm[r] = 0.0f;
   }
-  const int t0 = blockIdx.x * tok_per_block;
-  const int nslots = tok_per_block * K;
   if (tid < nslots) {
-    const int t = t0 + tid / K;
     int r = -1;
-    if (t < T) {
-      const int64_t i = (int64_t)t0 * K + tid;
-      const int rk = rank[i];
+    if (my_slot) {
+      const int64_t i = my_i;
+      const int rk = my_rank;
       if (rk >= 0) {
-        const int e = topk_idx[i] - expert_begin;
+        const int e = my_id - expert_begin;
         int64_t first;   // absolute first row of (chunk of i, e)
         if (FUSED) {
           first = s_start[e];
           for (int c = 0; c < (int)(i / kChunk); ++c) first += s_tab[c * El + e];
+        } else if (COLS) {
+          first = s_start[e] + s_pre[(int)(i / kChunk) > c0 ? 1 : 0][e];
         } else {
           first = table[(i / kChunk) * El + e];
         }
@@ -397,7 +474,7 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(
         if (rr < capacity) {
           r = (int)rr;
           src_of[r] = (int32_t)i;
-          w_perm[r] = topk_w[i];
+          w_perm[r] = my_w;
         } else {
           raise_error(dev_error, MOE_DEVERR_CAPACITY);
         }
@@ -651,17 +728,22 @@ int launch_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t*
     hipLaunchKernelGGL(permute_chunk_rank_kernel, dim3(nchunks), dim3(256), 0, stream, topk_idx,
                        TK, num_experts, expert_begin, El, nbits, table, rank, dev_error);
   const bool fused = (int64_t)nchunks * El <= kFuseTable && nchunks <= kFuseChunks && El <= 1024;
-  if (!fused)
+  // up to kColChunks chunks and 256 experts, the scatter's workgroups read
+  // the table's columns themselves and the scan kernel is not launched
+  const bool cols = !fused && T > 0 && nchunks <= kColChunks && El <= 256;
+  if (!fused && !cols)
     hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, stream, table, nchunks, El,
                        pad_pow2, capacity, counts, cu_seqlens, src_of, w_perm, dev_error);
-#define MOE_PERMUTE_SCATTER(F, Q)                                                               \
-  hipLaunchKernelGGL((permute_scatter_kernel<F, Q>), dim3(grid), dim3(256), 0, stream, topk_idx,  \
+#define MOE_PERMUTE_SCATTER(F, C, Q)                                                            \
+  hipLaunchKernelGGL((permute_scatter_kernel<F, C, Q>), dim3(grid), dim3(256), 0, stream, topk_idx, \
                      topk_w, hidden, T, K, H, expert_begin, El, tpb, capacity, table, nchunks,     \
                      pad_pow2, rank, x_perm, row_of, src_of, w_perm, dev_error, counts, cu_seqlens)
   if (fused) {
-    if (dispatch_fp8) MOE_PERMUTE_SCATTER(true, true); else MOE_PERMUTE_SCATTER(true, false);
+    if (dispatch_fp8) MOE_PERMUTE_SCATTER(true, false, true); else MOE_PERMUTE_SCATTER(true, false, false);
+  } else if (cols) {
+    if (dispatch_fp8) MOE_PERMUTE_SCATTER(false, true, true); else MOE_PERMUTE_SCATTER(false, true, false);
   } else if (T > 0 || capacity > 0) {
-    if (dispatch_fp8) MOE_PERMUTE_SCATTER(false, true); else MOE_PERMUTE_SCATTER(false, false);
+    if (dispatch_fp8) MOE_PERMUTE_SCATTER(false, false, true); else MOE_PERMUTE_SCATTER(false, false, false);
   }
 #undef MOE_PERMUTE_SCATTER
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;

@@ -332,13 +332,20 @@ def test_permute_edge_cases(seed):
     (3, 2, 4, 8320, 4, 0),             # rows wider than the single launch's up-front loads
     (4096, 8, 1024, 128, 1024, 0),     # 32 chunks per scan thread: its register path at the limit
     (4300, 8, 1024, 128, 1024, 0),     # 34 chunks per scan thread: its loop path
-    (2100, 8, 128, 128, 128, 0),       # 17 chunks over 8 scan threads: a short and an empty block
+    (4200, 8, 128, 128, 128, 0),       # 33 chunks over 8 scan threads: a short and an empty block
+    (4096, 8, 256, 128, 256, 0),       # 32 chunks x 256 experts: the column-read scatter at its limits
+    (4097, 8, 256, 128, 256, 0),       # 33 chunks: the scan kernel again
+    (2100, 8, 257, 128, 257, 0),       # 17 chunks x 257 experts: the scan kernel
+    (2100, 8, 300, 128, 256, 44),      # 17 chunks, an expert-parallel share: the column read
+    (3000, 6, 64, 128, 64, 0),         # 96 slots per workgroup: some span two chunks
 ])
 def test_permute_launch_path_boundaries(T, K, E, H, El, begin):
     """Either side of the single-launch permute's limits (4096 slots, 4 row
-    vectors per thread loaded up front), at the 1024-local-expert limit, and
-    either side of the scan kernel's 32 chunks per thread held in registers:
-    bit-exact."""
+    vectors per thread loaded up front), at the 1024-local-expert limit,
+    either side of the scan kernel's 32 chunks per thread held in registers,
+    and either side of the scatter that reads the chunk table's columns
+    itself (at most 32 chunks and 256 local experts), including workgroups
+    whose slots span two chunks: bit-exact."""
     rng = np.random.default_rng(T * K + E)
     idx = rng.integers(-1, E, size=(T, K)).astype(np.int32)
     w = rng.random((T, K)).astype(np.float32)

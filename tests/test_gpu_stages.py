@@ -359,6 +359,8 @@ def test_permute_launch_path_boundaries(T, K, E, H, El, begin):
     (300, 8, 16, 512, True, (4, 8)),     # one launch, pow2 buckets, an expert-parallel share
     (700, 8, 32, 384, False, None),      # 5600 slots: the multi-launch path
     (3, 2, 4, 8320, True, None),         # rows wider than the one launch's up-front loads
+    (2100, 8, 64, 256, True, None),      # 17 chunks: the scatter that reads the table's columns
+    (5000, 8, 300, 128, False, None),    # 40 chunks, 300 experts: the scan kernel
 ])
 def test_permute_dispatch_fp8_equals_quantize_then_permute(T, K, E, H, pow2, begin_el):
     """MOE_PERMUTE_DISPATCH_FP8: the permuted rows are the 1x128 FP8 dispatch

@@ -697,7 +697,7 @@ struct TallTile {
 template <bool GATE_UP, bool F8>
 __device__ __forceinline__ void tall_decode(TallTile& t, int vb, int nvirt, const int* t_incl,
                                             const int* t_m128, const int* t_seg, const int* t_cnt,
-                                            int G, int n_cb, int n_wt, int n_ct, int nks, int Kdim,
+                                            int G, int n_wt, int n_ct, int nks, int Kdim,
                                             int Nw, const uint16_t* A, const void* Wf,
                                             const float* Wsc, int w, int lane) {
   t.ok = 0;
@@ -830,7 +830,7 @@ __global__ void __launch_bounds__(8 * kWave, 2) tall_stream_kernel(
 
   TallTile cur, nxt;
   int vb = blockIdx.x;
-  tall_decode<GATE_UP, F8>(cur, vb, nvirt, t_incl, t_m128, t_seg, t_cnt, G, n_cb, n_wt, n_ct,
+  tall_decode<GATE_UP, F8>(cur, vb, nvirt, t_incl, t_m128, t_seg, t_cnt, G, n_wt, n_ct,
                            nks, Kdim, Nw, A, Wf, Wsc, w, lane);
   if (!cur.ok) return;   // the whole workgroup
 
@@ -970,7 +970,7 @@ __global__ void __launch_bounds__(8 * kWave, 2) tall_stream_kernel(
   uint16_t* epi = Epi[w];
   for (;;) {
     tall_decode<GATE_UP, F8>(nxt, vb + (int)gridDim.x, nvirt, t_incl, t_m128, t_seg, t_cnt, G,
-                             n_cb, n_wt, n_ct, nks, Kdim, Nw, A, Wf, Wsc, w, lane);
+                             n_wt, n_ct, nks, Kdim, Nw, A, Wf, Wsc, w, lane);
 #pragma unroll
     for (int i = 0; i < MS; ++i)
 #pragma unroll

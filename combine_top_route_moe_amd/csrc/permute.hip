@@ -172,8 +172,8 @@ __device__ __forceinline__ int next_pow2_dev(int n) {
 constexpr int kScanRegs = 32;
 __global__ void __launch_bounds__(1024) permute_scan_kernel(
     int32_t* __restrict__ table, int nchunks, int El, int pad_pow2, int64_t capacity,
-    int32_t* __restrict__ counts, int32_t* __restrict__ cu_seqlens, int32_t* __restrict__ src_of,
-    float* __restrict__ w_perm, int32_t* __restrict__ dev_error) {
+    int32_t* __restrict__ counts, int32_t* __restrict__ cu_seqlens,
+    int32_t* __restrict__ dev_error) {
   __shared__ int32_t part[1024];   // [P][El] partial sums
   __shared__ int32_t s_start[1024];
   __shared__ int32_t s_wave[16];
@@ -733,7 +733,7 @@ int launch_permute(const int32_t* topk_idx, const float* topk_w, const uint16_t*
   const bool cols = !fused && T > 0 && nchunks <= kColChunks && El <= 256;
   if (!fused && !cols)
     hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, stream, table, nchunks, El,
-                       pad_pow2, capacity, counts, cu_seqlens, src_of, w_perm, dev_error);
+                       pad_pow2, capacity, counts, cu_seqlens, dev_error);
 #define MOE_PERMUTE_SCATTER(F, C, Q)                                                            \
   hipLaunchKernelGGL((permute_scatter_kernel<F, C, Q>), dim3(grid), dim3(256), 0, stream, topk_idx, \
                      topk_w, hidden, T, K, H, expert_begin, El, tpb, capacity, table, nchunks,     \

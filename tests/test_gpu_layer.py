@@ -26,7 +26,7 @@ import torch
 
 import oracle
 import workloads
-from combine_top_route_moe_amd import MoELayer, ops
+from combine_top_route_moe_amd import MoELayer
 from oracle.numerics import bf16_bits_to_f64
 from tests.gpu_util import (need_gpu, dev_bf16, host_bits, dev, host, rel_err, check_rows,
                             w8a8_intermediate, check_fp8_intermediate)

@@ -15,7 +15,6 @@
 """
 
 import numpy as np
-import pytest
 
 import oracle
 from oracle.fp8_gemm import block_scaled_matmul, expert_ffn_w8a8, quantize_rows_fp8

@@ -2,7 +2,6 @@
 recipe's properties (segment-size ranges, padding share, hot experts)."""
 
 import numpy as np
-import pytest
 
 import oracle
 import workloads

@@ -450,13 +450,17 @@ def test_permute_expert_id_out_of_range_fails_closed(T, K, E, El, begin):
         ops.moe_permute(dev(idx), dev(w), dev_bf16(hid), El, E - El + 1, num_experts=E)
 
 
-def test_permute_capacity_overflow_is_flagged_not_written():
+@pytest.mark.parametrize("T,K,E,cap", [
+    (64, 4, 8, 100),          # the single-launch path; 256 rows are needed
+    (2100, 8, 64, 10000),     # the scatter that reads the chunk table's columns; 16800 needed
+    (5000, 8, 300, 20000),    # the scan kernel; 40000 needed
+])
+def test_permute_capacity_overflow_is_flagged_not_written(T, K, E, cap):
     rng = np.random.default_rng(9)
-    T, K, E, H = 64, 4, 8, 128
+    H = 128
     idx = rng.integers(0, E, size=(T, K)).astype(np.int32)
     w = rng.random((T, K)).astype(np.float32)
     hid = rng.integers(0, 2 ** 16, size=(T, H), dtype=np.uint64).astype(np.uint16)
-    cap = 100                                        # 256 rows are needed
     guard = 16
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = ops.alloc_permuted(T, K, H, E, cap + guard, "cuda")

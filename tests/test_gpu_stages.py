@@ -419,7 +419,8 @@ def test_empty_batch_every_stage():
     (64, 2, 8, 8, 0),          # one launch
     (300, 8, 64, 32, 16),      # one launch, an expert-parallel share
     (700, 8, 64, 64, 0),       # the multi-launch path, scan fused into the scatter
-    (4096, 8, 256, 256, 0),    # the multi-launch path with the scan kernel
+    (4096, 8, 256, 256, 0),    # the multi-launch path, the scatter reading the table's columns
+    (5000, 8, 300, 300, 0),    # the multi-launch path with the scan kernel
 ])
 def test_permute_expert_id_out_of_range_fails_closed(T, K, E, El, begin):
     """Router ids at or past the layer's expert count raise
